@@ -1,0 +1,102 @@
+"""Pins for the oracle's relayouts and scatter / gather (CPU only).
+
+Index-coded tensors (every element holds its own flat index) make each
+destination element's expected value a closed form of its position."""
+import numpy as np
+import pytest
+
+from oracle import relayout as X
+from ulysses_sequence_attention_amd import synth
+
+SHAPES = [  # B, S, H, D, P
+    (1, 7, 6, 4, 3),
+    (2, 5, 7, 2, 3),     # ragged heads 3/2/2
+    (1, 9, 4, 3, 4),     # ragged tokens 3/2/2/2
+    (3, 5, 5, 1, 5),     # one head and one token per group
+    (1, 6, 3, 2, 1),     # P = 1
+]
+
+
+def _heads_groups(H, P):
+    # head groups from an independent library routine (same remainder rule)
+    return np.array_split(np.arange(H), P)
+
+
+@pytest.mark.parametrize("B,S,H,D,P", SHAPES)
+def test_pack_closed_form(B, S, H, D, P):
+    seq = synth.index_coded((B, S, H, D), "f32")
+    blocks = X.pack_seq_to_heads(seq, P)
+    groups = _heads_groups(H, P)
+    for j in range(P):
+        assert blocks[j].shape == (B, S, len(groups[j]), D)
+        for b in range(B):
+            for s in range(S):
+                for i, head in enumerate(groups[j]):
+                    for d in range(D):
+                        assert blocks[j][b, s, i, d] == ((b * S + s) * H + head) * D + d
+
+
+@pytest.mark.parametrize("B,S,H,D,P", SHAPES)
+def test_pack_matches_library_split(B, S, H, D, P):
+    seq = synth.index_coded((B, S, H, D), "bf16")
+    blocks = X.pack_seq_to_heads(seq, P)
+    for j, ref in enumerate(np.array_split(seq, P, axis=2)):
+        assert np.array_equal(blocks[j], ref)
+
+
+@pytest.mark.parametrize("B,S,H,D,P", SHAPES)
+def test_roundtrips(B, S, H, D, P):
+    seq = synth.index_coded((B, S, H, D), "bf16")
+    blocks = X.pack_seq_to_heads(seq, P)
+    back = X.unpack_heads_to_seq(blocks, H)
+    assert back.tobytes() == seq.tobytes()
+    again = X.pack_seq_to_heads(back, P)
+    for a, b in zip(blocks, again):
+        assert a.tobytes() == b.tobytes()
+
+
+def test_p1_is_byte_identical():
+    seq = synth.index_coded((2, 5, 3, 4), "bf16")
+    (blk,) = X.pack_seq_to_heads(seq, 1)
+    assert blk.tobytes() == seq.tobytes()
+    assert X.unpack_heads_to_seq([blk], 3).tobytes() == seq.tobytes()
+
+
+@pytest.mark.parametrize("B,S,H,D,P", SHAPES)
+def test_elementwise_variant_agrees(B, S, H, D, P):
+    seq = synth.index_coded((B, S, H, D), "f32")
+    a = X.pack_seq_to_heads(seq, P)
+    b = X.pack_seq_to_heads_elementwise(seq, P)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("B,S,H,D,P", SHAPES)
+def test_rank_shares_tile_the_world(B, S, H, D, P):
+    seq = synth.index_coded((B, S, H, D), "f32")
+    world = X.pack_seq_to_heads(seq, P)
+    groups = _heads_groups(H, P)
+    tok = np.array_split(np.arange(S), P)
+    sentinel = -1.0
+    blocks = [np.full((B, S, len(g), D), sentinel, np.float32) for g in groups]
+    for r in range(P):
+        shard = X.scatter_sequence(seq, P, r)
+        before = [blk.copy() for blk in blocks]
+        X.pack_rank_share(shard, blocks, S, r)
+        for j in range(P):
+            changed = np.any(blocks[j] != before[j], axis=(0, 2, 3))
+            # only rank r's rows may change
+            assert set(np.nonzero(changed)[0]) <= set(tok[r].tolist())
+    for j in range(P):
+        assert np.array_equal(blocks[j], world[j])
+    for r in range(P):
+        assert np.array_equal(X.unpack_rank_share(world, H, r),
+                              X.scatter_sequence(seq, P, r))
+
+
+@pytest.mark.parametrize("S,P", [(7, 3), (9, 4), (5, 5), (6, 1)])
+def test_scatter_gather_identity(S, P):
+    x = synth.index_coded((2, S, 3), "f32")
+    shards = [X.scatter_sequence(x, P, r) for r in range(P)]
+    assert [s.shape[1] for s in shards] == [len(t) for t in np.array_split(np.arange(S), P)]
+    assert np.array_equal(X.gather_sequence(shards), x)
