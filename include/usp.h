@@ -1,0 +1,173 @@
+/*
+ * usp.h — C ABI of libusp, the MI355X (gfx950) hot path of Ulysses sequence
+ * parallelism: one rank's share of the work, at its real shape.
+ *
+ * The method (m-star "sequence_parallel" API page, module description):
+ * tokens are sharded over an SP group of P ranks; around attention, a first
+ * all-to-all turns each rank's sequence shard [seq/P, H, D] into the full
+ * sequence over its own head group [seq, H/P, D], attention runs locally per
+ * head, and a second all-to-all turns the result back. On one GPU the
+ * exchange is replaced by local permutations into "world layouts" that hold
+ * every rank's buffers side by side:
+ *
+ *   sequence-sharded world  seq[B][S][H][D], rank r owns token rows
+ *                           [t_r, t_{r+1}) of every batch row;
+ *   head-sharded world      P blocks, block j is blk_j[B][S][h_j][D] and holds
+ *                           heads [c_j, c_{j+1}) — exactly what rank j holds
+ *                           after the first all-to-all.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are dense row-major, element type USP_F32 (4 bytes) or
+ *     USP_BF16 (2 bytes, bfloat16). Device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronizes; device work is enqueued on the caller's stream
+ *     (a hipStream_t passed as void*; NULL = the default stream) and the call
+ *     returns without waiting for it.
+ *   - Every call returns USP_OK (0) or a negative status. On error nothing is
+ *     launched and no output is written; usp_last_error() gives a message.
+ *   - Sizes are validated against overflow; a launch failure reported by the
+ *     HIP runtime is returned as USP_EHIP.
+ */
+#ifndef USP_H
+#define USP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum usp_dtype { USP_F32 = 0, USP_BF16 = 1 } usp_dtype;
+
+enum {
+  USP_OK = 0,
+  USP_EINVAL = -1, /* an argument is out of its domain (counts, ranks, ranges) */
+  USP_ESHAPE = -2, /* sizes are inconsistent or overflow */
+  USP_EDTYPE = -3, /* element type not supported for this call */
+  USP_EALIGN = -4, /* a pointer or row is not 16-byte aligned */
+  USP_ENOSYS = -5, /* a valid request this build has no kernel for */
+  USP_EHIP = -6    /* the HIP runtime reported an error */
+};
+
+/* Largest SP degree the relayout calls accept (block pointers travel as
+ * kernel arguments). */
+#define USP_MAX_PARTS 64
+
+/* Message for the last non-zero status returned on the calling thread
+ * (thread-local; "" if none). The string stays valid until the next call. */
+const char* usp_last_error(void);
+
+/* Library version string, e.g. "usp 0.1.0 gfx950". */
+const char* usp_version(void);
+
+/*
+ * Balanced contiguous ranges (h3-blackwell-runtime distributed.py,
+ * balanced_ranges; m-star sp_seq_split): split `total` ordered items into
+ * `parts` contiguous non-empty ranges; with base = total / parts and
+ * extra = total % parts, range r has base + (r < extra) items, so earlier
+ * ranks carry the remainder.
+ *   bounds: caller-owned host array of parts + 1 int64; on success
+ *           bounds[0] = 0, bounds[parts] = total, range r = [bounds[r],
+ *           bounds[r+1]).
+ * Errors: parts < 1 or total < parts -> USP_EINVAL; bounds NULL -> USP_EINVAL.
+ */
+int usp_balanced_ranges(int64_t total, int32_t parts, int64_t* bounds);
+
+/* The same boundaries computed on the device by a kernel on `stream` into the
+ * caller-owned device array d_bounds[parts + 1] (8-byte aligned). Same
+ * errors as usp_balanced_ranges. */
+int usp_balanced_ranges_device(int64_t total, int32_t parts, int64_t* d_bounds,
+                               void* stream);
+
+/*
+ * Head-chunk plan (maxdiffusion PR #428, two-phase head-chunked Ulysses
+ * all-to-all: heads run in `chunks` passes, the final chunk carrying the
+ * remainder). Every chunk but the last holds ceil(heads / chunks) heads; the
+ * last holds the rest (8 heads in 3 chunks: 3/3/2).
+ *   bounds: caller-owned host array of chunks + 1 int32.
+ * Errors: heads < 1, chunks < 1, chunks > heads, or a plan that would leave a
+ * chunk empty (e.g. 5 heads in 4 chunks) -> USP_EINVAL.
+ */
+int usp_head_chunk_ranges(int32_t heads, int32_t chunks, int32_t* bounds);
+
+/*
+ * Sequence-sharded -> head-sharded relayout (the data movement around the
+ * first all-to-all: h3-blackwell-runtime distributed.py,
+ * SequenceParallelContext.seq_to_heads; m-star sp_head_slice for the head
+ * groups). Token ranges t = balanced(S, P), head ranges c = balanced(H, P).
+ *   rank < 0  (world): seq is [B][S][H][D]; for every j, b, s, i, d:
+ *             blk[j][b][s][i][d] = seq[b][s][c_j + i][d].
+ *   rank = r  (one rank's share): seq is r's compact shard [B][len_r][H][D]
+ *             and only rows [t_r, t_{r+1}) of every block are written:
+ *             blk[j][b][t_r + s][i][d] = seq[b][s][c_j + i][d].
+ *   blk: host array of P device pointers, block j of [B][S][h_j][D]. In a
+ *        multi-GPU system these are the peers' receive buffers.
+ *   P = 1 copies seq byte for byte. Pure data movement: results are exact.
+ * Errors: P < 1, P > USP_MAX_PARTS, S < P, H < P, rank >= P -> USP_EINVAL;
+ *   B < 1, D < 1 or byte sizes overflowing int64 -> USP_ESHAPE; dtype not
+ *   F32/BF16 -> USP_EDTYPE; D * element size not a multiple of 16 or a
+ *   pointer not 16-byte aligned -> USP_EALIGN; seq, blk or blk[j] NULL ->
+ *   USP_EINVAL. Buffers must not overlap.
+ */
+int usp_pack_seq_to_heads(const void* seq, void* const* blk, usp_dtype dtype, int64_t B,
+                          int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                          void* stream);
+
+/*
+ * Head-sharded -> sequence-sharded relayout (the data movement around the
+ * second all-to-all: h3-blackwell-runtime distributed.py,
+ * SequenceParallelContext.heads_to_seq). Exact inverse of the pack:
+ *   rank < 0: seq[b][s][c_j + i][d] = blk[j][b][s][i][d] for all rows;
+ *   rank = r: seq is r's shard [B][len_r][H][D],
+ *             seq[b][s][c_j + i][d] = blk[j][b][t_r + s][i][d].
+ * Same arguments and errors as usp_pack_seq_to_heads.
+ */
+int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
+                            int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                            void* stream);
+
+/*
+ * Non-causal multi-head attention over the full sequence for heads
+ * [head_lo, head_hi) of one head-group block (m-star ulysses_attention: the
+ * rank runs the unchanged attention kernel on [seq, H/P, D]). For each b,
+ * head n in range, query s:
+ *   O[b][s][n][:] = sum_t softmax_t(scale * <Q[b][s][n][:], K[b][t][n][:]>)
+ *                   * V[b][t][n][:]
+ *   q, k, v, o: device [B][S][h][D] (h = heads of the block); heads outside
+ *               the range are neither read nor written.
+ *   in_dt:  USP_BF16 (flash kernel on MFMA; D in {64, 128}) or USP_F32
+ *           (plain fp32 kernel; D in {32, 64, 128}).
+ *   out_dt: USP_F32 or USP_BF16 for bf16 inputs; USP_F32 for fp32 inputs.
+ *   scale:  softmax scale; <= 0 selects 1/sqrt(D).
+ *   lse:    NULL, or device fp32 [B][h][S] receiving the natural-log softmax
+ *           normaliser log(sum_t exp(scale * <Q, K_t>)) for heads in range.
+ * Scores, softmax and accumulation are fp32. The result for a head depends
+ * only on that head's inputs, never on [head_lo, head_hi): a head computed in
+ * any sub-range is bitwise equal to the same head computed single-shot.
+ * Errors: h < 1, head range empty or outside [0, h) -> USP_EINVAL;
+ *   B < 1, S < 1 or sizes overflowing -> USP_ESHAPE; unsupported
+ *   in_dt/out_dt pair -> USP_EDTYPE; unsupported D -> USP_ENOSYS; misaligned
+ *   pointers -> USP_EALIGN; q, k, v or o NULL -> USP_EINVAL.
+ */
+int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
+                      usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
+                      int32_t head_lo, int32_t head_hi, float scale, float* lse, void* stream);
+
+/*
+ * Head-chunked attention (maxdiffusion PR #428, two-phase Ulysses: attention
+ * over head sub-groups in turn, mathematically the single-shot result since
+ * heads are independent): runs usp_attention_fwd over each range of
+ * usp_head_chunk_ranges(h, chunks) in order on `stream`. Bitwise equal to
+ * the single-shot call. Errors: those of usp_head_chunk_ranges and
+ * usp_attention_fwd.
+ */
+int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,
+                              usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
+                              int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* USP_H */

@@ -1,0 +1,66 @@
+"""Helpers shared by the GPU parity tests (host <-> device marshalling, error
+metrics). Not a test module."""
+import sys
+
+import numpy as np
+
+from ulysses_sequence_attention_amd import synth
+
+DEV = "cuda:0"
+
+
+def log(msg):
+    """Name the case before each GPU step so a failing run says what it ran."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr, dtype):
+    import torch
+    if dtype == synth.BF16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(DEV)
+
+
+def to_host(t):
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def poisoned(shape, dtype):
+    """Device tensor filled with a NaN pattern (bf16 0xFFFF / fp32 NaN)."""
+    import torch
+    if dtype == synth.BF16:
+        return torch.full(shape, -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+
+
+def widen(arr, dtype):
+    """Stored values (bf16 bits or fp32) as float64."""
+    if dtype == synth.BF16:
+        return synth.bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def err(out, ref):
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = out - ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    return max_abs, rel
+
+
+# Tolerances stated for the attention path: bf16 inputs (fp32 output
+# epilogue) and the all-fp32 path.
+BF16_MAX_ABS, BF16_REL_FROB = 1e-2, 5e-3
+F32_MAX_ABS, F32_REL_FROB = 1e-5, 1e-5
+
+
+def bf16_ulp(x):
+    """One bf16 ulp at |x| (for grading the bf16-output epilogue)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)

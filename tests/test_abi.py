@@ -1,0 +1,116 @@
+"""The C ABI on the host (no GPU): exports, host range logic, argument checks.
+
+Every call here returns before any device work: host-only range functions,
+and invalid arguments that the library must reject without launching."""
+import ctypes
+import subprocess
+
+import pytest
+
+import ulysses_sequence_attention_amd as usp
+from oracle import ranges as R
+
+L = usp.lib()
+FAKE = 0x10000  # 16-byte aligned address that is never dereferenced
+
+
+def test_exports_every_declared_symbol():
+    declared = usp.header_symbols()
+    assert len(declared) >= 9
+    out = subprocess.run(["nm", "-D", "--defined-only", usp._binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version():
+    assert "gfx950" in usp.usp_version()
+
+
+def test_host_ranges_match_oracle():
+    for total in range(1, 80):
+        for parts in range(1, min(total, 70) + 1):
+            assert usp.usp_balanced_ranges(total, parts) == R.balanced_ranges(total, parts)
+    for total, parts in [(32760, 8), (65537, 4), (131072, 7), (2**40 + 3, 64)]:
+        assert usp.usp_balanced_ranges(total, parts) == R.balanced_ranges(total, parts)
+
+
+def test_head_chunks_match_oracle():
+    for heads in range(1, 40):
+        for chunks in range(1, heads + 1):
+            try:
+                ref = R.head_chunk_ranges(heads, chunks)
+            except ValueError:
+                with pytest.raises(usp.UspError) as e:
+                    usp.usp_head_chunk_ranges(heads, chunks)
+                assert e.value.status == -1
+                continue
+            assert usp.usp_head_chunk_ranges(heads, chunks) == ref
+
+
+@pytest.mark.parametrize("total,parts", [(3, 4), (5, 0), (0, 1), (-1, 1)])
+def test_range_errors(total, parts):
+    with pytest.raises(usp.UspError) as e:
+        usp.usp_balanced_ranges(total, parts)
+    assert e.value.status == -1
+    assert usp.usp_last_error()
+
+
+def _pack(seq=FAKE, blk=(FAKE,), dt=1, B=1, S=8, H=4, D=64, P=1, rank=-1):
+    arr = (ctypes.c_void_p * max(len(blk), 1))(*blk)
+    return L.usp_pack_seq_to_heads(seq, arr, dt, B, S, H, D, P, rank, None)
+
+
+def _unpack(seq=FAKE, blk=(FAKE,), dt=1, B=1, S=8, H=4, D=64, P=1, rank=-1):
+    arr = (ctypes.c_void_p * max(len(blk), 1))(*blk)
+    return L.usp_unpack_heads_to_seq(arr, seq, dt, B, S, H, D, P, rank, None)
+
+
+@pytest.mark.parametrize("fn", [_pack, _unpack])
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), -1), (dict(P=65, blk=(FAKE,) * 65, H=65, S=65), -1),
+    (dict(S=2, P=3, blk=(FAKE,) * 3), -1), (dict(H=2, P=3, blk=(FAKE,) * 3), -1),
+    (dict(rank=1), -1), (dict(B=0), -2), (dict(D=0), -2), (dict(dt=7), -3),
+    (dict(D=4), -4), (dict(dt=0, D=2), -4), (dict(seq=FAKE + 8), -4),
+    (dict(blk=(FAKE + 4,)), -4), (dict(seq=None), -1), (dict(blk=(None,)), -1),
+    (dict(B=2**40, S=2**40), -2),
+])
+def test_relayout_rejects(fn, kw, status):
+    assert fn(**kw) == status
+    assert usp.usp_last_error()
+
+
+def _attn(q=FAKE, k=FAKE, v=FAKE, o=FAKE, i=1, out=0, B=1, S=16, h=2, D=64, lo=0, hi=2,
+          scale=0.0, lse=None):
+    return L.usp_attention_fwd(q, k, v, o, i, out, B, S, h, D, lo, hi, scale, lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(h=0, hi=0), -1), (dict(lo=1, hi=1), -1),
+    (dict(lo=0, hi=3), -1), (dict(lo=-1), -1), (dict(B=0), -2), (dict(S=0), -2),
+    (dict(i=5), -3), (dict(out=5), -3), (dict(i=0, out=1), -3), (dict(D=96), -5),
+    (dict(i=0, D=48), -5), (dict(k=FAKE + 2), -4), (dict(lse=FAKE + 2), -4),
+])
+def test_attention_rejects(kw, status):
+    assert _attn(**kw) == status
+    assert usp.usp_last_error()
+
+
+def test_chunked_rejects():
+    f = L.usp_attention_fwd_chunked
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 64, 0.0, None, 4, None) == -1  # empty chunk
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 64, 0.0, None, 6, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 64, 0.0, None, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 80, 0.0, None, 2, None) == -5
+
+
+def test_single_hip_runtime_in_process():
+    # libusp must share PyTorch's HIP runtime: a second libamdhip64 copy in the
+    # process leaves PyTorch on a runtime it was not built for.
+    import os
+    usp.lib()
+    with open(f"/proc/{os.getpid()}/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, paths

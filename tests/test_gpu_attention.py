@@ -1,0 +1,237 @@
+"""GPU parity of attention against the float64 oracle.
+
+Tolerances: bf16 inputs graded on the fp32-output epilogue, max-abs <= 1e-2
+and relative Frobenius <= 5e-3; the fp32 path <= 1e-5 for both. The bf16
+output epilogue is graded per element within max(1e-2, one bf16 ulp of the
+reference)."""
+import numpy as np
+import pytest
+
+import ulysses_sequence_attention_amd as usp
+from oracle import attention as A
+from oracle import ranges as R
+from oracle import relayout as X
+from ulysses_sequence_attention_amd import synth
+
+from gpu_util import (BF16_MAX_ABS, BF16_REL_FROB, DEV, F32_MAX_ABS, F32_REL_FROB, bf16_ulp, err,
+                      log, poisoned, to_dev, to_host, widen)
+
+pytestmark = pytest.mark.gpu
+BF, F = synth.BF16, synth.F32
+
+
+def _run(q, k, v, dtype, out_dtype, lo=0, hi=None, scale=0.0, want_lse=False, chunks=None):
+    import torch
+    B, S, h, D = q.shape
+    dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
+    o = poisoned((B, S, h, D), out_dtype)
+    lse = torch.full((B, h, S), float("nan"), device=DEV) if want_lse else None
+    if chunks is None:
+        usp.usp_attention_fwd(dq, dk, dv, o, head_lo=lo, head_hi=hi, scale=scale, lse=lse)
+    else:
+        usp.usp_attention_fwd_chunked(dq, dk, dv, o, chunks, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    out = to_host(o)
+    return (out, lse.cpu().numpy()) if want_lse else out
+
+
+SMALL = [  # B, S, h, D : several tiles and ragged tails on both kernels' tilings
+    (1, 1, 1, 64), (1, 2, 2, 128), (1, 31, 1, 64), (2, 65, 3, 128), (1, 257, 2, 64),
+    (1, 300, 1, 128), (1, 1000, 2, 128), (2, 513, 2, 64), (1, 777, 3, 64), (1, 129, 1, 128),
+]
+
+
+@pytest.mark.parametrize("B,S,h,D", SMALL)
+def test_bf16_small_full_compare(B, S, h, D):
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=100 + S + D)
+    ref, ref_lse = A.attention(*(widen(x, BF) for x in (q, k, v)), return_lse=True)
+    log(f"attention bf16->f32 B={B} S={S} h={h} D={D}")
+    out, lse = _run(q, k, v, BF, F, want_lse=True)
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-3
+    log(f"attention bf16->bf16 B={B} S={S} h={h} D={D}")
+    ob = widen(_run(q, k, v, BF, BF), BF)
+    assert np.all(np.abs(ob - ref) <= np.maximum(BF16_MAX_ABS, bf16_ulp(ref)))
+
+
+@pytest.mark.parametrize("B,S,h,D", [(1, 1, 1, 32), (1, 70, 2, 64), (2, 257, 2, 128),
+                                     (1, 100, 3, 32)])
+def test_f32_small_full_compare(B, S, h, D):
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=7 + S, dtype=F)
+    ref, ref_lse = A.attention(q, k, v, return_lse=True)
+    log(f"attention f32 B={B} S={S} h={h} D={D}")
+    out, lse = _run(q, k, v, F, F, want_lse=True)
+    ma, rf = err(out, ref)
+    assert ma <= F32_MAX_ABS and rf <= F32_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lse - ref_lse)) <= 1e-5
+
+
+def test_custom_scale_and_head_range_isolation():
+    B, S, h, D = 1, 200, 4, 128
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=5)
+    ref = A.attention(*(widen(x, BF) for x in (q, k, v)), scale=0.3)
+    log("attention head range [1, 3) scale 0.3")
+    out = _run(q, k, v, BF, F, lo=1, hi=3, scale=0.3)
+    ma, rf = err(out[:, :, 1:3], ref[:, :, 1:3])
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB
+    assert np.all(np.isnan(out[:, :, 0])) and np.all(np.isnan(out[:, :, 3]))
+
+
+def test_peaky_softmax_small():
+    # 1% of K rows x8: large logits, near one-hot rows
+    q, k, v = synth.draw_qkv(1, 2000, 2, 64, seed=9, peaky_frac=0.01)
+    ref = A.attention(*(widen(x, BF) for x in (q, k, v)))
+    log("attention peaky S=2000")
+    ma, rf = err(_run(q, k, v, BF, F), ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+
+
+@pytest.mark.parametrize("h,chunks", [(8, 3), (5, 2), (3, 3), (4, 1)])
+def test_chunked_bitwise_equals_single_shot_small(h, chunks):
+    q, k, v = synth.draw_qkv(1, 333, h, 128, seed=h)
+    log(f"attention chunked h={h} chunks={chunks}")
+    one = _run(q, k, v, BF, F)
+    many = _run(q, k, v, BF, F, chunks=chunks)
+    assert one.tobytes() == many.tobytes()
+
+
+def _ulysses_gpu(w: synth.Workload, q, k, v, out_dtype):
+    """pack (world) -> attention per head-group block -> unpack, on the GPU."""
+    import torch
+    B, S, H, D, P = w.B, w.S, w.H, w.D, w.P
+    hb = R.balanced_ranges(H, P)
+    blocks = []
+    for x in (q, k, v):
+        bl = [poisoned((B, S, hb[j + 1] - hb[j], D), w.dtype) for j in range(P)]
+        usp.usp_pack_seq_to_heads(to_dev(x, w.dtype), bl)
+        blocks.append(bl)
+    ob = [poisoned((B, S, hb[j + 1] - hb[j], D), out_dtype) for j in range(P)]
+    for j in range(P):
+        usp.usp_attention_fwd(blocks[0][j], blocks[1][j], blocks[2][j], ob[j])
+    out = poisoned((B, S, H, D), out_dtype)
+    usp.usp_unpack_heads_to_seq(ob, out)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def test_tiny_fp32_workload_full():
+    w = synth.WORKLOADS["tiny_fp32"]
+    q, k, v = synth.draw_workload(w)
+    ref = A.attention(q, k, v)  # single-device attention over all heads
+    log("workload tiny_fp32: pack -> attention x3 -> unpack")
+    out = _ulysses_gpu(w, q, k, v, F)
+    ma, rf = err(out, ref)
+    assert ma <= F32_MAX_ABS and rf <= F32_REL_FROB, (ma, rf)
+
+
+def test_vit_l16_workload_full():
+    w = synth.WORKLOADS["vit_l16"]
+    q, k, v = synth.draw_workload(w)
+    qf, kf, vf = (widen(x, BF) for x in (q, k, v))
+    log("workload vit_l16: pack -> attention x4 -> unpack")
+    out = _ulysses_gpu(w, q, k, v, F)
+    par = A.attention_parallel(qf, kf, vf)
+    ref = np.empty(out.shape)
+    for (b, hd), (rows, o, _) in par.items():
+        ref[b, rows, hd] = o
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+
+
+def _sample_rows(S, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, S - 2, S - 1], rng.choice(S, n, replace=False)]))
+
+
+def _risky_rows(qf, kf, b, hd, n):
+    """Query rows whose softmax is dominated by few keys: the rows with the
+    largest scores against the largest-norm keys (the scaled keys of the
+    peaky workload), where bf16 rounding of the weights matters most."""
+    K = kf[b, :, hd]
+    big = np.argsort(np.einsum("sd,sd->s", K, K))[-max(1, K.shape[0] // 100):]
+    sc = qf[b, :, hd] @ K[big].T
+    top2 = np.sort(np.partition(sc, -2, axis=1)[:, -2:], axis=1)
+    # large top score, and a close runner-up (two comparable dominant weights)
+    order1 = np.argsort(top2[:, 1])[-n // 2:]
+    order2 = np.argsort(top2[:, 1] - 4.0 * np.abs(top2[:, 1] - top2[:, 0]))[-n // 2:]
+    return np.unique(np.concatenate([order1, order2]))
+
+
+def _check_sampled(out, q, k, v, dtype, B, S, rows_per_head, lse=None):
+    """Compare ``out`` against the oracle on ``rows_per_head[(b, head)]``."""
+    qf, kf, vf = (widen(x, dtype) for x in (q, k, v))
+    par = A.attention_parallel(qf, kf, vf, rows_per_head=rows_per_head,
+                               workers=min(16, A.host_cores()))
+    got, ref, lg, lr = [], [], [], []
+    for (b, hd), (rows, o, ls) in par.items():
+        got.append(out[b, rows, hd]); ref.append(o)
+        if lse is not None:
+            lg.append(lse[b, hd, rows]); lr.append(ls)
+    ma, rf = err(np.concatenate(got), np.concatenate(ref))
+    log(f"sampled parity: {sum(len(r) for r in rows_per_head.values())} rows "
+        f"max_abs={ma:.3e} rel_frob={rf:.3e}")
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    if lse is not None:
+        assert np.max(np.abs(np.concatenate(lg) - np.concatenate(lr))) <= 1e-3
+    return ma, rf
+
+
+def test_video_dit_share_full_size():
+    import torch
+    w = synth.WORKLOADS["video_dit_share"]
+    q, k, v = synth.draw_workload(w)
+    hb = R.balanced_ranges(w.H, w.P)
+    h0 = hb[1] - hb[0]
+    # head-group block 0 (rank 0's share) through the GPU pack, attention there
+    blocks = []
+    for x in (q, k, v):
+        bl = [poisoned((w.B, w.S, hb[j + 1] - hb[j], w.D), BF) for j in range(w.P)]
+        log("workload video_dit_share: pack world")
+        usp.usp_pack_seq_to_heads(to_dev(x, BF), bl)
+        blocks.append(bl[0])
+        del bl
+    o = poisoned((w.B, w.S, h0, w.D), F)
+    lse = torch.empty((w.B, h0, w.S), device=DEV)
+    log("workload video_dit_share: attention block 0 (h=5, S=32760)")
+    usp.usp_attention_fwd(blocks[0], blocks[1], blocks[2], o, lse=lse)
+    torch.cuda.synchronize()
+    out = to_host(o)
+    assert not np.any(np.isnan(out))
+    sl = slice(hb[0], hb[1])
+    rows = {(0, hd): _sample_rows(w.S, 256, 30 + hd) for hd in range(h0)}
+    _check_sampled(out, q[:, :, sl], k[:, :, sl], v[:, :, sl], BF, w.B, w.S, rows,
+                   lse=lse.cpu().numpy())
+
+
+def test_long_chunked_full_size():
+    w = synth.WORKLOADS["long_chunked"]
+    q, k, v = synth.draw_workload(w)
+    log("workload long_chunked: single shot (S=131072, h=8)")
+    one = _run(q, k, v, BF, F)
+    log("workload long_chunked: 3 head-chunk passes")
+    many = _run(q, k, v, BF, F, chunks=w.chunks)
+    assert usp.usp_head_chunk_ranges(w.H, w.chunks) == [0, 3, 6, 8]
+    assert one.tobytes() == many.tobytes()
+    assert not np.any(np.isnan(one))
+    rows = {(0, hd): _sample_rows(w.S, 64, 40 + hd) for hd in range(w.H)}
+    _check_sampled(one, q, k, v, BF, w.B, w.S, rows)
+
+
+def test_indivisible_long_full_size():
+    w = synth.WORKLOADS["indivisible_long"]
+    q, k, v = synth.draw_workload(w)
+    log("workload indivisible_long: pack -> attention x4 -> unpack (S=65537)")
+    out = _ulysses_gpu(w, q, k, v, F)
+    assert not np.any(np.isnan(out))
+    kf = widen(k, BF)
+    qf = widen(q, BF)
+    rows = {}
+    for b in range(w.B):
+        for hd in range(w.H):
+            r = _sample_rows(w.S, 48, 50 + 31 * b + hd)
+            if hd % 4 == 0:   # the riskiest rows of a third of the heads
+                r = np.unique(np.concatenate([r, _risky_rows(qf, kf, b, hd, 400)]))
+            rows[(b, hd)] = r
+    del kf, qf
+    _check_sampled(out, q, k, v, BF, w.B, w.S, rows)

@@ -1,0 +1,110 @@
+"""GPU parity of ranges and relayouts against the oracle: bit-exact.
+
+Inputs are index-coded (each element holds its own flat index) and outputs
+start poisoned (NaN patterns), so a missed, doubled or misplaced element
+fails the byte compare."""
+import numpy as np
+import pytest
+
+import ulysses_sequence_attention_amd as usp
+from oracle import ranges as R
+from oracle import relayout as X
+from ulysses_sequence_attention_amd import synth
+
+from gpu_util import DEV, log, poisoned, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+BF, F = synth.BF16, synth.F32
+
+WORLD_CASES = [  # B, S, H, D, P, dtype
+    (1, 257, 6, 64, 3, F),       # tiny fp32 workload
+    (32, 577, 16, 64, 4, BF),    # ViT-L/16 workload
+    (2, 37, 7, 64, 3, BF),       # ragged heads 3/2/2, ragged tokens
+    (1, 100, 10, 128, 4, F),     # ragged heads 3/3/2/2
+    (1, 64, 64, 8, 64, BF),      # P at its maximum, 16-byte heads
+    (3, 11, 5, 16, 1, BF),       # P = 1
+    (2, 9, 9, 4, 9, F),          # one head and one token per rank
+]
+
+
+def test_device_ranges():
+    import torch
+    for total, parts in [(257, 3), (577, 4), (32760, 8), (65537, 4), (12, 4), (40, 8), (1, 1),
+                         (2**40 + 7, 64), (1000, 999)]:
+        log(f"usp_balanced_ranges_device total={total} parts={parts}")
+        out = torch.full((parts + 1,), -1, dtype=torch.int64, device=DEV)
+        usp.usp_balanced_ranges_device(total, parts, out)
+        torch.cuda.synchronize()
+        assert out.cpu().tolist() == R.balanced_ranges(total, parts)
+
+
+def _world_roundtrip(B, S, H, D, P, dtype):
+    import torch
+    seq = synth.index_coded((B, S, H, D), dtype)
+    ref_blocks = X.pack_seq_to_heads(seq, P)
+    hb = R.balanced_ranges(H, P)
+    d_seq = to_dev(seq, dtype)
+    blocks = [poisoned((B, S, hb[j + 1] - hb[j], D), dtype) for j in range(P)]
+    log(f"pack world B={B} S={S} H={H} D={D} P={P} {dtype}")
+    usp.usp_pack_seq_to_heads(d_seq, blocks)
+    torch.cuda.synchronize()
+    for j in range(P):
+        assert to_host(blocks[j]).tobytes() == ref_blocks[j].tobytes(), f"block {j}"
+    back = poisoned((B, S, H, D), dtype)
+    log(f"unpack world B={B} S={S} H={H} D={D} P={P} {dtype}")
+    usp.usp_unpack_heads_to_seq(blocks, back)
+    torch.cuda.synchronize()
+    assert to_host(back).tobytes() == seq.tobytes()
+
+
+@pytest.mark.parametrize("B,S,H,D,P,dtype", WORLD_CASES)
+def test_world_pack_unpack(B, S, H, D, P, dtype):
+    _world_roundtrip(B, S, H, D, P, dtype)
+
+
+def test_world_pack_unpack_indivisible_long():
+    _world_roundtrip(2, 65537, 12, 64, 4, BF)
+
+
+def test_world_pack_unpack_video_dit():
+    _world_roundtrip(1, 32760, 40, 128, 8, BF)
+
+
+@pytest.mark.parametrize("B,S,H,D,P,dtype", [(1, 257, 6, 64, 3, F), (2, 37, 7, 64, 3, BF),
+                                             (2, 65537, 12, 64, 4, BF), (1, 9, 9, 8, 9, BF)])
+def test_rank_share_pack_unpack(B, S, H, D, P, dtype):
+    import torch
+    seq = synth.index_coded((B, S, H, D), dtype)
+    world = X.pack_seq_to_heads(seq, P)
+    hb = R.balanced_ranges(H, P)
+    tb = R.balanced_ranges(S, P)
+    for r in range(P):
+        shard = X.scatter_sequence(seq, P, r)
+        blocks = [poisoned((B, S, hb[j + 1] - hb[j], D), dtype) for j in range(P)]
+        log(f"pack rank {r} B={B} S={S} H={H} D={D} P={P} {dtype}")
+        usp.usp_pack_seq_to_heads(to_dev(shard, dtype), blocks, rank=r)
+        torch.cuda.synchronize()
+        for j in range(P):
+            got = to_host(blocks[j])
+            # rank r's rows equal the world pack, every other row is untouched
+            assert got[:, tb[r]:tb[r + 1]].tobytes() == world[j][:, tb[r]:tb[r + 1]].tobytes()
+            poison = to_host(poisoned((1,), dtype)).tobytes()
+            rest = np.concatenate([got[:, :tb[r]], got[:, tb[r + 1]:]], axis=1)
+            assert rest.tobytes() == poison * rest.size
+        d_world = [to_dev(w, dtype) for w in world]
+        out = poisoned(shard.shape, dtype)
+        log(f"unpack rank {r}")
+        usp.usp_unpack_heads_to_seq(d_world, out, rank=r)
+        torch.cuda.synchronize()
+        assert to_host(out).tobytes() == X.unpack_rank_share(world, H, r).tobytes()
+
+
+def test_p1_is_byte_identical():
+    import torch
+    x = synth.draw_qkv(2, 33, 3, 64, 11)[0]
+    blk = poisoned((2, 33, 3, 64), BF)
+    log("pack P=1")
+    usp.usp_pack_seq_to_heads(to_dev(x, BF), [blk])
+    torch.cuda.synchronize()
+    assert to_host(blk).tobytes() == x.tobytes()

@@ -1,0 +1,181 @@
+"""ctypes binding of libusp.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls (include/usp.h) and
+takes PyTorch tensors for device buffers (PyTorch provides device memory and
+streams; all work runs in the library's HIP kernels). Shapes become integer
+arguments, dtypes the usp_dtype enum, tensors their data pointers, and the
+stream defaults to PyTorch's current stream on the tensor's device. A
+negative status raises ``UspError`` with the library's message.
+
+The library must have been built (``python -m ulysses_sequence_attention_amd.build``);
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libusp.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "usp.h")
+
+USP_F32, USP_BF16 = 0, 1
+STATUS = {0: "USP_OK", -1: "USP_EINVAL", -2: "USP_ESHAPE", -3: "USP_EDTYPE", -4: "USP_EALIGN",
+          -5: "USP_ENOSYS", -6: "USP_EHIP"}
+USP_MAX_PARTS = 64
+
+_i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class UspError(RuntimeError):
+    def __init__(self, status: int, fn: str, message: str):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {message}")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libusp.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m ulysses_sequence_attention_amd.build`")
+        # PyTorch ships its own HIP runtime (libamdhip64.so.7). Load it first so
+        # libusp's dependency on that soname resolves to the same copy: one HIP
+        # runtime per process. Loading libusp first would bring in the system
+        # runtime and leave PyTorch running on a runtime it was not built for.
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        L.usp_last_error.restype = ctypes.c_char_p
+        L.usp_last_error.argtypes = []
+        L.usp_version.restype = ctypes.c_char_p
+        L.usp_version.argtypes = []
+        L.usp_balanced_ranges.argtypes = [_i64, _i32, ctypes.POINTER(_i64)]
+        L.usp_balanced_ranges_device.argtypes = [_i64, _i32, _vp, _vp]
+        L.usp_head_chunk_ranges.argtypes = [_i32, _i32, ctypes.POINTER(_i32)]
+        rel = [_vp, _vp, ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
+        L.usp_pack_seq_to_heads.argtypes = rel
+        L.usp_unpack_heads_to_seq.argtypes = rel
+        L.usp_attention_fwd.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
+                                        _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
+        L.usp_attention_fwd_chunked.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                                _i64, _i64, _i32, _i32, _f32, _vp, _i32, _vp]
+        for name in ("usp_balanced_ranges", "usp_balanced_ranges_device", "usp_head_chunk_ranges",
+                     "usp_pack_seq_to_heads", "usp_unpack_heads_to_seq", "usp_attention_fwd",
+                     "usp_attention_fwd_chunked"):
+            getattr(L, name).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/usp.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(usp_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, fn: str) -> None:
+    if status != 0:
+        raise UspError(status, fn, lib().usp_last_error().decode())
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return USP_F32
+    if t.dtype == torch.bfloat16:
+        return USP_BF16
+    return 99  # rejected by the library with USP_EDTYPE
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libusp must be contiguous")
+    return t.data_ptr()
+
+
+def usp_version() -> str:
+    return lib().usp_version().decode()
+
+
+def usp_last_error() -> str:
+    return lib().usp_last_error().decode()
+
+
+def usp_balanced_ranges(total: int, parts: int) -> list[int]:
+    """Host boundaries [0, ..., total] of ``parts`` balanced ranges."""
+    n = max(int(parts), 0) + 1
+    buf = (_i64 * n)()
+    _check(lib().usp_balanced_ranges(total, parts, buf), "usp_balanced_ranges")
+    return list(buf)
+
+
+def usp_balanced_ranges_device(total: int, parts: int, out, stream=None) -> None:
+    """Boundaries into the device int64 tensor ``out`` (parts + 1 elements)."""
+    _check(lib().usp_balanced_ranges_device(total, parts, _ptr(out), _stream(out, stream)),
+           "usp_balanced_ranges_device")
+
+
+def usp_head_chunk_ranges(heads: int, chunks: int) -> list[int]:
+    n = max(int(chunks), 0) + 1
+    buf = (_i32 * n)()
+    _check(lib().usp_head_chunk_ranges(heads, chunks, buf), "usp_head_chunk_ranges")
+    return list(buf)
+
+
+def _relayout_dims(seq, blocks, rank):
+    B, L, H, D = seq.shape
+    S = blocks[0].shape[1] if rank >= 0 else L
+    return B, S, H, D
+
+
+def usp_pack_seq_to_heads(seq, blocks, rank: int = -1, stream=None) -> None:
+    """seq [B,S,H,D] (world, rank < 0) or rank's shard [B,len_r,H,D] ->
+    blocks[j] [B,S,h_j,D]; P = len(blocks)."""
+    P = len(blocks)
+    arr = (_vp * max(P, 1))(*[_ptr(b) for b in blocks])
+    B, S, H, D = _relayout_dims(seq, blocks, rank)
+    _check(lib().usp_pack_seq_to_heads(_ptr(seq), arr, _dtype(seq), B, S, H, D, P, rank,
+                                       _stream(seq, stream)), "usp_pack_seq_to_heads")
+
+
+def usp_unpack_heads_to_seq(blocks, seq, rank: int = -1, stream=None) -> None:
+    """blocks[j] [B,S,h_j,D] -> seq [B,S,H,D] (world) or rank's shard."""
+    P = len(blocks)
+    arr = (_vp * max(P, 1))(*[_ptr(b) for b in blocks])
+    B, S, H, D = _relayout_dims(seq, blocks, rank)
+    _check(lib().usp_unpack_heads_to_seq(arr, _ptr(seq), _dtype(seq), B, S, H, D, P, rank,
+                                         _stream(seq, stream)), "usp_unpack_heads_to_seq")
+
+
+def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
+                      lse=None, stream=None) -> None:
+    """Attention over heads [head_lo, head_hi) of q, k, v, o [B,S,h,D]."""
+    B, S, h, D = q.shape
+    hi = h if head_hi is None else head_hi
+    _check(lib().usp_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B, S,
+                                   h, D, head_lo, hi, scale, _ptr(lse), _stream(q, stream)),
+           "usp_attention_fwd")
+
+
+def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=None,
+                              stream=None) -> None:
+    """Attention as ``chunks`` head-chunk passes (bitwise equal to single shot)."""
+    B, S, h, D = q.shape
+    _check(lib().usp_attention_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
+                                           _dtype(o), B, S, h, D, scale, _ptr(lse), chunks,
+                                           _stream(q, stream)), "usp_attention_fwd_chunked")

@@ -1,0 +1,65 @@
+"""Build libusp.so (HIP, gfx950) in-tree.
+
+Usage: ``python -m ulysses_sequence_attention_amd.build [--verbose]``.
+Compiles every ``csrc/*.hip`` with hipcc for gfx950 into ``_build/`` at the
+repository root and links ``ulysses_sequence_attention_amd/libusp.so``.
+Always recompiles (the build check must compile every time it is asked to).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libusp.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+    # packed fp32 VALU ops stay off (the compiler still emits scalar fp32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    return r.stdout + r.stderr
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    flags = FLAGS + list(extra_flags or [])
+    objs = []
+    jobs = []
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        for src in sources:
+            obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+            objs.append(obj)
+            jobs.append(ex.submit(_run, [HIPCC, *flags, "-c", src, "-o", obj], verbose))
+        logs = [j.result() for j in jobs]
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    if verbose:
+        for log in logs:
+            if log.strip():
+                print(log)
+    return LIB
+
+
+if __name__ == "__main__":
+    extra = [a for a in sys.argv[1:] if a != "--verbose"]
+    print(build(verbose="--verbose" in sys.argv, extra_flags=extra))

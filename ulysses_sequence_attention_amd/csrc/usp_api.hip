@@ -1,0 +1,217 @@
+// libusp C ABI: argument validation, error reporting, host-side ranges and
+// dispatch to the HIP kernels. See include/usp.h for the contract of each call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "usp_internal.h"
+
+namespace usp {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return USP_OK;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(USP_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return USP_OK;
+}
+
+// Balanced contiguous ranges (h3-blackwell-runtime distributed.py,
+// balanced_ranges): base = total / parts, the first total % parts ranges take
+// one extra item.
+static int check_ranges(int64_t total, int32_t parts) {
+  if (parts < 1) return fail(USP_EINVAL, "parts must be positive (got %d)", parts);
+  if (total < parts)
+    return fail(USP_EINVAL, "cannot split %lld items into %d non-empty ranges",
+                (long long)total, parts);
+  return USP_OK;
+}
+
+static void host_bounds(int64_t total, int32_t parts, int64_t* bounds) {
+  const int64_t base = total / parts, extra = total % parts;
+  for (int32_t r = 0; r <= parts; ++r) bounds[r] = r * base + (r < extra ? r : extra);
+}
+
+static int esize_of(usp_dtype dt) { return dt == USP_F32 ? 4 : dt == USP_BF16 ? 2 : 0; }
+
+// Overflow-checked product of non-negative int64 factors.
+static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+static int check_relayout(const void* seq, const void* const* blk, usp_dtype dt, int64_t B,
+                          int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank) {
+  if (P < 1 || P > USP_MAX_PARTS)
+    return fail(USP_EINVAL, "P must be in [1, %d] (got %d)", USP_MAX_PARTS, P);
+  if (S < P) return fail(USP_EINVAL, "cannot split %lld tokens over %d ranks", (long long)S, P);
+  if (H < P) return fail(USP_EINVAL, "cannot split %d heads over %d ranks", H, P);
+  if (rank >= P) return fail(USP_EINVAL, "rank %d out of range for P = %d", rank, P);
+  if (B < 1 || D < 1) return fail(USP_ESHAPE, "B and D must be positive");
+  const int es = esize_of(dt);
+  if (!es) return fail(USP_EDTYPE, "unsupported dtype %d", (int)dt);
+  if ((int64_t(D) * es) % 16)
+    return fail(USP_EALIGN, "D * element size (%d bytes) must be a multiple of 16", D * es);
+  int64_t n;
+  if (!mul_ok(B, S, &n) || !mul_ok(n, H, &n) || !mul_ok(n, D, &n) || !mul_ok(n, es, &n))
+    return fail(USP_ESHAPE, "tensor size overflows");
+  if (!seq || !blk) return fail(USP_EINVAL, "null seq or block array");
+  if (!aligned16(seq)) return fail(USP_EALIGN, "seq pointer is not 16-byte aligned");
+  for (int32_t j = 0; j < P; ++j) {
+    if (!blk[j]) return fail(USP_EINVAL, "block pointer %d is null", j);
+    if (!aligned16(blk[j])) return fail(USP_EALIGN, "block pointer %d is not 16-byte aligned", j);
+  }
+  return USP_OK;
+}
+
+static int check_attention(const AttnArgs& a) {
+  if (!a.q || !a.k || !a.v || !a.o) return fail(USP_EINVAL, "null q, k, v or o");
+  if (a.h < 1) return fail(USP_EINVAL, "h must be positive");
+  if (a.head_lo < 0 || a.head_hi > a.h || a.head_lo >= a.head_hi)
+    return fail(USP_EINVAL, "head range [%d, %d) is empty or outside [0, %d)", a.head_lo,
+                a.head_hi, a.h);
+  if (a.B < 1 || a.S < 1) return fail(USP_ESHAPE, "B and S must be positive");
+  const int es = esize_of(a.in_dt);
+  if (!es) return fail(USP_EDTYPE, "unsupported input dtype %d", (int)a.in_dt);
+  if (a.out_dt != USP_F32 && a.out_dt != USP_BF16)
+    return fail(USP_EDTYPE, "unsupported output dtype %d", (int)a.out_dt);
+  if (a.in_dt == USP_F32 && a.out_dt != USP_F32)
+    return fail(USP_EDTYPE, "fp32 inputs require an fp32 output");
+  if (a.in_dt == USP_BF16 && a.D != 64 && a.D != 128)
+    return fail(USP_ENOSYS, "bf16 attention supports D in {64, 128} (got %d)", a.D);
+  if (a.in_dt == USP_F32 && a.D != 32 && a.D != 64 && a.D != 128)
+    return fail(USP_ENOSYS, "fp32 attention supports D in {32, 64, 128} (got %d)", a.D);
+  int64_t n;
+  if (!mul_ok(a.B, a.S, &n) || !mul_ok(n, a.h, &n) || !mul_ok(n, a.D, &n) ||
+      !mul_ok(n, 4, &n))
+    return fail(USP_ESHAPE, "tensor size overflows");
+  if (a.S > (int64_t(1) << 31) - 1024 || a.B * a.h > (int64_t(1) << 31) - 1)
+    return fail(USP_ESHAPE, "S or B * h too large for one launch");
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.o))
+    return fail(USP_EALIGN, "q, k, v and o must be 16-byte aligned");
+  if (a.lse && (reinterpret_cast<uintptr_t>(a.lse) & 3u))
+    return fail(USP_EALIGN, "lse must be 4-byte aligned");
+  return USP_OK;
+}
+
+static int run_attention(const AttnArgs& a, hipStream_t s) {
+  return a.in_dt == USP_F32 ? launch_attention_f32(a, s) : launch_attention_bf16(a, s);
+}
+
+}  // namespace usp
+
+using namespace usp;
+
+extern "C" {
+
+const char* usp_last_error(void) { return g_last_error.c_str(); }
+
+const char* usp_version(void) { return "usp 0.1.0 gfx950"; }
+
+int usp_balanced_ranges(int64_t total, int32_t parts, int64_t* bounds) {
+  if (int st = check_ranges(total, parts)) return st;
+  if (!bounds) return fail(USP_EINVAL, "bounds is null");
+  host_bounds(total, parts, bounds);
+  return ok();
+}
+
+int usp_balanced_ranges_device(int64_t total, int32_t parts, int64_t* d_bounds, void* stream) {
+  if (int st = check_ranges(total, parts)) return st;
+  if (!d_bounds) return fail(USP_EINVAL, "d_bounds is null");
+  if (reinterpret_cast<uintptr_t>(d_bounds) & 7u) return fail(USP_EALIGN, "d_bounds misaligned");
+  if (int st = launch_ranges_device(total, parts, d_bounds, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_head_chunk_ranges(int32_t heads, int32_t chunks, int32_t* bounds) {
+  if (heads < 1) return fail(USP_EINVAL, "heads must be positive (got %d)", heads);
+  if (chunks < 1) return fail(USP_EINVAL, "chunks must be positive (got %d)", chunks);
+  if (chunks > heads)
+    return fail(USP_EINVAL, "cannot run %d heads in %d non-empty chunks", heads, chunks);
+  if (!bounds) return fail(USP_EINVAL, "bounds is null");
+  const int32_t size = (heads + chunks - 1) / chunks;
+  // every chunk non-empty <=> (chunks - 1) * size < heads
+  if (int64_t(chunks - 1) * size >= heads)
+    return fail(USP_EINVAL, "%d chunks of %d heads leave a chunk empty for %d heads", chunks,
+                size, heads);
+  for (int32_t c = 0; c < chunks; ++c) bounds[c] = c * size;
+  bounds[chunks] = heads;
+  return ok();
+}
+
+int usp_pack_seq_to_heads(const void* seq, void* const* blk, usp_dtype dtype, int64_t B,
+                          int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                          void* stream) {
+  if (int st = check_relayout(seq, (const void* const*)blk, dtype, B, S, H, D, P, rank))
+    return st;
+  RelayoutArgs a{seq, nullptr, nullptr, blk, B, S, H, D, P, rank < 0 ? -1 : rank,
+                 esize_of(dtype)};
+  if (int st = launch_relayout(a, true, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
+                            int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                            void* stream) {
+  if (int st = check_relayout(seq, blk, dtype, B, S, H, D, P, rank)) return st;
+  RelayoutArgs a{nullptr, seq, blk, nullptr, B, S, H, D, P, rank < 0 ? -1 : rank,
+                 esize_of(dtype)};
+  if (int st = launch_relayout(a, false, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
+                      usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
+                      int32_t head_lo, int32_t head_hi, float scale, float* lse, void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt};
+  if (int st = check_attention(a)) return st;
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,
+                              usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
+                              int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
+                              void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, 0, h, scale, in_dt, out_dt};
+  if (int st = check_attention(a)) return st;
+  if (chunks < 1 || chunks > h)
+    return fail(USP_EINVAL, "cannot run %d heads in %d non-empty chunks", h, chunks);
+  int32_t bounds[USP_MAX_PARTS + 1];
+  int32_t* hb = bounds;
+  std::string heap;  // large chunk counts: bounds on the heap
+  if (chunks > USP_MAX_PARTS) {
+    heap.resize(sizeof(int32_t) * (chunks + 1));
+    hb = reinterpret_cast<int32_t*>(&heap[0]);
+  }
+  if (int st = usp_head_chunk_ranges(h, chunks, hb)) return st;
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  for (int32_t c = 0; c < chunks; ++c) {
+    a.head_lo = hb[c];
+    a.head_hi = hb[c + 1];
+    if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal helpers of libusp (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/usp.h"
+
+namespace usp {
+
+// Record a status and message for usp_last_error(); returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the thread's message and return USP_OK.
+int ok();
+// Translate the last HIP launch status into USP_EHIP (or USP_OK).
+int check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Unsigned division by a run-time invariant d >= 1 for dividends n < 2^31,
+// as a multiply-high and a shift (Granlund & Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, round-up variant):
+// shift = ceil(log2 d), mul = floor(2^32 (2^shift - d) / d) + 1,
+// n / d = (mulhi(n, mul) + n) >> shift.
+struct FastDiv {
+  uint32_t d, mul, shift;
+  FastDiv() : d(1), mul(1), shift(0) {}
+  explicit FastDiv(uint32_t divisor) : d(divisor) {
+    shift = 0;
+    while ((1ull << shift) < divisor) ++shift;
+    mul = (uint32_t)(((1ull << 32) * ((1ull << shift) - divisor)) / divisor + 1);
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (__umulhi(n, mul) + n) >> shift;
+  }
+};
+
+// Kernel launchers (one per translation unit).
+int launch_ranges_device(int64_t total, int32_t parts, int64_t* d_bounds, hipStream_t s);
+
+struct RelayoutArgs {
+  const void* seq_in;          // pack: source seq; unpack: unused
+  void* seq_out;               // unpack: destination seq; pack: unused
+  const void* const* blk_in;   // unpack: P source blocks
+  void* const* blk_out;        // pack: P destination blocks
+  int64_t B, S;
+  int32_t H, D, P, rank, esize;
+};
+int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s);
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int64_t B, S;
+  int32_t h, D, head_lo, head_hi;
+  float scale;
+  usp_dtype in_dt, out_dt;
+};
+int launch_attention_f32(const AttnArgs& a, hipStream_t s);
+int launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+
+}  // namespace usp
