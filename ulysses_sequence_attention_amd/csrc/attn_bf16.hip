@@ -5,12 +5,20 @@
 // run on the full sequence of the rank's head group): per head n,
 //   O[s] = sum_t softmax_t(scale * <Q[s], K[t]>) V[t].
 //
-// Work decomposition. A workgroup of 4 waves owns BM = 4 * 64 query rows of
-// one (batch, head); each wave owns 64 rows as two 32-row MFMA blocks. The
-// keys are walked in tiles of BN rows (64 for D = 128, 128 for D = 64), each
-// tile staged in LDS (K row-major, V transposed), double buffered: the next
-// tile's global loads are issued before the current tile's math and written
-// to the other LDS buffer after it, with one barrier per tile.
+// Work decomposition. A workgroup of NW waves owns BM = NW * QB * 32 query
+// rows of one (batch, head); each wave owns QB blocks of 32 rows (one MFMA
+// column block each). Keys are walked in tiles of BN rows staged in LDS (K
+// row-major, V transposed). With 8 waves of 32 rows, two waves share each
+// SIMD.
+//
+// Software pipeline. K is staged one tile ahead of V: while iteration j
+// turns the scores of tile j into weights (exp2, VALU), the same basic block
+// computes the scores of tile j + 1 (MFMA), so the matrix pipe and the VALU
+// work at once inside one wave; then the weights of tile j multiply V_j.
+// LDS holds two K tiles and two V^T tiles; the global loads of K_{j+2} and
+// V_{j+1} are issued at the top of iteration j and written to LDS at its end,
+// with one barrier per tile. The last (possibly partial) tile is peeled off
+// the loop so the steady-state body carries no key mask.
 //
 // Layout trick. The score block is computed transposed, S^T = K Q^T (A = K,
 // B = Q^T), so a lane of the 32x32 accumulator holds 16 keys of ONE query
@@ -53,8 +61,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+// Tile shapes (waves per workgroup, 32-row query blocks per wave, keys per
+// tile) per head dim.
+#ifndef USP_D128_WAVES
+#define USP_D128_WAVES 8
+#define USP_D128_QB 1
+#define USP_D128_BN 64
+#endif
+#ifndef USP_D64_WAVES
+#define USP_D64_WAVES 8
+#define USP_D64_QB 1
+#define USP_D64_BN 128
+#endif
+
 constexpr float kTau = 1.0f;  // lazy-rescale threshold, log2 units
 
 struct Params {
@@ -70,27 +89,48 @@ struct Params {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ uint32_t half16(const uint4& u, int j) {
-  const uint32_t w = (j >> 1) == 0 ? u.x : (j >> 1) == 1 ? u.y : (j >> 1) == 2 ? u.z : u.w;
-  return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+__device__ __forceinline__ uint32_t word(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
 
-template <int D, int QB, int BN, bool kOutBf16>
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
-  constexpr int BM = kWaves * QB * 32;
+// bf16 element j of a and of b side by side in one dword (a low, b high)
+__device__ __forceinline__ uint32_t pair16(const uint4& a, const uint4& b, int j) {
+  // v_perm_b32 byte select over {b (bytes 4-7), a (bytes 0-3)}
+  return __builtin_amdgcn_perm(word(b, j >> 1), word(a, j >> 1), (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// max / sum of a value with the same value in lane ^ 32 (v_permlane32_swap:
+// with both operands x it returns (x of lanes 0-31, x of lanes 32-63) in
+// both halves)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int NW, int QB, int BN, bool kOutBf16>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
+  constexpr int kThreads = NW * 64;
+  constexpr int BM = NW * QB * 32;
   constexpr int NKB = BN / 32;           // 32-key blocks per tile
   constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;            // 32-wide blocks of the output head dim
   constexpr int KLD = D + 8;             // K tile row stride (elements)
   constexpr int VLD = BN + 8;            // V^T tile row stride (elements)
   constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  constexpr int NKL = BN * CPR / kThreads;        // K chunks per thread per tile
-  constexpr int NVP = (BN / 4) * CPR / kThreads;  // V (4-key x chunk) groups per thread
+  constexpr int NKL = BN * CPR / kThreads;  // K chunks per thread per tile
+  constexpr int G = BN * CPR / kThreads;    // V keys per thread (one 16-byte chunk each)
   static_assert(NKL * kThreads == BN * CPR, "K tile must split evenly over the block");
-  static_assert(NVP * kThreads == (BN / 4) * CPR, "V tile must split evenly over the block");
+  static_assert(G == 1 || G == 2 || G == 4, "V staging handles 1, 2 or 4 keys per thread");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][D * VLD];
+  // LDS: two K tiles, then two V^T tiles
+  constexpr int KT = BN * KLD, VT = D * VLD;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KT + VT)];
+  uint16_t* const ks0 = lds;           // K tile buffer 0 (buffer 1 follows)
+  uint16_t* const vt0 = lds + 2 * KT;  // V^T tile buffer 0 (buffer 1 follows)
 
   // ---- XCD-aware workgroup -> (batch, head, query tile) -------------------
   const int nwg = gridDim.x, bid = blockIdx.x;
@@ -107,6 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   const size_t rs = size_t(p.h) * D;                             // token row stride
   const size_t hb = size_t(b) * S * rs + size_t(head) * D;       // (b, token 0, head)
   const int qrow0 = qt * BM + w * (QB * 32);
+  const float c = p.c;
 
   // ---- Q^T fragments (B operand), resident for the whole key walk --------
   bf16x8 qf[QB][KS];
@@ -121,48 +162,67 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     }
   }
 
-  // ---- K/V tile staging ---------------------------------------------------
+  // ---- K/V tile staging (global -> registers -> LDS) ----------------------
+  // Each thread loads fixed (row, chunk) slots of every tile: a per-lane
+  // 32-bit element offset from the tile's (uniform) base. Only the last tile
+  // can run past S, so only it is loaded with row guards.
   uint4 kreg[NKL];
-  uint4 vreg[NVP][4];
-  auto load_tile = [&](int t0) {
+  uint4 vreg[G];
+  uint32_t koff[NKL], krow[NKL];
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) {
+    const int idx = tid + i * kThreads;
+    krow[i] = idx / CPR;
+    koff[i] = uint32_t(krow[i] * rs + (idx % CPR) * 8);
+  }
+  const int vkq = tid % (BN / G), vch = tid / (BN / G);
+  const uint32_t voff = uint32_t(G * vkq * rs + vch * 8);
+  auto load_k = [&](int t0, bool guard) {
+    const uint16_t* base = p.k + hb + size_t(t0) * rs;
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / CPR, ch = idx % CPR;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (t0 + r < S)
-        kreg[i] = *reinterpret_cast<const uint4*>(p.k + hb + size_t(t0 + r) * rs + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < NVP; ++i) {
-      const int idx = tid + i * kThreads;
-      const int kq = idx % (BN / 4), ch = idx / (BN / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = t0 + 4 * kq + e;
-        vreg[i][e] = make_uint4(0, 0, 0, 0);
-        if (key < S)
-          vreg[i][e] = *reinterpret_cast<const uint4*>(p.v + hb + size_t(key) * rs + ch * 8);
-      }
+      if (!guard || t0 + int(krow[i]) < S)
+        kreg[i] = *reinterpret_cast<const uint4*>(base + koff[i]);
+      else
+        kreg[i] = make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto load_v = [&](int t0, bool guard) {
+    const uint16_t* base = p.v + hb + size_t(t0) * rs;
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      if (!guard || t0 + G * vkq + e < S)
+        vreg[e] = *reinterpret_cast<const uint4*>(base + voff + e * rs);
+      else
+        vreg[e] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
       const int idx = tid + i * kThreads;
       const int r = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(&ks[buf][r * KLD + ch * 8]) = kreg[i];
+      *reinterpret_cast<uint4*>(&ks0[buf * KT + r * KLD + ch * 8]) = kreg[i];
     }
+  };
+  auto store_v = [&](int buf) {
+    // transpose: head-dim element j of the G keys becomes G consecutive keys
+    // of V^T row ch * 8 + j
 #pragma unroll
-    for (int i = 0; i < NVP; ++i) {
-      const int idx = tid + i * kThreads;
-      const int kq = idx % (BN / 4), ch = idx / (BN / 4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j) {
+      uint16_t* dst = &vt0[buf * VT + (vch * 8 + j) * VLD + G * vkq];
+      if constexpr (G == 1) {
+        *dst = uint16_t(word(vreg[0], j >> 1) >> (16 * (j & 1)));
+        continue;
+      }
+      const uint32_t lo = pair16(vreg[0], vreg[G > 1 ? 1 : 0], j);
+      if constexpr (G == 4) {
         uint2 x;
-        x.x = half16(vreg[i][0], j) | (half16(vreg[i][1], j) << 16);
-        x.y = half16(vreg[i][2], j) | (half16(vreg[i][3], j) << 16);
-        *reinterpret_cast<uint2*>(&vt[buf][(ch * 8 + j) * VLD + 4 * kq]) = x;
+        x.x = lo;
+        x.y = pair16(vreg[2], vreg[3], j);
+        *reinterpret_cast<uint2*>(dst) = x;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = lo;
       }
     }
   };
@@ -170,6 +230,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   // K row fed to A-operand row l32 (see the layout note above)
   const int a4 = l32 >> 3, g4 = (l32 >> 2) & 1, c4 = l32 & 3;
   const int pi = 16 * (a4 >> 1) + 8 * g4 + 4 * (a4 & 1) + c4;
+
+  // ---- the per-tile steps ---------------------------------------------------
+  // S^T = K Q^T for the K tile in ks[buf]
+  auto qk = [&](int buf, f32x16 (&sacc)[NKB][QB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 kf = as_bf16x8(
+            *reinterpret_cast<const uint4*>(&ks0[buf * KT + (kb * 32 + pi) * KLD + s * 16 + g * 8]));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sacc[kb][qb], 0, 0, 0);
+      }
+    }
+  };
 
   f32x16 oacc[QB][NDB];
 #pragma unroll
@@ -185,51 +267,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
     lrow[qb] = 0.f;
   }
 
-  const int nkt = (S + BN - 1) / BN;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const bool has_next = kt + 1 < nkt;
-    if (has_next) load_tile((kt + 1) * BN);
-
-    // ---- S^T = K Q^T ------------------------------------------------------
-    f32x16 sacc[NKB][QB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf =
-            as_bf16x8(*reinterpret_cast<const uint4*>(&ks[buf][(kb * 32 + pi) * KLD + s * 16 + g * 8]));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sacc[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask keys past the end (last tile only) ---------------------------
-    if ((kt + 1) * BN > S) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * BN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= S) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[kb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // ---- online softmax ------------------------------------------------------
+  // row maxima of a score tile, moving the reference maxima (and rescaling O
+  // and the row sums) where a row's maximum grew by more than kTau
+  auto update_max = [&](f32x16 (&sacc)[NKB][QB]) {
     float mnew[QB];
     bool need[QB];
     bool any_need = false;
@@ -240,26 +280,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_halves(mx);
       mnew[qb] = fmaxf(mrow[qb], mx);
-      need[qb] = (mnew[qb] - mrow[qb]) * p.c > kTau;
+      need[qb] = (mnew[qb] - mrow[qb]) * c > kTau;
       any_need |= need[qb];
     }
     if (__any(any_need)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float mu = need[qb] ? mnew[qb] : mrow[qb];
-        const float alpha = __builtin_amdgcn_exp2f((mrow[qb] - mu) * p.c);
+        const float alpha = __builtin_amdgcn_exp2f((mrow[qb] - mu) * c);
         lrow[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
         mrow[qb] = mu;
       }
     }
-    bf16x8 pf[QB][NKB][2];
+  };
+
+  // weights exp2(c s - c m) rounded to bf16 (the B operand of the P V
+  // product) and their row sums
+  auto weights = [&](f32x16 (&sacc)[NKB][QB], bf16x8 (&pf)[QB][NKB][2]) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float mc = mrow[qb] * p.c;
+      const float mc = mrow[qb] * c;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -268,10 +313,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
           f32x8 pv;
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * h2 + j], p.c, -mc));
+            pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * h2 + j], c, -mc));
           const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
           pf[qb][kb][h2] = pb;
-          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
           ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, ls, false);
           ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, ls, false);
           ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, ls, false);
@@ -280,16 +324,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
       }
       lrow[qb] += ls;
     }
+  };
 
-    // ---- O^T += V^T P^T ----------------------------------------------------
+  // O^T += V^T P^T for the V tile in vt[buf]
+  auto pv = [&](int buf, bf16x8 (&pf)[QB][NKB][2]) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
+        for (int db = 0; db < NDB; ++db) {
           const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4*>(
-              &vt[buf][(db * 32 + l32) * VLD + kb * 32 + h2 * 16 + g * 8]));
+              &vt0[buf * VT + (db * 32 + l32) * VLD + kb * 32 + h2 * 16 + g * 8]));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             oacc[qb][db] =
@@ -297,15 +343,85 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
         }
       }
     }
+  };
 
-    if (has_next) store_tile(buf ^ 1);
+  // keys at or past S get score -inf (weight 0)
+  auto mask = [&](f32x16 (&sacc)[NKB][QB], int tile) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = tile * BN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+        if (key >= S) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sacc[kb][qb][r] = -INFINITY;
+        }
+      }
+  };
+
+  const int nkt = (S + BN - 1) / BN;
+  auto key0 = [&](int kt) { return kt * BN; };                // first key of tile kt
+  auto partial = [&](int kt) { return key0(kt) + BN > S; };   // tile runs past S
+
+  // ---- prologue: K_0, V_0, K_1 in LDS; scores of tile 0 -------------------
+  load_k(key0(0), partial(0));
+  load_v(key0(0), partial(0));
+  store_k(0);
+  store_v(0);
+  if (nkt > 1) {
+    load_k(key0(1), partial(1));
+    store_k(1);
+  }
+  __syncthreads();
+
+  f32x16 sa[NKB][QB], sb[NKB][QB];
+  qk(0, sa);
+  __syncthreads();  // every wave has read K_0 before step 0 refills buffer 0 with K_2
+
+  // one steady-state iteration on tile kt (< nkt - 1): `cur` holds the scores
+  // of tile kt, `nxt` receives those of tile kt + 1
+  auto step = [&](int kt, f32x16 (&cur)[NKB][QB], f32x16 (&nxt)[NKB][QB]) {
+    const bool has2 = kt + 2 < nkt;
+    if (has2) load_k(key0(kt + 2), partial(kt + 2));
+    load_v(key0(kt + 1), partial(kt + 1));
+    if (partial(kt)) mask(cur, kt);
+    update_max(cur);
+    bf16x8 pf[QB][NKB][2];
+    qk((kt + 1) & 1, nxt);  // MFMA: scores of the next tile ...
+    weights(cur, pf);       // ... while the VALU turns this tile into weights
+    pv(kt & 1, pf);
+    if (has2) store_k(kt & 1);
+    store_v((kt + 1) & 1);
     __syncthreads();
+  };
+
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    step(kt, sa, sb);
+    step(kt + 1, sb, sa);
+  }
+  if (kt + 1 < nkt) {
+    step(kt, sa, sb);
+    ++kt;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = sb[kb][qb];
+  }
+
+  // ---- last tile -------------------------------------------------------------
+  {
+    if (partial(kt)) mask(sa, kt);
+    update_max(sa);
+    bf16x8 pf[QB][NKB][2];
+    weights(sa, pf);
+    pv(kt & 1, pf);
   }
 
   // ---- epilogue: normalise and store ------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lrow[qb] + __shfl_xor(lrow[qb], 32);
+    const float lt = sum_halves(lrow[qb]);
     const float inv = 1.0f / lt;
     const int row = qrow0 + qb * 32 + l32;
     if (row < S) {
@@ -334,9 +450,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(Params p) {
   }
 }
 
-template <int D, int QB, int BN>
+template <int D, int NW, int QB, int BN>
 int launch(const AttnArgs& a, hipStream_t s) {
-  constexpr int BM = kWaves * QB * 32;
+  constexpr int BM = NW * QB * 32;
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -353,9 +469,9 @@ int launch(const AttnArgs& a, hipStream_t s) {
   const int64_t grid = int64_t(p.n_qtiles) * p.nheads * a.B;
   if (grid > 0x7fffffff) return fail(USP_ESHAPE, "attention grid too large");
   if (a.out_dt == USP_BF16)
-    attn_bf16_kernel<D, QB, BN, true><<<unsigned(grid), kThreads, 0, s>>>(p);
+    attn_bf16_kernel<D, NW, QB, BN, true><<<unsigned(grid), NW * 64, 0, s>>>(p);
   else
-    attn_bf16_kernel<D, QB, BN, false><<<unsigned(grid), kThreads, 0, s>>>(p);
+    attn_bf16_kernel<D, NW, QB, BN, false><<<unsigned(grid), NW * 64, 0, s>>>(p);
   return check_launch("attn_bf16_kernel");
 }
 
@@ -364,9 +480,9 @@ int launch(const AttnArgs& a, hipStream_t s) {
 int launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   switch (a.D) {
     case 128:
-      return launch<128, 2, 64>(a, s);
+      return launch<128, USP_D128_WAVES, USP_D128_QB, USP_D128_BN>(a, s);
     case 64:
-      return launch<64, 2, 128>(a, s);
+      return launch<64, USP_D64_WAVES, USP_D64_QB, USP_D64_BN>(a, s);
     default:
       return fail(USP_ENOSYS, "bf16 attention: unsupported D %d", a.D);
   }
