@@ -14,19 +14,27 @@ path, every row of it:
   unpack   rank 0's rows of the 8 output blocks back to [1, 4095, 40, 128]
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
-Also reported: the attention kernel alone (HIP events around each launch on
-the launch stream), and the world-tensor pack / unpack bandwidth of the full
-[1, 32760, 40, 128] tensor (read + write bytes / time, buffers rotated so
-the 256 MB last-level cache cannot serve repeats).
+Also reported: each kernel alone (HIP events around each launch on the
+launch stream), the world-tensor pack / unpack bandwidth of the full
+[1, 32760, 40, 128] tensor (read + write bytes / time, buffers rotated so the
+256 MB last-level cache cannot serve repeats), and a plain device copy of
+1 GiB as the practical HBM reference.
 
 cpu_baseline: the float64 CPU oracle on a bounded sample of query rows of
 the same attention, on every host core this process may use.
+
+roofline.traffic: HBM bytes per attention launch from rocprofv3 FETCH_SIZE /
+WRITE_SIZE counter runs, each scaled by what the counter reads for the plain
+copy kernel of known size in the same run (``--pmc-summary``); reported only
+while the attention kernel source is the one the counters were taken on.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -40,6 +48,14 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s + % MFMA peak at S=32760,h=5,D=128; pack/unpack GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "ulysses_sequence_attention_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_video_dit_share_traffic.json")
+COPY_BYTES = 1 << 30
+
+
+def source_digest(path=ATTN_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def cpu_baseline(q, k, v, h0, S, D, target_s):
@@ -52,20 +68,82 @@ def cpu_baseline(q, k, v, h0, S, D, target_s):
                   for x in (q, k, v))
     cores = A.host_cores()
     rng = np.random.default_rng(123)
-    # calibrate on one core
+    # calibrate on one core, then size the sample for about target_s of wall time
     t0 = time.perf_counter()
     A.attention_rows(qf, kf, vf, 0, 0, np.arange(64))
     per_row = (time.perf_counter() - t0) / 64
     n = int(max(64, min(S, target_s * cores / (per_row * h0))))
-    rows = {(0, hd): np.sort(rng.choice(S, n, replace=False)) for hd in range(h0)}
+    rows = {(0, hd): (np.arange(S) if n >= S else np.sort(rng.choice(S, n, replace=False)))
+            for hd in range(h0)}
     t0 = time.perf_counter()
     A.attention_parallel(qf, kf, vf, rows_per_head=rows, workers=cores)
     wall = time.perf_counter() - t0
     flops = 4.0 * S * D * n * h0
     return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} query rows x {h0} heads of the S={S}, D={D} attention "
+            "sample": (f"all {S} query rows" if n >= S else f"{n} query rows") +
+                      f" x {h0} heads of the S={S}, D={D} attention "
                       f"({flops:.3e} flop, {wall:.1f} s wall, float64 NumPy, "
                       f"{cores} worker processes x 1 BLAS thread)"}
+
+
+def stored_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def pmc_summary(dirs, out_json):
+    """Parse rocprofv3 --pmc counter CSVs (FETCH_SIZE and WRITE_SIZE runs of
+    this benchmark) into per-kernel KiB per dispatch, calibrate both counters
+    on the plain copy kernel (COPY_BYTES read and written per dispatch), and
+    write the attention kernel's HBM traffic per launch to ``out_json``."""
+    per = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    name = r["Kernel_Name"]
+                    kind = ("attention" if "attn_bf16_kernel" in name else
+                            "copy" if "copyBuffer" in name else
+                            "pack" if "relayout_kernel<true>" in name else
+                            "unpack" if "relayout_kernel<false>" in name else None)
+                    if kind is None:
+                        continue
+                    key = (kind, r["Counter_Name"])
+                    per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+                    per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    avg = {k: float(np.mean(list(v.values()))) for k, v in per.items()}
+    lines = ["kernel     counter      KiB/dispatch  dispatches"]
+    for (kind, ctr), val in sorted(avg.items()):
+        lines.append(f"{kind:10s} {ctr:12s} {val:12.1f}  {len(per[(kind, ctr)])}")
+    f_copy = avg.get(("copy", "FETCH_SIZE"))
+    w_copy = avg.get(("copy", "WRITE_SIZE"))
+    ff = COPY_BYTES / (f_copy * 1024) if f_copy else None
+    fw = COPY_BYTES / (w_copy * 1024) if w_copy else None
+    lines.append(f"copy calibration ({COPY_BYTES} B read and written per dispatch): "
+                 f"FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}" if ff and fw else
+                 "copy calibration missing")
+    res = {"source_sha256": source_digest(), "fetch_factor": ff, "write_factor": fw}
+    for kind in ("attention", "pack", "unpack"):
+        f_k, w_k = avg.get((kind, "FETCH_SIZE")), avg.get((kind, "WRITE_SIZE"))
+        if f_k is not None and w_k is not None and ff and fw:
+            rb, wb = f_k * 1024 * ff, w_k * 1024 * fw
+            res[kind] = {"read_bytes": rb, "write_bytes": wb}
+            lines.append(f"{kind}: HBM read {rb / 1e6:.1f} MB + write {wb / 1e6:.1f} MB per "
+                         f"dispatch (calibrated)")
+    if "attention" in res:
+        res["traffic_bytes_per_launch"] = res["attention"]["read_bytes"] + \
+            res["attention"]["write_bytes"]
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    print("\n".join(lines))
 
 
 def main():
@@ -78,8 +156,13 @@ def main():
                     help="target wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-relayout-bw", action="store_true")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 counter runs of this benchmark and exit")
     args = ap.parse_args()
 
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, TRAFFIC_JSON)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not "
               "supported (the multi-GPU exchange is not part of this build)", file=sys.stderr)
@@ -109,6 +192,9 @@ def main():
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     world = [bf(x) for x in (q, k, v)]
     del q, k, v
     shard = [x[:, tb[0]:tb[1]].contiguous() for x in world]
@@ -121,23 +207,26 @@ def main():
     oshard = torch.empty((B, len0, H, D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step(e=None):
+        if e is not None:
+            e[0].record()
         for x, bl in zip(shard, blocks):
             usp.usp_pack_seq_to_heads(x, bl, rank=0)
-        if ev is not None:
-            ev[0].record()
+        if e is not None:
+            e[1].record()
         usp.usp_attention_fwd(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0])
-        if ev is not None:
-            ev[1].record()
+        if e is not None:
+            e[2].record()
         usp.usp_unpack_heads_to_seq(oblocks, oshard, rank=0)
+        if e is not None:
+            e[3].record()
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t_start.record()
@@ -146,14 +235,33 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    unpack_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    elem = 2  # bf16
+    share_bytes = 2 * B * len0 * H * D * elem   # one tensor, read + write
+
+    # plain device copy of 1 GiB: practical HBM reference and counter calibration
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b_ = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(4):
+        dst.copy_(src)
+    b_.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * COPY_BYTES / (a.elapsed_time(b_) / 4 * 1e-3) / 1e9
+    del src, dst
 
     rel = {}
     if not args.skip_relayout_bw:
         # world pack / unpack of the full [1, 32760, 40, 128] tensor, 3 rotating buffer sets
         print("[bench] world pack/unpack bandwidth", file=sys.stderr, flush=True)
-        nbytes = B * S * H * D * 2
+        nbytes = B * S * H * D * elem
         srcs = [world[0]] + [torch.empty_like(world[0]).copy_(world[0]) for _ in range(2)]
         dsts = [[torch.empty((B, S, hb[j + 1] - hb[j], D), dtype=torch.bfloat16, device=dev)
                  for j in range(P)] for _ in range(3)]
@@ -162,7 +270,7 @@ def main():
             for i in range(3):
                 fn(i)
             torch.cuda.synchronize()
-            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b_ = ev(), ev()
             a.record()
             for i in range(args.relayout_reps):
                 fn(i)
@@ -171,7 +279,7 @@ def main():
             ms = a.elapsed_time(b_) / args.relayout_reps
             gbs = 2.0 * nbytes / (ms * 1e-3) / 1e9
             rel[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
-                         "bytes_rw": 2 * nbytes}
+                         "frac_of_copy": gbs / copy_gbs, "bytes_rw": 2 * nbytes}
 
     out = {
         "metric": METRIC,
@@ -192,10 +300,15 @@ def main():
                            "the full sequence -> unpack rank-0 rows"},
         "attention": {"ms": attn_ms, "TFLOP/s": attn_tflops,
                       "frac_peak": attn_tflops / PEAK_BF16_TFLOPS, "flop": attn_flops},
+        "step_pack_qkv": {"us": pack_ms * 1e3,
+                          "GB/s": 3 * share_bytes / (pack_ms * 1e-3) / 1e9},
+        "step_unpack_o": {"us": unpack_ms * 1e3,
+                          "GB/s": share_bytes / (unpack_ms * 1e-3) / 1e9},
         "relayout_world": rel,
+        "copy_reference_GB/s": copy_gbs,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": stored_traffic()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
