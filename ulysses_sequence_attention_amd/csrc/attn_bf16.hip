@@ -48,6 +48,8 @@
 // robin over the 8 XCDs, so ids are remapped to give each XCD a contiguous
 // range of (batch, head, query tile) work, keeping one head's K/V stream in
 // one XCD's L2.
+#include <type_traits>
+
 #include "usp_internal.h"
 
 namespace usp {
@@ -234,12 +236,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   // ---- the per-tile steps ---------------------------------------------------
   // S^T = K Q^T for the K tile in ks[buf]
   auto qk = [&](int buf, f32x16 (&sacc)[NKB][QB]) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
+    const f32x16 zero = {};  // first k-step: accumulator operand is the inline constant 0
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -248,7 +245,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
             *reinterpret_cast<const uint4*>(&ks0[buf * KT + (kb * 32 + pi) * KLD + s * 16 + g * 8]));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sacc[kb][qb], 0, 0, 0);
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s],
+                                                                  s == 0 ? zero : sacc[kb][qb], 0, 0, 0);
       }
     }
   };
@@ -379,12 +377,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   __syncthreads();  // every wave has read K_0 before step 0 refills buffer 0 with K_2
 
   // one steady-state iteration on tile kt (< nkt - 1): `cur` holds the scores
-  // of tile kt, `nxt` receives those of tile kt + 1
-  auto step = [&](int kt, f32x16 (&cur)[NKB][QB], f32x16 (&nxt)[NKB][QB]) {
-    const bool has2 = kt + 2 < nkt;
-    if (has2) load_k(key0(kt + 2), partial(kt + 2));
-    load_v(key0(kt + 1), partial(kt + 1));
-    if (partial(kt)) mask(cur, kt);
+  // of tile kt, `nxt` receives those of tile kt + 1. With `full` true every
+  // tile the step loads (K of tile kt + 2, V of tile kt + 1) lies wholly
+  // before S, so its loads carry no row guards.
+  auto step = [&](auto full, int kt, f32x16 (&cur)[NKB][QB], f32x16 (&nxt)[NKB][QB]) {
+    constexpr bool kFull = decltype(full)::value;
+    const bool has2 = kFull || kt + 2 < nkt;
+    if (kFull) {
+      load_k(key0(kt + 2), false);
+      load_v(key0(kt + 1), false);
+    } else {
+      if (has2) load_k(key0(kt + 2), partial(kt + 2));
+      load_v(key0(kt + 1), partial(kt + 1));
+    }
     update_max(cur);
     bf16x8 pf[QB][NKB][2];
     qk((kt + 1) & 1, nxt);  // MFMA: scores of the next tile ...
@@ -394,14 +399,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     store_v((kt + 1) & 1);
     __syncthreads();
   };
+  const std::integral_constant<bool, true> full;
+  const std::integral_constant<bool, false> guarded;
 
   int kt = 0;
+  // pairs of steps whose loads all lie before the (possibly partial) last tile
+  for (; kt + 5 <= nkt; kt += 2) {
+    step(full, kt, sa, sb);
+    step(full, kt + 1, sb, sa);
+  }
   for (; kt + 2 < nkt; kt += 2) {
-    step(kt, sa, sb);
-    step(kt + 1, sb, sa);
+    step(guarded, kt, sa, sb);
+    step(guarded, kt + 1, sb, sa);
   }
   if (kt + 1 < nkt) {
-    step(kt, sa, sb);
+    step(guarded, kt, sa, sb);
     ++kt;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
