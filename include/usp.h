@@ -141,9 +141,20 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
  *   scale:  softmax scale; <= 0 selects 1/sqrt(D).
  *   lse:    NULL, or device fp32 [B][h][S] receiving the natural-log softmax
  *           normaliser log(sum_t exp(scale * <Q, K_t>)) for heads in range.
- * Scores, softmax and accumulation are fp32. The result for a head depends
- * only on that head's inputs, never on [head_lo, head_hi): a head computed in
- * any sub-range is bitwise equal to the same head computed single-shot.
+ * Scores, softmax and accumulation are fp32. Every row is computed from its
+ * own head's inputs only. Rounding: with bf16 inputs, the query tiles of a
+ * launch's last, under-filled round of workgroups are split over their key
+ * range and the parts merged (softmax-weighted by their log-sum-exps), which
+ * rounds those rows differently from an unsplit tile; since the split depends
+ * on the launch size (B, S, head count, CU count), a row's last bits may
+ * differ between head groupings of the same problem. Results are bitwise
+ * reproducible for a given launch shape and device.
+ * Memory: the bf16 path uses a device workspace owned by the library, one
+ * per (current device, stream), of (resident workgroups) * 256 * 129 * 4
+ * bytes (about 34 MB on 256 CUs), allocated with hipMalloc on the first call
+ * that splits and kept until the process ends; calls on one stream share it
+ * in stream order. A call under stream capture that would have to allocate
+ * it runs without the split instead.
  * Errors: h < 1, head range empty or outside [0, h) -> USP_EINVAL;
  *   B < 1, S < 1 or sizes overflowing -> USP_ESHAPE; unsupported
  *   in_dt/out_dt pair -> USP_EDTYPE; unsupported D -> USP_ENOSYS; misaligned
@@ -157,8 +168,9 @@ int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_
  * Head-chunked attention (maxdiffusion PR #428, two-phase Ulysses: attention
  * over head sub-groups in turn, mathematically the single-shot result since
  * heads are independent): runs usp_attention_fwd over each range of
- * usp_head_chunk_ranges(h, chunks) in order on `stream`. Bitwise equal to
- * the single-shot call. Errors: those of usp_head_chunk_ranges and
+ * usp_head_chunk_ranges(h, chunks) in order on `stream`: bitwise equal to
+ * those usp_attention_fwd calls, and equal to the single-shot call up to the
+ * rounding of split tail tiles described there. Errors: those of usp_head_chunk_ranges and
  * usp_attention_fwd.
  */
 int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,

@@ -174,7 +174,9 @@ def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float =
 
 def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=None,
                               stream=None) -> None:
-    """Attention as ``chunks`` head-chunk passes (bitwise equal to single shot)."""
+    """Attention as ``chunks`` head-chunk passes, one usp_attention_fwd per
+    range of usp_head_chunk_ranges (the single-shot result up to the rounding
+    of split tail tiles)."""
     B, S, h, D = q.shape
     _check(lib().usp_attention_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
                                            _dtype(o), B, S, h, D, scale, _ptr(lse), chunks,

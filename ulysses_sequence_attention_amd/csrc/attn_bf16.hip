@@ -40,14 +40,25 @@
 // weight exp2(0) = 1, exact in bf16. Weights are rounded to bf16 once for the
 // P V product, and the row sum is taken over those same rounded weights
 // (v_dot2c_f32_bf16 against (1, 1)), so the rounding of a dominant weight
-// cancels between numerator and denominator. Every decision depends on one
-// (batch, head, query) row only, so a head's result does not depend on which
-// other heads share the launch.
+// cancels between numerator and denominator.
+//
+// Tail split. One workgroup fills a CU, so a launch of W query tiles on C
+// CUs runs in ceil(W / C) rounds and a last round holding W mod C <= C / 2
+// tiles leaves most CUs idle. Those tail tiles are instead split over their
+// key range into f = min(C / (W mod C), 4) parts run by separate workgroups;
+// each part writes its softmax-normalised O rows (fp32) and base-2 log-sum-
+// exp to a workspace, and a merge kernel combines the f parts of a row with
+// weights 2^(lse_i - lse). The split changes only the rounding of the rows
+// it touches; which tiles split depends on the launch size, so results are
+// bitwise reproducible per launch shape, not across head groupings.
 //
 // Block -> tile order is XCD aware: the hardware deals workgroup ids round
 // robin over the 8 XCDs, so ids are remapped to give each XCD a contiguous
 // range of (batch, head, query tile) work, keeping one head's K/V stream in
-// one XCD's L2.
+// one XCD's L2. Unsplit tiles take the low ids (they are dispatched first),
+// the tail's parts the high ids.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "usp_internal.h"
@@ -77,6 +88,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #endif
 
 constexpr float kTau = 1.0f;  // lazy-rescale threshold, log2 units
+constexpr int kMaxSplit = 4;  // most key-range parts a tail tile is split into
+constexpr int kBM = 256;      // query rows per workgroup, every head dim
 
 struct Params {
   const uint16_t* q;
@@ -87,7 +100,20 @@ struct Params {
   int S, h, head_lo, nheads, n_qtiles;
   float c;      // scale * log2(e)
   float scale;  // softmax scale (for the natural-log normaliser)
+  // tail split: tiles [0, n_full) run whole; tiles [n_full, n_full + n_tail)
+  // run as nsplit key-range parts writing ws (fp32 [part][tile][kBM][D]) and
+  // ws_lse ([part][tile][kBM], base 2)
+  int n_full, n_tail, nsplit;
+  float* ws;
+  float* ws_lse;
 };
+
+// workgroup id (< n) -> logical work id, giving each of the 8 XCDs (which
+// are dealt ids round robin) a contiguous range of logical ids
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  const int per = n >> 3, rem = n & 7, xcd = id & 7;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + (id >> 3);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -117,6 +143,7 @@ template <int D, int NW, int QB, int BN, bool kOutBf16>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   constexpr int kThreads = NW * 64;
   constexpr int BM = NW * QB * 32;
+  static_assert(BM == kBM, "workspace rows assume kBM query rows per workgroup");
   constexpr int NKB = BN / 32;           // 32-key blocks per tile
   constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;            // 32-wide blocks of the output head dim
@@ -134,10 +161,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   uint16_t* const ks0 = lds;           // K tile buffer 0 (buffer 1 follows)
   uint16_t* const vt0 = lds + 2 * KT;  // V^T tile buffer 0 (buffer 1 follows)
 
-  // ---- XCD-aware workgroup -> (batch, head, query tile) -------------------
-  const int nwg = gridDim.x, bid = blockIdx.x;
-  const int per = nwg >> 3, rem = nwg & 7, xcd = bid & 7;
-  const int lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + (bid >> 3);
+  // ---- XCD-aware workgroup -> (batch, head, query tile[, key part]) -------
+  const int bid = blockIdx.x;
+  int lid, unit = -1;  // unit: workspace slot of a tail part, -1 for a whole tile
+  if (bid < p.n_full) {
+    lid = xcd_remap(bid, p.n_full);
+  } else {
+    unit = xcd_remap(bid - p.n_full, p.n_tail * p.nsplit);  // part-major
+    lid = p.n_full + unit % p.n_tail;
+  }
   const int qt = lid % p.n_qtiles;
   const int bh = lid / p.n_qtiles;
   const int head = p.head_lo + bh % p.nheads;
@@ -343,13 +375,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     }
   };
 
-  // keys at or past S get score -inf (weight 0)
-  auto mask = [&](f32x16 (&sacc)[NKB][QB], int tile) {
+  // keys at or past S get score -inf (weight 0); t0 is the tile's first key
+  auto mask = [&](f32x16 (&sacc)[NKB][QB], int t0) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = tile * BN + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+        const int key = t0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
         if (key >= S) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) sacc[kb][qb][r] = -INFINITY;
@@ -357,8 +389,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
       }
   };
 
-  const int nkt = (S + BN - 1) / BN;
-  auto key0 = [&](int kt) { return kt * BN; };                // first key of tile kt
+  // key tiles [kt_lo, kt_lo + nkt) of this workgroup; tile indices below
+  // are relative to kt_lo, so only the last tile of the range can be partial
+  const int nkt_all = (S + BN - 1) / BN;
+  const int part = unit < 0 ? 0 : unit / p.n_tail;
+  const int parts = unit < 0 ? 1 : p.nsplit;
+  const int kt_lo = part * nkt_all / parts;
+  const int nkt = (part + 1) * nkt_all / parts - kt_lo;
+  auto key0 = [&](int kt) { return (kt_lo + kt) * BN; };      // first key of tile kt
   auto partial = [&](int kt) { return key0(kt) + BN > S; };   // tile runs past S
 
   // ---- prologue: K_0, V_0, K_1 in LDS; scores of tile 0 -------------------
@@ -423,7 +461,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 
   // ---- last tile -------------------------------------------------------------
   {
-    if (partial(kt)) mask(sa, kt);
+    if (partial(kt)) mask(sa, key0(kt));
     update_max(sa);
     bf16x8 pf[QB][NKB][2];
     weights(sa, pf);
@@ -431,6 +469,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   }
 
   // ---- epilogue: normalise and store ------------------------------------------
+  if (unit >= 0) {
+    // a tail part: normalised fp32 O rows and base-2 log-sum-exp to the
+    // workspace, combined by attn_merge_kernel
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = sum_halves(lrow[qb]);
+      const float inv = 1.0f / lt;
+      const int rloc = w * (QB * 32) + qb * 32 + l32;
+      if (qrow0 + qb * 32 + l32 < S) {
+        float* wo = p.ws + (size_t(unit) * BM + rloc) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = oacc[qb][db][4 * a + e] * inv;
+            *reinterpret_cast<f32x4*>(wo + db * 32 + 8 * a + 4 * g) = x;
+          }
+        }
+        if (g == 0) p.ws_lse[size_t(unit) * BM + rloc] = mrow[qb] * c + log2f(lt);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = sum_halves(lrow[qb]);
@@ -462,6 +525,116 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   }
 }
 
+// Combines the key-range parts of the tail tiles: per row, with part
+// log-sum-exps l_i (base 2), lse = M + log2(sum_i 2^(l_i - M)) (M = max l_i)
+// and O = sum_i 2^(l_i - lse) O_i. One thread per 4 head-dim elements of a
+// row; a row's threads are consecutive, so workspace reads and output
+// writes are contiguous.
+template <int D, bool kOutBf16>
+__global__ __launch_bounds__(256) void attn_merge_kernel(Params p) {
+  constexpr int CH = D / 4;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(p.n_tail) * kBM * CH) return;
+  const int ch = int(idx % CH);
+  const int64_t tr = idx / CH;
+  const int r = int(tr % kBM), i = int(tr / kBM);
+  const int lid = p.n_full + i;
+  const int qt = lid % p.n_qtiles, bh = lid / p.n_qtiles;
+  const int head = p.head_lo + bh % p.nheads, b = bh / p.nheads;
+  const int row = qt * kBM + r;
+  if (row >= p.S) return;
+
+  float l2[kMaxSplit];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; ++j) {
+    if (j < p.nsplit) {
+      l2[j] = p.ws_lse[(size_t(j) * p.n_tail + i) * kBM + r];
+      m = fmaxf(m, l2[j]);
+    }
+  }
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; ++j) {
+    if (j < p.nsplit) {
+      const float wj = __builtin_amdgcn_exp2f(l2[j] - m);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(
+          p.ws + ((size_t(j) * p.n_tail + i) * kBM + r) * D + ch * 4);
+      wsum += wj;
+      acc += wj * x;
+    }
+  }
+  acc *= 1.0f / wsum;
+  const size_t ob = ((size_t(b) * p.S + row) * p.h + head) * D + ch * 4;
+  if (kOutBf16)
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ob) = __builtin_convertvector(acc, bf16x4);
+  else
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + ob) = acc;
+  if (p.lse && ch == 0)
+    p.lse[(size_t(b) * p.h + head) * p.S + row] = (m + log2f(wsum)) * 0.69314718055994531f;
+}
+
+// Workgroups of one kernel resident at once on the current device (CUs x
+// workgroups per CU), cached per device.
+template <typename K>
+int resident_slots(K kernel, int threads) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  v = cus * per;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int D, int NW, int QB, int BN, bool kOutBf16>
+int launch_split(Params& p, int64_t tiles, hipStream_t s) {
+  constexpr int kThreads = NW * 64;
+  auto* kern = attn_bf16_kernel<D, NW, QB, BN, kOutBf16>;
+  // plan the tail split
+  const int nkt = (p.S + BN - 1) / BN;
+  const int slots = resident_slots(kern, kThreads);
+  int64_t tail = 0;
+  int f = 1;
+  if (slots > 0) {
+    tail = tiles % slots;
+    if (tail > 0 && 2 * tail <= slots) f = int(std::min<int64_t>({slots / tail, kMaxSplit, nkt}));
+  }
+  if (f >= 2) {
+    // room for any plan on this device: f * tail <= slots parts
+    const size_t bytes = size_t(slots) * kBM * (128 + 1) * sizeof(float);
+    float* ws = static_cast<float*>(stream_workspace(bytes, s));
+    if (ws) {
+      p.ws = ws;
+      p.ws_lse = ws + size_t(slots) * kBM * 128;
+    } else {
+      f = 1;  // no workspace (e.g. under stream capture): run every tile whole
+    }
+  }
+  if (f < 2) tail = 0;
+  p.n_full = int(tiles - tail);
+  p.n_tail = int(tail);
+  p.nsplit = f;
+  const int64_t grid = p.n_full + int64_t(f) * tail;
+  if (grid > 0x7fffffff) return fail(USP_ESHAPE, "attention grid too large");
+  kern<<<unsigned(grid), kThreads, 0, s>>>(p);
+  if (int st = check_launch("attn_bf16_kernel")) return st;
+  if (tail > 0) {
+    const int64_t threads = tail * kBM * (D / 4);
+    attn_merge_kernel<D, kOutBf16><<<unsigned((threads + 255) / 256), 256, 0, s>>>(p);
+    if (int st = check_launch("attn_merge_kernel")) return st;
+  }
+  return USP_OK;
+}
+
 template <int D, int NW, int QB, int BN>
 int launch(const AttnArgs& a, hipStream_t s) {
   constexpr int BM = NW * QB * 32;
@@ -478,13 +651,13 @@ int launch(const AttnArgs& a, hipStream_t s) {
   p.n_qtiles = int((a.S + BM - 1) / BM);
   p.c = a.scale * 1.4426950408889634f;
   p.scale = a.scale;
-  const int64_t grid = int64_t(p.n_qtiles) * p.nheads * a.B;
-  if (grid > 0x7fffffff) return fail(USP_ESHAPE, "attention grid too large");
-  if (a.out_dt == USP_BF16)
-    attn_bf16_kernel<D, NW, QB, BN, true><<<unsigned(grid), NW * 64, 0, s>>>(p);
-  else
-    attn_bf16_kernel<D, NW, QB, BN, false><<<unsigned(grid), NW * 64, 0, s>>>(p);
-  return check_launch("attn_bf16_kernel");
+  p.n_full = p.n_tail = 0;
+  p.nsplit = 1;
+  p.ws = p.ws_lse = nullptr;
+  const int64_t tiles = int64_t(p.n_qtiles) * p.nheads * a.B;
+  if (tiles > 0x7fffffff) return fail(USP_ESHAPE, "attention grid too large");
+  return a.out_dt == USP_BF16 ? launch_split<D, NW, QB, BN, true>(p, tiles, s)
+                              : launch_split<D, NW, QB, BN, false>(p, tiles, s);
 }
 
 }  // namespace

@@ -4,7 +4,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "usp_internal.h"
 
@@ -31,6 +34,39 @@ int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(USP_EHIP, "%s: %s", what, hipGetErrorString(e));
   return USP_OK;
+}
+
+void* stream_workspace(size_t bytes, hipStream_t s) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> buffers;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  auto& e = buffers[{dev, s}];
+  if (e.first && e.second >= bytes) return e.first;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (e.first) {
+    // earlier launches on this stream may still read the old buffer
+    if (hipStreamSynchronize(s) != hipSuccess || hipFree(e.first) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    e = {nullptr, 0};
+  }
+  void* ptr = nullptr;
+  if (hipMalloc(&ptr, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  e = {ptr, bytes};
+  return ptr;
 }
 
 // Balanced contiguous ranges (h3-blackwell-runtime distributed.py,

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/usp.h"
+#include "usp.h"  // include/ is on the include path
 
 namespace usp {
 
@@ -34,6 +34,13 @@ struct FastDiv {
     return (__umulhi(n, mul) + n) >> shift;
   }
 };
+
+// Device scratch owned by the library, one buffer per (current device,
+// stream), grown to at least `bytes` on first need and kept until the process
+// ends. Work on one stream is ordered, so its launches share the buffer
+// safely. Returns nullptr (and allocates nothing) when the buffer must grow
+// while the stream is being captured into a graph, or when hipMalloc fails.
+void* stream_workspace(size_t bytes, hipStream_t s);
 
 // Kernel launchers (one per translation unit).
 int launch_ranges_device(int64_t total, int32_t parts, int64_t* d_bounds, hipStream_t s);
