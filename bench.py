@@ -23,10 +23,14 @@ launch stream), the world-tensor pack / unpack bandwidth of the full
 cpu_baseline: the float64 CPU oracle on a bounded sample of query rows of
 the same attention, on every host core this process may use.
 
-roofline.traffic: HBM bytes per attention launch from rocprofv3 FETCH_SIZE /
-WRITE_SIZE counter runs, each scaled by what the counter reads for the plain
-copy kernel of known size in the same run (``--pmc-summary``); reported only
-while the attention kernel source is the one the counters were taken on.
+roofline: the attention call (usp_attention_fwd: the flash kernel plus, when
+the last round of query tiles is split over keys, the small merge kernel) is
+the dominant step; ``achieved`` is its flops over its event-timed duration.
+roofline.traffic: HBM bytes per attention call from rocprofv3 FETCH_SIZE /
+WRITE_SIZE counter runs (both kernels), each scaled by what the counter reads
+for the plain copy kernel of known size in the same run (``--pmc-summary``);
+reported only while the attention source is the one the counters were taken
+on.
 """
 from __future__ import annotations
 
@@ -111,6 +115,7 @@ def pmc_summary(dirs, out_json):
                 for r in csv.DictReader(f):
                     name = r["Kernel_Name"]
                     kind = ("attention" if "attn_bf16_kernel" in name else
+                            "merge" if "attn_merge_kernel" in name else
                             "copy" if "copyBuffer" in name else
                             "pack" if "relayout_kernel<true>" in name else
                             "unpack" if "relayout_kernel<false>" in name else None)
@@ -131,7 +136,7 @@ def pmc_summary(dirs, out_json):
                  f"FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}" if ff and fw else
                  "copy calibration missing")
     res = {"source_sha256": source_digest(), "fetch_factor": ff, "write_factor": fw}
-    for kind in ("attention", "pack", "unpack"):
+    for kind in ("attention", "merge", "pack", "unpack"):
         f_k, w_k = avg.get((kind, "FETCH_SIZE")), avg.get((kind, "WRITE_SIZE"))
         if f_k is not None and w_k is not None and ff and fw:
             rb, wb = f_k * 1024 * ff, w_k * 1024 * fw
@@ -139,8 +144,10 @@ def pmc_summary(dirs, out_json):
             lines.append(f"{kind}: HBM read {rb / 1e6:.1f} MB + write {wb / 1e6:.1f} MB per "
                          f"dispatch (calibrated)")
     if "attention" in res:
-        res["traffic_bytes_per_launch"] = res["attention"]["read_bytes"] + \
-            res["attention"]["write_bytes"]
+        # one attention call = one flash-kernel dispatch (+ one merge dispatch)
+        res["traffic_bytes_per_launch"] = sum(
+            res[k]["read_bytes"] + res[k]["write_bytes"] for k in ("attention", "merge")
+            if k in res)
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
     print("\n".join(lines))
@@ -149,8 +156,8 @@ def pmc_summary(dirs, out_json):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--relayout-reps", type=int, default=6)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
@@ -308,7 +315,8 @@ def main():
         "copy_reference_GB/s": copy_gbs,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic()},
+                     "traffic": stored_traffic(),
+                     "kernel": "usp_attention_fwd: attn_bf16_kernel + attn_merge_kernel"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
