@@ -139,27 +139,34 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i's bytes land at lds_base + 16 i, with
+// lds_base uniform over the wave. The builtin exists for the device target
+// only; the host pass sees an empty body.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+#endif
+}
+
 template <int D, int NW, int QB, int BN, bool kOutBf16>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
-  constexpr int kThreads = NW * 64;
   constexpr int BM = NW * QB * 32;
   static_assert(BM == kBM, "workspace rows assume kBM query rows per workgroup");
   constexpr int NKB = BN / 32;           // 32-key blocks per tile
   constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;            // 32-wide blocks of the output head dim
-  constexpr int KLD = D + 8;             // K tile row stride (elements)
-  constexpr int VLD = BN + 8;            // V^T tile row stride (elements)
-  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  constexpr int NKL = BN * CPR / kThreads;  // K chunks per thread per tile
-  constexpr int G = BN * CPR / kThreads;    // V keys per thread (one 16-byte chunk each)
-  static_assert(NKL * kThreads == BN * CPR, "K tile must split evenly over the block");
-  static_assert(G == 1 || G == 2 || G == 4, "V staging handles 1, 2 or 4 keys per thread");
+  constexpr int ROWB = 2 * D;            // bytes per K/V row
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int RPL = 256 / ROWB;        // rows per 256-byte line of the 64 LDS banks
+  constexpr int RPI = 1024 / ROWB;       // rows per direct load (64 lanes x 16 bytes)
+  constexpr int NQ = BN * ROWB / 1024;   // direct loads per tile
+  constexpr int NI = NQ / NW;            // direct loads per wave per tile (K and V each)
+  static_assert(NI * NW == NQ, "a tile must split evenly into the waves' direct loads");
+  constexpr int TB = BN * ROWB;          // bytes per K or V tile
 
-  // LDS: two K tiles, then two V^T tiles
-  constexpr int KT = BN * KLD, VT = D * VLD;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (KT + VT)];
-  uint16_t* const ks0 = lds;           // K tile buffer 0 (buffer 1 follows)
-  uint16_t* const vt0 = lds + 2 * KT;  // V^T tile buffer 0 (buffer 1 follows)
+  // LDS: K tiles in buffers 0, 1, then V tiles in buffers 0, 1; rows unpadded
+  __shared__ __attribute__((aligned(16))) char lds[4 * TB];
 
   // ---- XCD-aware workgroup -> (batch, head, query tile[, key part]) -------
   const int bid = blockIdx.x;
@@ -196,74 +203,66 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     }
   }
 
-  // ---- K/V tile staging (global -> registers -> LDS) ----------------------
-  // Each thread loads fixed (row, chunk) slots of every tile: a per-lane
-  // 32-bit element offset from the tile's (uniform) base. Only the last tile
-  // can run past S, so only it is loaded with row guards.
-  uint4 kreg[NKL];
-  uint4 vreg[G];
-  uint32_t koff[NKL], krow[NKL];
+  // ---- K/V tile staging (global -> LDS directly) ---------------------------
+  // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i, so
+  // one load fills RPI whole rows and rows cannot be padded. Instead the
+  // 16-byte chunks of a row are stored at XOR-swizzled positions (lane i
+  // fetches the chunk whose swizzled position is i mod CPR):
+  //   K: chunk c of row r at position c ^ ((r / RPL) mod CPR), so the 16 rows
+  //      of a fragment read fall on 16 distinct bank quads;
+  //   V: chunk c of row r at position c ^ 4((r / RPL) mod (CPR / 4)), so the
+  //      4 rows x 4 chunks of a transposed read are distinct bank quads.
+  // Wave w issues loads q = w + NW i of each tile (rows [q RPI, q RPI + RPI)).
+  auto swz_k = [](int r) { return (r / RPL) % CPR; };
+  auto swz_v = [](int r) { return 4 * ((r / RPL) % (CPR / 4)); };
+  uint32_t kgo[NI], vgo[NI];  // per-lane element offsets from the tile's first row
 #pragma unroll
-  for (int i = 0; i < NKL; ++i) {
-    const int idx = tid + i * kThreads;
-    krow[i] = idx / CPR;
-    koff[i] = uint32_t(krow[i] * rs + (idx % CPR) * 8);
+  for (int i = 0; i < NI; ++i) {
+    const int r = (w + NW * i) * RPI + lane / CPR, pos = lane % CPR;
+    kgo[i] = uint32_t(r * rs + (pos ^ swz_k(r)) * 8);
+    vgo[i] = uint32_t(r * rs + (pos ^ swz_v(r)) * 8);
   }
-  const int vkq = tid % (BN / G), vch = tid / (BN / G);
-  const uint32_t voff = uint32_t(G * vkq * rs + vch * 8);
-  auto load_k = [&](int t0, bool guard) {
-    const uint16_t* base = p.k + hb + size_t(t0) * rs;
+  // A tile that runs past S loads row S - 1 in place of the missing rows:
+  // finite data whose scores the mask sets to -inf (weight 0).
+  auto issue = [&](const uint16_t* src, const uint32_t (&go)[NI], int lbase, int t0, bool guard,
+                   bool is_v) {
+    const uint16_t* base = src + hb + size_t(t0) * rs;
 #pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      if (!guard || t0 + int(krow[i]) < S)
-        kreg[i] = *reinterpret_cast<const uint4*>(base + koff[i]);
-      else
-        kreg[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto load_v = [&](int t0, bool guard) {
-    const uint16_t* base = p.v + hb + size_t(t0) * rs;
-#pragma unroll
-    for (int e = 0; e < G; ++e) {
-      if (!guard || t0 + G * vkq + e < S)
-        vreg[e] = *reinterpret_cast<const uint4*>(base + voff + e * rs);
-      else
-        vreg[e] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(&ks0[buf * KT + r * KLD + ch * 8]) = kreg[i];
-    }
-  };
-  auto store_v = [&](int buf) {
-    // transpose: head-dim element j of the G keys becomes G consecutive keys
-    // of V^T row ch * 8 + j
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint16_t* dst = &vt0[buf * VT + (vch * 8 + j) * VLD + G * vkq];
-      if constexpr (G == 1) {
-        *dst = uint16_t(word(vreg[0], j >> 1) >> (16 * (j & 1)));
-        continue;
+    for (int i = 0; i < NI; ++i) {
+      uint32_t off = go[i];
+      if (guard) {
+        const int r = (w + NW * i) * RPI + lane / CPR, pos = lane % CPR;
+        const int rc = min(r, S - 1 - t0);
+        off = uint32_t(rc * rs + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8);
       }
-      const uint32_t lo = pair16(vreg[0], vreg[G > 1 ? 1 : 0], j);
-      if constexpr (G == 4) {
-        uint2 x;
-        x.x = lo;
-        x.y = pair16(vreg[2], vreg[3], j);
-        *reinterpret_cast<uint2*>(dst) = x;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = lo;
-      }
+      load_lds16(base + off, lds + lbase + (w + NW * i) * 1024);
     }
   };
+  auto load_k = [&](int buf, int t0, bool guard) { issue(p.k, kgo, buf * TB, t0, guard, false); };
+  auto load_v = [&](int buf, int t0, bool guard) { issue(p.v, vgo, (2 + buf) * TB, t0, guard, true); };
+  // the wave's direct loads have landed in LDS (a barrier then publishes them)
+  auto loads_done = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // K row fed to A-operand row l32 (see the layout note above)
   const int a4 = l32 >> 3, g4 = (l32 >> 2) & 1, c4 = l32 & 3;
   const int pi = 16 * (a4 >> 1) + 8 * g4 + 4 * (a4 & 1) + c4;
+  // per-lane byte offsets of the fragment reads within a K tile (k-step s,
+  // key block 0) and a V tile (head-dim block db, key row 0); key blocks
+  // and rows add uniform offsets, the swizzles depend on the lane only
+  uint32_t kad[KS], vad[NDB];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) kad[st] = uint32_t(pi * ROWB + (((2 * st + g) ^ swz_k(pi)) * 16));
+  {
+    // ds_read_b64_tr_b16: in each 16-lane group, lane j points at 4 bf16 of
+    // row j / 4 (head-dim offset 4 (j mod 4)) and receives element j mod 4
+    // of lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4: 4 keys of head
+    // dim j. Lane l32 = 16 dh + j of half g covers keys 8 g + 4 half + (0..3).
+    const int j = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vad[db] = uint32_t((8 * g + j / 4) * ROWB +
+                         (((4 * db + 2 * dh + (j & 3) / 2) ^ swz_v(j / 4)) * 16) + (j & 1) * 8);
+  }
 
   // ---- the per-tile steps ---------------------------------------------------
   // S^T = K Q^T for the K tile in ks[buf]
@@ -274,7 +273,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 kf = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&ks0[buf * KT + (kb * 32 + pi) * KLD + s * 16 + g * 8]));
+            *reinterpret_cast<const uint4*>(lds + buf * TB + kb * 32 * ROWB + kad[s]));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s],
@@ -364,8 +363,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
       for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4*>(
-              &vt0[buf * VT + (db * 32 + l32) * VLD + kb * 32 + h2 * 16 + g * 8]));
+          const char* vrow = lds + (2 + buf) * TB + (kb * 32 + h2 * 16) * ROWB + vad[db];
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow + 4 * ROWB));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             oacc[qb][db] =
@@ -400,14 +403,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   auto partial = [&](int kt) { return key0(kt) + BN > S; };   // tile runs past S
 
   // ---- prologue: K_0, V_0, K_1 in LDS; scores of tile 0 -------------------
-  load_k(key0(0), partial(0));
-  load_v(key0(0), partial(0));
-  store_k(0);
-  store_v(0);
-  if (nkt > 1) {
-    load_k(key0(1), partial(1));
-    store_k(1);
-  }
+  load_k(0, key0(0), partial(0));
+  load_v(0, key0(0), partial(0));
+  if (nkt > 1) load_k(1, key0(1), partial(1));
+  loads_done();
   __syncthreads();
 
   f32x16 sa[NKB][QB], sb[NKB][QB];
@@ -415,26 +414,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   __syncthreads();  // every wave has read K_0 before step 0 refills buffer 0 with K_2
 
   // one steady-state iteration on tile kt (< nkt - 1): `cur` holds the scores
-  // of tile kt, `nxt` receives those of tile kt + 1. With `full` true every
-  // tile the step loads (K of tile kt + 2, V of tile kt + 1) lies wholly
-  // before S, so its loads carry no row guards.
+  // of tile kt, `nxt` receives those of tile kt + 1. At its start the step
+  // loads K of tile kt + 2 into the K buffer tile kt used (read in the
+  // previous step) and V of tile kt + 1 into the V buffer tile kt - 1 used;
+  // the barrier at its end publishes both. With `full` true both tiles lie
+  // wholly before S, so the loads carry no row guards.
   auto step = [&](auto full, int kt, f32x16 (&cur)[NKB][QB], f32x16 (&nxt)[NKB][QB]) {
     constexpr bool kFull = decltype(full)::value;
-    const bool has2 = kFull || kt + 2 < nkt;
     if (kFull) {
-      load_k(key0(kt + 2), false);
-      load_v(key0(kt + 1), false);
+      load_k(kt & 1, key0(kt + 2), false);
+      load_v((kt + 1) & 1, key0(kt + 1), false);
     } else {
-      if (has2) load_k(key0(kt + 2), partial(kt + 2));
-      load_v(key0(kt + 1), partial(kt + 1));
+      if (kt + 2 < nkt) load_k(kt & 1, key0(kt + 2), partial(kt + 2));
+      load_v((kt + 1) & 1, key0(kt + 1), partial(kt + 1));
     }
     update_max(cur);
     bf16x8 pf[QB][NKB][2];
     qk((kt + 1) & 1, nxt);  // MFMA: scores of the next tile ...
     weights(cur, pf);       // ... while the VALU turns this tile into weights
     pv(kt & 1, pf);
-    if (has2) store_k(kt & 1);
-    store_v((kt + 1) & 1);
+    loads_done();
     __syncthreads();
   };
   const std::integral_constant<bool, true> full;
