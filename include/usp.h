@@ -31,6 +31,7 @@
 #ifndef USP_H
 #define USP_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -141,20 +142,12 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
  *   scale:  softmax scale; <= 0 selects 1/sqrt(D).
  *   lse:    NULL, or device fp32 [B][h][S] receiving the natural-log softmax
  *           normaliser log(sum_t exp(scale * <Q, K_t>)) for heads in range.
- * Scores, softmax and accumulation are fp32. Every row is computed from its
- * own head's inputs only. Rounding: with bf16 inputs, the query tiles of a
- * launch's last, under-filled round of workgroups are split over their key
- * range and the parts merged (softmax-weighted by their log-sum-exps), which
- * rounds those rows differently from an unsplit tile; since the split depends
- * on the launch size (B, S, head count, CU count), a row's last bits may
- * differ between head groupings of the same problem. Results are bitwise
- * reproducible for a given launch shape and device.
- * Memory: the bf16 path uses a device workspace owned by the library, one
- * per (current device, stream), of (resident workgroups) * 256 * 129 * 4
- * bytes (about 34 MB on 256 CUs), allocated with hipMalloc on the first call
- * that splits and kept until the process ends; calls on one stream share it
- * in stream order. A call under stream capture that would have to allocate
- * it runs without the split instead.
+ * Scores, softmax and accumulation are fp32. The result for a head depends
+ * only on that head's inputs, never on [head_lo, head_hi), B or the device:
+ * a head computed in any sub-range is bitwise equal to the same head computed
+ * single-shot. Nothing is allocated: with bf16 inputs one kernel runs, in
+ * which two groups of waves walk the two key halves (split at a point set by
+ * S and D only) of 128 query rows and merge their softmax states in LDS.
  * Errors: h < 1, head range empty or outside [0, h) -> USP_EINVAL;
  *   B < 1, S < 1 or sizes overflowing -> USP_ESHAPE; unsupported
  *   in_dt/out_dt pair -> USP_EDTYPE; unsupported D -> USP_ENOSYS; misaligned
@@ -165,12 +158,45 @@ int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_
                       int32_t head_lo, int32_t head_hi, float scale, float* lse, void* stream);
 
 /*
+ * Device workspace (bytes) usp_attention_fwd_ws needs for `heads` heads
+ * (head_hi - head_lo) of B batches of S tokens: 0 for USP_F32 inputs, else
+ * B * heads * ceil(S / 256) * 2 * 256 * (D + 3) * 4 (171.7 MB for B = 1,
+ * heads = 5, S = 32760, D = 128). Written to *bytes.
+ * Errors: bytes NULL -> USP_EINVAL; a size < 1 or too large for one launch
+ *   -> USP_ESHAPE; unknown in_dt -> USP_EDTYPE.
+ */
+int usp_attention_workspace_bytes(usp_dtype in_dt, int64_t B, int64_t S, int32_t heads, int32_t D,
+                                  size_t* bytes);
+
+/*
+ * usp_attention_fwd with a caller-provided device workspace (the same
+ * operation and result, bitwise, as usp_attention_fwd). With bf16 inputs
+ * each tile of 256 query rows is computed by two workgroups, one per key
+ * half, that leave their unnormalised softmax state in `ws`; a second
+ * kernel merges the halves exactly as usp_attention_fwd's workgroups merge
+ * them in LDS. This keeps one K/V stream per workgroup (the key-group kernel
+ * of usp_attention_fwd streams two per 128 rows) and is the faster path.
+ *   ws, ws_bytes: device buffer, 16-byte aligned, of at least
+ *                 usp_attention_workspace_bytes(in_dt, B, S, head_hi -
+ *                 head_lo, D) bytes, owned by the caller; its contents on
+ *                 entry do not matter and are undefined on return. Calls
+ *                 that may overlap must not share one. Ignored (may be NULL)
+ *                 for USP_F32 inputs.
+ * Other arguments, layouts and errors as usp_attention_fwd, plus: bf16
+ * inputs with ws NULL or ws_bytes too small -> USP_EINVAL; ws misaligned ->
+ * USP_EALIGN.
+ */
+int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
+                         usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
+                         int32_t head_lo, int32_t head_hi, float scale, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
  * Head-chunked attention (maxdiffusion PR #428, two-phase Ulysses: attention
  * over head sub-groups in turn, mathematically the single-shot result since
  * heads are independent): runs usp_attention_fwd over each range of
- * usp_head_chunk_ranges(h, chunks) in order on `stream`: bitwise equal to
- * those usp_attention_fwd calls, and equal to the single-shot call up to the
- * rounding of split tail tiles described there. Errors: those of usp_head_chunk_ranges and
+ * usp_head_chunk_ranges(h, chunks) in order on `stream`. Bitwise equal to
+ * the single-shot call. Errors: those of usp_head_chunk_ranges and
  * usp_attention_fwd.
  */
 int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,

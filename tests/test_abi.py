@@ -98,6 +98,40 @@ def test_attention_rejects(kw, status):
     assert usp.usp_last_error()
 
 
+def _ws_bytes(i, B, S, heads, D):
+    out = ctypes.c_size_t(12345)
+    st = L.usp_attention_workspace_bytes(i, B, S, heads, D, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_bytes():
+    # two key halves x 256-row tiles x (D unnormalised O + 1 maximum + 2 row sums) fp32
+    assert _ws_bytes(1, 1, 32760, 5, 128) == (0, 128 * 5 * 2 * 256 * 131 * 4)
+    assert _ws_bytes(1, 2, 257, 3, 64) == (0, 2 * 3 * 2 * 2 * 256 * 67 * 4)
+    assert _ws_bytes(1, 1, 1, 1, 64) == (0, 2 * 256 * 67 * 4)
+    assert _ws_bytes(0, 1, 1000, 4, 64) == (0, 0)  # fp32 inputs need none
+    assert usp.usp_attention_workspace_bytes(usp.USP_BF16, 1, 512, 2, 128) == 2 * 2 * 2 * 256 * 131 * 4
+    assert L.usp_attention_workspace_bytes(1, 1, 16, 2, 64, None) == -1
+    assert _ws_bytes(1, 0, 16, 2, 64)[0] == -2
+    assert _ws_bytes(1, 1, 16, 0, 64)[0] == -2
+    assert _ws_bytes(7, 1, 16, 2, 64)[0] == -3
+
+
+def _attn_ws(ws=FAKE, nbytes=1 << 40, q=FAKE, i=1, out=0, B=1, S=16, h=2, D=64, lo=0, hi=2):
+    return L.usp_attention_fwd_ws(q, FAKE, FAKE, FAKE, i, out, B, S, h, D, lo, hi, 0.0, None, ws,
+                                  nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), -1), (dict(ws=FAKE + 4), -4), (dict(nbytes=1000), -1),
+    (dict(nbytes=2 * 2 * 256 * 67 * 4 - 1), -1), (dict(q=None), -1), (dict(D=96), -5),
+    (dict(lo=0, hi=3), -1),
+])
+def test_attention_ws_rejects(kw, status):
+    assert _attn_ws(**kw) == status
+    assert usp.usp_last_error()
+
+
 def test_chunked_rejects():
     f = L.usp_attention_fwd_chunked
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 64, 0.0, None, 4, None) == -1  # empty chunk

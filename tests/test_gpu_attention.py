@@ -35,6 +35,24 @@ def _run(q, k, v, dtype, out_dtype, lo=0, hi=None, scale=0.0, want_lse=False, ch
     return (out, lse.cpu().numpy()) if want_lse else out
 
 
+def _run_ws(q, k, v, dtype, out_dtype, lo=0, hi=None, want_lse=False):
+    """usp_attention_fwd_ws with a NaN-poisoned workspace of exactly the size
+    the library asks for."""
+    import torch
+    B, S, h, D = q.shape
+    hi = h if hi is None else hi
+    nb = usp.usp_attention_workspace_bytes(usp.USP_BF16 if dtype == BF else usp.USP_F32,
+                                           B, S, hi - lo, D)
+    ws = torch.full((max(nb, 16) // 4,), float("nan"), device=DEV)
+    dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
+    o = poisoned((B, S, h, D), out_dtype)
+    lse = torch.full((B, h, S), float("nan"), device=DEV) if want_lse else None
+    usp.usp_attention_fwd_ws(dq, dk, dv, o, ws, head_lo=lo, head_hi=hi, lse=lse)
+    torch.cuda.synchronize()
+    out = to_host(o)
+    return (out, lse.cpu().numpy()) if want_lse else out
+
+
 SMALL = [  # B, S, h, D : several tiles and ragged tails on both kernels' tilings
     (1, 1, 1, 64), (1, 2, 2, 128), (1, 31, 1, 64), (2, 65, 3, 128), (1, 257, 2, 64),
     (1, 300, 1, 128), (1, 1000, 2, 128), (2, 513, 2, 64), (1, 777, 3, 64), (1, 129, 1, 128),
@@ -88,44 +106,42 @@ def test_peaky_softmax_small():
 
 
 @pytest.mark.parametrize("h,chunks", [(8, 3), (5, 2), (3, 3), (4, 1)])
-def test_chunked_equals_head_range_calls_small(h, chunks):
-    """A chunked call is its head-range passes, bit for bit; it matches the
-    single-shot call and the oracle to the attention tolerance (a tail tile
-    split over keys can round differently under another head grouping)."""
+def test_chunked_bitwise_equals_single_shot_small(h, chunks):
+    """Chunked passes equal the single-shot call and the per-range calls,
+    bit for bit, and the oracle to the attention tolerance."""
     q, k, v = synth.draw_qkv(1, 333, h, 128, seed=h)
     log(f"attention chunked h={h} chunks={chunks}")
     one = _run(q, k, v, BF, F)
     many = _run(q, k, v, BF, F, chunks=chunks)
+    assert one.tobytes() == many.tobytes()
     cb = usp.usp_head_chunk_ranges(h, chunks)
     by_range = np.concatenate([_run(q, k, v, BF, F, lo=cb[j], hi=cb[j + 1])[:, :, cb[j]:cb[j + 1]]
                                for j in range(chunks)], axis=2)
-    assert many.tobytes() == by_range.tobytes()
+    assert one.tobytes() == by_range.tobytes()
     ref = A.attention(*(widen(x, BF) for x in (q, k, v)))
-    for out in (one, many):
-        ma, rf = err(out, ref)
-        assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    ma, rf = err(one, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
 
 
-# Launch plans of the bf16 kernel on a device holding 256 workgroups at once
-# (one 512-thread workgroup per CU on 256 CUs), 256 query rows per tile, key
-# tiles of 64 (D=128) or 128 (D=64) keys. A last round of t <= 128 tiles is
-# split over keys into min(256 // t, 4, key tiles) parts.
-SPLIT_CASES = [  # B, S, h, D, plan
-    (1, 257, 50, 128, "100 tiles, 2 parts of 5 key tiles (2 + 3, last has 1 key)"),
-    (1, 513, 25, 64, "75 tiles, 3 parts of 5 key tiles (1 + 2 + 2)"),
-    (1, 1000, 2, 128, "8 tiles, 4 parts of 16 key tiles"),
-    (1, 257, 178, 64, "356 tiles: 256 whole, 100 in 2 parts"),
-    (1, 257, 100, 128, "200 tiles: tail over half a round, no split"),
-    (3, 64, 7, 128, "21 tiles of one key tile each, no split"),
+# Launch plans on a device with 256 CUs: tiles of 256 query rows; whole
+# rounds of 256 tiles run as 8-wave workgroups, a last round of t <= 128
+# tiles as 2t 4-wave workgroups of 128 rows (one per CU).
+TAIL_CASES = [  # B, S, h, D, plan
+    (1, 257, 50, 128, "100 tiles, all in 4-wave halves (second halves past S)"),
+    (1, 513, 25, 64, "75 tiles, all in 4-wave halves"),
+    (1, 1000, 2, 128, "8 tiles, all in 4-wave halves"),
+    (1, 257, 178, 64, "356 tiles: 256 whole, 100 in halves"),
+    (1, 257, 100, 128, "200 tiles: a tail over half the CUs runs whole"),
+    (3, 64, 7, 128, "21 tiles of one key tile each, in halves"),
 ]
 
 
-@pytest.mark.parametrize("B,S,h,D,plan", SPLIT_CASES)
-def test_tail_split_plans(B, S, h, D, plan):
+@pytest.mark.parametrize("B,S,h,D,plan", TAIL_CASES)
+def test_tail_round_plans(B, S, h, D, plan):
     q, k, v = synth.draw_qkv(B, S, h, D, seed=11 + S + h)
     qf, kf, vf = (widen(x, BF) for x in (q, k, v))
     ref, ref_lse = A.attention(qf, kf, vf, return_lse=True)
-    log(f"attention tail split B={B} S={S} h={h} D={D}: {plan}")
+    log(f"attention tail plan B={B} S={S} h={h} D={D}: {plan}")
     out, lse = _run(q, k, v, BF, F, want_lse=True)
     ma, rf = err(out, ref)
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
@@ -134,31 +150,52 @@ def test_tail_split_plans(B, S, h, D, plan):
     assert np.all(np.abs(ob - ref) <= np.maximum(BF16_MAX_ABS, bf16_ulp(ref)))
 
 
-def test_split_workspace_per_stream():
-    """Calls on two streams (each with its own workspace) and repeated calls
-    on one stream give identical bits."""
-    import torch
-    B, S, h, D = 1, 1000, 2, 128
-    q, k, v = synth.draw_qkv(B, S, h, D, seed=21)
-    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
-    outs = []
-    s2 = torch.cuda.Stream()
-    log("attention on the current stream twice, then on a second stream")
-    for stream in (None, None, s2):
-        o = poisoned((B, S, h, D), F)
-        if stream is None:
-            usp.usp_attention_fwd(dq, dk, dv, o)
-        else:
-            s2.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s2):
-                usp.usp_attention_fwd(dq, dk, dv, o)
-            torch.cuda.current_stream().wait_stream(s2)
-        torch.cuda.synchronize()
-        outs.append(to_host(o))
-    assert outs[0].tobytes() == outs[1].tobytes() == outs[2].tobytes()
-    ref = A.attention(*(widen(x, BF) for x in (q, k, v)))
-    ma, rf = err(outs[0], ref)
+@pytest.mark.parametrize("D", [128, 64])
+def test_rows_bitwise_independent_of_launch(D):
+    """40 heads at once are 160 tiles, a tail over more than half the CUs, so
+    every tile runs in an 8-wave workgroup; head ranges of 10 heads are 40
+    tiles each, all in 4-wave halves. Both give the same bits."""
+    q, k, v = synth.draw_qkv(1, 1000, 40, D, seed=31)
+    log(f"attention D={D}: 40 heads in one launch vs four launches of 10 heads")
+    one = _run(q, k, v, BF, F)
+    parts = np.concatenate([_run(q, k, v, BF, F, lo=lo, hi=lo + 10)[:, :, lo:lo + 10]
+                            for lo in range(0, 40, 10)], axis=2)
+    assert one.tobytes() == parts.tobytes()
+    sub = slice(0, 40, 13)
+    ref = A.attention(*(widen(x[:, :, sub], BF) for x in (q, k, v)))
+    ma, rf = err(one[:, :, sub], ref)
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+
+
+WS_CASES = [  # B, S, h, D: one key tile (empty first half), odd key-tile counts, both D
+    (1, 1, 1, 64), (1, 64, 3, 128), (1, 257, 5, 128), (2, 513, 2, 64), (1, 1000, 2, 128),
+    (1, 130, 4, 64), (3, 300, 2, 128),
+]
+
+
+@pytest.mark.parametrize("B,S,h,D", WS_CASES)
+def test_workspace_path_bitwise_equals_default(B, S, h, D):
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=41 + S)
+    log(f"attention with workspace B={B} S={S} h={h} D={D}")
+    for out_dtype in (F, BF):
+        a, la = _run(q, k, v, BF, out_dtype, want_lse=True)
+        b, lb = _run_ws(q, k, v, BF, out_dtype, want_lse=True)
+        assert a.tobytes() == b.tobytes()
+        assert la.tobytes() == lb.tobytes()
+    if h > 1:
+        a = _run(q, k, v, BF, F, lo=1, hi=h)
+        b = _run_ws(q, k, v, BF, F, lo=1, hi=h)
+        assert a.tobytes() == b.tobytes()
+        assert np.all(np.isnan(b[:, :, 0]))
+    ref = A.attention(*(widen(x, BF) for x in (q, k, v)))
+    ma, rf = err(_run_ws(q, k, v, BF, F), ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+
+
+def test_workspace_path_fp32_inputs():
+    q, k, v = synth.draw_qkv(1, 100, 2, 64, seed=3, dtype=F)
+    log("attention with workspace, fp32 inputs (no workspace used)")
+    assert _run_ws(q, k, v, F, F).tobytes() == _run(q, k, v, F, F).tobytes()
 
 
 def _ulysses_gpu(w: synth.Workload, q, k, v, out_dtype):
@@ -263,6 +300,16 @@ def test_video_dit_share_full_size():
     torch.cuda.synchronize()
     out = to_host(o)
     assert not np.any(np.isnan(out))
+    log("workload video_dit_share: attention block 0 with a workspace")
+    ws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, w.B, w.S, h0, w.D) // 4,
+                     device=DEV)
+    o2 = poisoned((w.B, w.S, h0, w.D), F)
+    lse2 = torch.empty((w.B, h0, w.S), device=DEV)
+    usp.usp_attention_fwd_ws(blocks[0], blocks[1], blocks[2], o2, ws, lse=lse2)
+    torch.cuda.synchronize()
+    assert to_host(o2).tobytes() == out.tobytes()
+    assert lse2.cpu().numpy().tobytes() == lse.cpu().numpy().tobytes()
+    del ws, o2, lse2
     sl = slice(hb[0], hb[1])
     rows = {(0, hd): _sample_rows(w.S, 256, 30 + hd) for hd in range(h0)}
     _check_sampled(out, q[:, :, sl], k[:, :, sl], v[:, :, sl], BF, w.B, w.S, rows,
@@ -277,9 +324,6 @@ def test_long_chunked_full_size():
     log("workload long_chunked: 3 head-chunk passes")
     many = _run(q, k, v, BF, F, chunks=w.chunks)
     assert usp.usp_head_chunk_ranges(w.H, w.chunks) == [0, 3, 6, 8]
-    # 512 query tiles per head: 4096 tiles single shot and 1536, 1536, 1024
-    # per pass are whole rounds on 256 CUs, so no pass splits a tile and the
-    # passes reproduce the single-shot bits
     assert one.tobytes() == many.tobytes()
     assert not np.any(np.isnan(one))
     rows = {(0, hd): _sample_rows(w.S, 64, 40 + hd) for hd in range(w.H)}

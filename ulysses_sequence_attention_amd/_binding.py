@@ -64,9 +64,15 @@ def lib() -> ctypes.CDLL:
                                         _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
         L.usp_attention_fwd_chunked.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
                                                 _i64, _i64, _i32, _i32, _f32, _vp, _i32, _vp]
+        L.usp_attention_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i32, _i32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.usp_attention_fwd_ws.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
+                                           _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+                                           ctypes.c_size_t, _vp]
         for name in ("usp_balanced_ranges", "usp_balanced_ranges_device", "usp_head_chunk_ranges",
                      "usp_pack_seq_to_heads", "usp_unpack_heads_to_seq", "usp_attention_fwd",
-                     "usp_attention_fwd_chunked"):
+                     "usp_attention_fwd_chunked", "usp_attention_workspace_bytes",
+                     "usp_attention_fwd_ws"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -172,11 +178,29 @@ def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float =
            "usp_attention_fwd")
 
 
+def usp_attention_workspace_bytes(in_dtype: int, B: int, S: int, heads: int, D: int) -> int:
+    """Workspace bytes usp_attention_fwd_ws needs (``in_dtype``: USP_F32 or USP_BF16)."""
+    out = ctypes.c_size_t(0)
+    _check(lib().usp_attention_workspace_bytes(in_dtype, B, S, heads, D, ctypes.byref(out)),
+           "usp_attention_workspace_bytes")
+    return out.value
+
+
+def usp_attention_fwd_ws(q, k, v, o, ws, head_lo: int = 0, head_hi=None, scale: float = 0.0,
+                         lse=None, stream=None) -> None:
+    """usp_attention_fwd with the caller's workspace tensor ``ws`` (any dtype;
+    its byte size is passed; None for fp32 inputs)."""
+    B, S, h, D = q.shape
+    hi = h if head_hi is None else head_hi
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().usp_attention_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B,
+                                      S, h, D, head_lo, hi, scale, _ptr(lse), _ptr(ws), nbytes,
+                                      _stream(q, stream)), "usp_attention_fwd_ws")
+
+
 def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=None,
                               stream=None) -> None:
-    """Attention as ``chunks`` head-chunk passes, one usp_attention_fwd per
-    range of usp_head_chunk_ranges (the single-shot result up to the rounding
-    of split tail tiles)."""
+    """Attention as ``chunks`` head-chunk passes (bitwise equal to single shot)."""
     B, S, h, D = q.shape
     _check(lib().usp_attention_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
                                            _dtype(o), B, S, h, D, scale, _ptr(lse), chunks,

@@ -7,18 +7,17 @@
 //
 // Work decomposition. A workgroup of NW waves owns BM = NW * QB * 32 query
 // rows of one (batch, head); each wave owns QB blocks of 32 rows (one MFMA
-// column block each). Keys are walked in tiles of BN rows staged in LDS (K
-// row-major, V transposed). With 8 waves of 32 rows, two waves share each
-// SIMD.
+// column block each). Keys are walked in tiles of BN rows staged in LDS,
+// both row-major. With 8 waves of 32 rows, two waves share each SIMD.
 //
 // Software pipeline. K is staged one tile ahead of V: while iteration j
 // turns the scores of tile j into weights (exp2, VALU), the same basic block
 // computes the scores of tile j + 1 (MFMA), so the matrix pipe and the VALU
 // work at once inside one wave; then the weights of tile j multiply V_j.
-// LDS holds two K tiles and two V^T tiles; the global loads of K_{j+2} and
-// V_{j+1} are issued at the top of iteration j and written to LDS at its end,
-// with one barrier per tile. The last (possibly partial) tile is peeled off
-// the loop so the steady-state body carries no key mask.
+// LDS holds two K tiles and two V tiles; iteration j issues the direct
+// global-to-LDS loads of K_{j+2} and V_{j+1} at its top and ends with one
+// barrier. The last (possibly partial) tile is peeled off the loop so the
+// steady-state body carries no key mask.
 //
 // Layout trick. The score block is computed transposed, S^T = K Q^T (A = K,
 // B = Q^T), so a lane of the 32x32 accumulator holds 16 keys of ONE query
@@ -29,8 +28,9 @@
 // register r (< 16) of a lane in half g holds key 16(r / 8) + 8g + (r % 8):
 // registers 0..7 and 8..15 are each 8 consecutive keys, which is exactly the
 // B operand layout of the second product O^T = V^T P^T (A = V^T). So P^T
-// goes from accumulators to bf16 operands without any lane exchange, and
-// V^T fragments are single 16-byte LDS reads of 8 consecutive keys.
+// goes from accumulators to bf16 operands without any lane exchange; the
+// V^T fragments (8 consecutive keys of one head-dim column) come from the
+// row-major V tile through two transposing LDS reads.
 //
 // Online softmax (base 2: weights are exp2(c * s - c * m), c = scale *
 // log2(e)) with lazy rescaling: the reference maximum m of a row is only
@@ -42,23 +42,27 @@
 // (v_dot2c_f32_bf16 against (1, 1)), so the rounding of a dominant weight
 // cancels between numerator and denominator.
 //
-// Tail split. One workgroup fills a CU, so a launch of W query tiles on C
-// CUs runs in ceil(W / C) rounds and a last round holding W mod C <= C / 2
-// tiles leaves most CUs idle. Those tail tiles are instead split over their
-// key range into f = min(C / (W mod C), 4) parts run by separate workgroups;
-// each part writes its softmax-normalised O rows (fp32) and base-2 log-sum-
-// exp to a workspace, and a merge kernel combines the f parts of a row with
-// weights 2^(lse_i - lse). The split changes only the rounding of the rows
-// it touches; which tiles split depends on the launch size, so results are
-// bitwise reproducible per launch shape, not across head groupings.
+// Key halves. Every row's key range is split once, at key tile
+// floor(nkt / 2) (nkt = ceil(S / BN)), into two walks whose softmax states
+// (reference maximum m, row sum l, unnormalised O) are merged at the end
+// with weights 2^(c (m_i - M)), M the larger maximum. The split point
+// depends on S and D only, so a row's bits never depend on the launch (its
+// head range, batch or the device); splitting the work this way gives 2x
+// as many work units, which keeps the last round of a launch from running
+// half empty (a workgroup fills a CU, and at S = 32760, 128 tiles of 256
+// rows per head, a head is exactly one round of 256 half-walks). Two forms:
+//   * key groups (usp_attention_fwd): a workgroup of 8 waves is two groups
+//     of 4 waves that walk the two halves for the same 128 rows, each with
+//     its own K/V buffers, and merge through LDS;
+//   * key-half parts (usp_attention_fwd_ws): 8-wave workgroups of 256 rows
+//     walk one half each and leave their state in a caller workspace, and
+//     attn_merge_halves merges them with the same arithmetic. Half as much
+//     K/V staging per row; same bits.
 //
 // Block -> tile order is XCD aware: the hardware deals workgroup ids round
 // robin over the 8 XCDs, so ids are remapped to give each XCD a contiguous
 // range of (batch, head, query tile) work, keeping one head's K/V stream in
-// one XCD's L2. Unsplit tiles take the low ids (they are dispatched first),
-// the tail's parts the high ids.
-#include <algorithm>
-#include <atomic>
+// one XCD's L2.
 #include <type_traits>
 
 #include "usp_internal.h"
@@ -74,22 +78,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Tile shapes (waves per workgroup, 32-row query blocks per wave, keys per
-// tile) per head dim.
-#ifndef USP_D128_WAVES
-#define USP_D128_WAVES 8
-#define USP_D128_QB 1
+// Key groups per workgroup (1: 8 waves over all keys for 256 rows; 2: two
+// groups of 4 waves over the two key halves for 128 rows).
+#ifndef USP_KEY_GROUPS
+#define USP_KEY_GROUPS 2
+#endif
+// Keys per K/V tile, per head dim.
+#ifndef USP_D128_BN
 #define USP_D128_BN 64
 #endif
-#ifndef USP_D64_WAVES
-#define USP_D64_WAVES 8
-#define USP_D64_QB 1
+#ifndef USP_D64_BN
 #define USP_D64_BN 128
 #endif
 
 constexpr float kTau = 1.0f;  // lazy-rescale threshold, log2 units
-constexpr int kMaxSplit = 4;  // most key-range parts a tail tile is split into
-constexpr int kBM = 256;      // query rows per workgroup, every head dim
+constexpr int kTileRows = 256;  // query rows of a tile (an 8-wave workgroup)
 
 struct Params {
   const uint16_t* q;
@@ -100,12 +103,13 @@ struct Params {
   int S, h, head_lo, nheads, n_qtiles;
   float c;      // scale * log2(e)
   float scale;  // softmax scale (for the natural-log normaliser)
-  // tail split: tiles [0, n_full) run whole; tiles [n_full, n_full + n_tail)
-  // run as nsplit key-range parts writing ws (fp32 [part][tile][kBM][D]) and
-  // ws_lse ([part][tile][kBM], base 2)
-  int n_full, n_tail, nsplit;
-  float* ws;
-  float* ws_lse;
+  // key-half walks (PARTS = 2): unit (part, tile) = part * n_tiles + tile
+  // leaves its unnormalised O rows in ws_o [unit][256][D], reference maxima
+  // in ws_m [unit][256] and the two lane-half row sums in ws_l [unit][256][2]
+  int n_tiles;
+  float* ws_o;
+  float* ws_m;
+  float* ws_l;
 };
 
 // workgroup id (< n) -> logical work id, giving each of the 8 XCDs (which
@@ -149,10 +153,17 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
 #endif
 }
 
-template <int D, int NW, int QB, int BN, bool kOutBf16>
+// KG key groups of NW / KG waves share a workgroup; PARTS = 2 makes each
+// workgroup walk one key half and leave its state in the workspace.
+template <int D, int NW, int KG, int PARTS, int BN, bool kOutBf16>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
-  constexpr int BM = NW * QB * 32;
-  static_assert(BM == kBM, "workspace rows assume kBM query rows per workgroup");
+  constexpr int QB = 1;                         // 32-row query blocks per wave
+  constexpr int GW = NW / KG;                   // waves per key group
+  static_assert(GW * KG == NW && KG <= 2, "one or two key groups of equal size");
+  static_assert(PARTS == 1 || (PARTS == 2 && KG == 1), "key halves in groups or in parts");
+  constexpr int BM = GW * QB * 32;              // query rows of the workgroup
+  constexpr int SUB = kTileRows / BM;           // workgroups per tile
+  static_assert(SUB * BM == kTileRows, "a tile must split evenly into workgroups");
   constexpr int NKB = BN / 32;           // 32-key blocks per tile
   constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;            // 32-wide blocks of the output head dim
@@ -161,33 +172,34 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   constexpr int RPL = 256 / ROWB;        // rows per 256-byte line of the 64 LDS banks
   constexpr int RPI = 1024 / ROWB;       // rows per direct load (64 lanes x 16 bytes)
   constexpr int NQ = BN * ROWB / 1024;   // direct loads per tile
-  constexpr int NI = NQ / NW;            // direct loads per wave per tile (K and V each)
-  static_assert(NI * NW == NQ, "a tile must split evenly into the waves' direct loads");
+  constexpr int NI = NQ / GW;            // direct loads per wave per tile (K and V each)
+  static_assert(NI * GW == NQ, "a tile must split evenly into the group's direct loads");
   constexpr int TB = BN * ROWB;          // bytes per K or V tile
 
-  // LDS: K tiles in buffers 0, 1, then V tiles in buffers 0, 1; rows unpadded
-  __shared__ __attribute__((aligned(16))) char lds[4 * TB];
+  // LDS: per key group K tiles in buffers 0, 1, then V tiles in buffers 0,
+  // 1; rows unpadded. After the key walk the space holds the second group's
+  // partial results for the merge.
+  constexpr int MERGE_B = GW * 64 * (NDB * 16 + 2) * 4;
+  static_assert(KG == 1 || MERGE_B <= KG * 4 * TB, "merge area must fit the tile buffers");
+  __shared__ __attribute__((aligned(16))) char lds[KG * 4 * TB];
 
-  // ---- XCD-aware workgroup -> (batch, head, query tile[, key part]) -------
-  const int bid = blockIdx.x;
-  int lid, unit = -1;  // unit: workspace slot of a tail part, -1 for a whole tile
-  if (bid < p.n_full) {
-    lid = xcd_remap(bid, p.n_full);
-  } else {
-    unit = xcd_remap(bid - p.n_full, p.n_tail * p.nsplit);  // part-major
-    lid = p.n_full + unit % p.n_tail;
-  }
+  // ---- XCD-aware workgroup -> (batch, head, query tile, sub-tile[, part])
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  const int part = PARTS == 2 ? u / p.n_tiles : 0;
+  const int lid = PARTS == 2 ? u % p.n_tiles : u / SUB, sub = PARTS == 2 ? 0 : u % SUB;
   const int qt = lid % p.n_qtiles;
   const int bh = lid / p.n_qtiles;
   const int head = p.head_lo + bh % p.nheads;
   const int b = bh / p.nheads;
 
   const int S = p.S;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = (tid >> 6) / GW, w = (tid >> 6) % GW;  // key group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
+  char* const glds = lds + grp * 4 * TB;  // this group's tile buffers
   const size_t rs = size_t(p.h) * D;                             // token row stride
   const size_t hb = size_t(b) * S * rs + size_t(head) * D;       // (b, token 0, head)
-  const int qrow0 = qt * BM + w * (QB * 32);
+  const int qrow0 = qt * kTileRows + sub * BM + w * (QB * 32);
   const float c = p.c;
 
   // ---- Q^T fragments (B operand), resident for the whole key walk --------
@@ -212,13 +224,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   //      of a fragment read fall on 16 distinct bank quads;
   //   V: chunk c of row r at position c ^ 4((r / RPL) mod (CPR / 4)), so the
   //      4 rows x 4 chunks of a transposed read are distinct bank quads.
-  // Wave w issues loads q = w + NW i of each tile (rows [q RPI, q RPI + RPI)).
+  // Wave w of a group issues loads q = w + GW i of each of the group's tiles
+  // (rows [q RPI, q RPI + RPI)).
   auto swz_k = [](int r) { return (r / RPL) % CPR; };
   auto swz_v = [](int r) { return 4 * ((r / RPL) % (CPR / 4)); };
   uint32_t kgo[NI], vgo[NI];  // per-lane element offsets from the tile's first row
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int r = (w + NW * i) * RPI + lane / CPR, pos = lane % CPR;
+    const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
     kgo[i] = uint32_t(r * rs + (pos ^ swz_k(r)) * 8);
     vgo[i] = uint32_t(r * rs + (pos ^ swz_v(r)) * 8);
   }
@@ -231,11 +244,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     for (int i = 0; i < NI; ++i) {
       uint32_t off = go[i];
       if (guard) {
-        const int r = (w + NW * i) * RPI + lane / CPR, pos = lane % CPR;
+        const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
         const int rc = min(r, S - 1 - t0);
         off = uint32_t(rc * rs + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8);
       }
-      load_lds16(base + off, lds + lbase + (w + NW * i) * 1024);
+      load_lds16(base + off, glds + lbase + (w + GW * i) * 1024);
     }
   };
   auto load_k = [&](int buf, int t0, bool guard) { issue(p.k, kgo, buf * TB, t0, guard, false); };
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 kf = as_bf16x8(
-            *reinterpret_cast<const uint4*>(lds + buf * TB + kb * 32 * ROWB + kad[s]));
+            *reinterpret_cast<const uint4*>(glds + buf * TB + kb * 32 * ROWB + kad[s]));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s],
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
       for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const char* vrow = lds + (2 + buf) * TB + (kb * 32 + h2 * 16) * ROWB + vad[db];
+          const char* vrow = glds + (2 + buf) * TB + (kb * 32 + h2 * 16) * ROWB + vad[db];
           typedef short s16x4 __attribute__((ext_vector_type(4)));
           typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow));
@@ -392,16 +405,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
       }
   };
 
-  // key tiles [kt_lo, kt_lo + nkt) of this workgroup; tile indices below
-  // are relative to kt_lo, so only the last tile of the range can be partial
+  // key tiles [kt_lo, kt_lo + nkt) of this group or part: half 0 is the
+  // first nkt_all / 2 tiles (rounded down), half 1 the rest; tile indices
+  // below are relative to kt_lo, so only the last tile of half 1 can be
+  // partial. The halves depend on S and BN only.
   const int nkt_all = (S + BN - 1) / BN;
-  const int part = unit < 0 ? 0 : unit / p.n_tail;
-  const int parts = unit < 0 ? 1 : p.nsplit;
-  const int kt_lo = part * nkt_all / parts;
-  const int nkt = (part + 1) * nkt_all / parts - kt_lo;
+  constexpr bool kHalves = KG == 2 || PARTS == 2;
+  const int half = KG == 2 ? grp : part;
+  const int kt_lo = kHalves ? half * (nkt_all / 2) : 0;
+  const int nkt = !kHalves ? nkt_all : half == 0 ? nkt_all / 2 : nkt_all - nkt_all / 2;
   auto key0 = [&](int kt) { return (kt_lo + kt) * BN; };      // first key of tile kt
   auto partial = [&](int kt) { return key0(kt) + BN > S; };   // tile runs past S
 
+  // ---- the key walk: 2 + (nkt - 1) barriers when nkt > 0 ------------------
+  if (nkt > 0) {
   // ---- prologue: K_0, V_0, K_1 in LDS; scores of tile 0 -------------------
   load_k(0, key0(0), partial(0));
   load_v(0, key0(0), partial(0));
@@ -466,31 +483,72 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     weights(sa, pf);
     pv(kt & 1, pf);
   }
+  }  // nkt > 0
+
+  if constexpr (KG == 2) {
+    // the shorter walk (group 0, by at most one tile, or empty for a single
+    // tile) matches the other group's barrier count
+    const int n1 = nkt_all - nkt_all / 2;
+    for (int i = nkt > 0 ? nkt + 1 : 0; i < n1 + 1; ++i) __syncthreads();
+    __syncthreads();  // every wave is done with its tile buffers
+    // Merge. Group 1 leaves its unnormalised O^T accumulators, reference
+    // maxima and (lane-partial) row sums in LDS; wave w of group 0, which
+    // owns the same 32 rows, weighs both sides by 2^(c (m_i - M)), M the
+    // larger maximum (a group that saw no key has m = -inf, weight 0). The
+    // arithmetic is spelled out (fmaf) because attn_merge_halves repeats it
+    // bit for bit.
+    f32x4* const mo = reinterpret_cast<f32x4*>(lds);
+    float* const mm = reinterpret_cast<float*>(lds + GW * 64 * NDB * 16 * 4);
+    float* const ml = mm + GW * 64;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[0][db][4 * a + e];
+          mo[((w * NDB + db) * 4 + a) * 64 + lane] = x;
+        }
+      mm[w * 64 + lane] = mrow[0];
+      ml[w * 64 + lane] = lrow[0];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = mm[w * 64 + lane], l1 = ml[w * 64 + lane];
+    const float mx = fmaxf(mrow[0], m1);
+    const float a0 = __builtin_amdgcn_exp2f((mrow[0] - mx) * c);
+    const float a1 = __builtin_amdgcn_exp2f((m1 - mx) * c);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 x = mo[((w * NDB + db) * 4 + a) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[0][db][4 * a + e] = fmaf(x[e], a1, oacc[0][db][4 * a + e] * a0);
+      }
+    lrow[0] = fmaf(l1, a1, lrow[0] * a0);
+    mrow[0] = mx;
+  }
 
   // ---- epilogue: normalise and store ------------------------------------------
-  if (unit >= 0) {
-    // a tail part: normalised fp32 O rows and base-2 log-sum-exp to the
-    // workspace, combined by attn_merge_kernel
+  if constexpr (PARTS == 2) {
+    // a key-half walk: the raw state goes to the workspace (rows past S too:
+    // the merge skips them)
+    const size_t ur = size_t(part) * p.n_tiles + lid;  // unit
+    const int rloc = w * 32 + l32;                      // row within the tile
+    float* const wo = p.ws_o + (ur * kTileRows + rloc) * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float lt = sum_halves(lrow[qb]);
-      const float inv = 1.0f / lt;
-      const int rloc = w * (QB * 32) + qb * 32 + l32;
-      if (qrow0 + qb * 32 + l32 < S) {
-        float* wo = p.ws + (size_t(unit) * BM + rloc) * D;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+      for (int a = 0; a < 4; ++a) {
+        f32x4 x;
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            f32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = oacc[qb][db][4 * a + e] * inv;
-            *reinterpret_cast<f32x4*>(wo + db * 32 + 8 * a + 4 * g) = x;
-          }
-        }
-        if (g == 0) p.ws_lse[size_t(unit) * BM + rloc] = mrow[qb] * c + log2f(lt);
+        for (int e = 0; e < 4; ++e) x[e] = oacc[0][db][4 * a + e];
+        *reinterpret_cast<f32x4*>(wo + db * 32 + 8 * a + 4 * g) = x;
       }
-    }
+    if (g == 0) p.ws_m[ur * kTileRows + rloc] = mrow[0];
+    p.ws_l[(ur * kTileRows + rloc) * 2 + g] = lrow[0];
     return;
   }
 #pragma unroll
@@ -519,124 +577,75 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
         }
       }
       if (p.lse && g == 0)
-        p.lse[(size_t(b) * p.h + head) * S + row] = mrow[qb] * p.scale + logf(lt);
+        p.lse[(size_t(b) * p.h + head) * S + row] = fmaf(mrow[qb], p.scale, logf(lt));
     }
   }
 }
 
-// Combines the key-range parts of the tail tiles: per row, with part
-// log-sum-exps l_i (base 2), lse = M + log2(sum_i 2^(l_i - M)) (M = max l_i)
-// and O = sum_i 2^(l_i - lse) O_i. One thread per 4 head-dim elements of a
-// row; a row's threads are consecutive, so workspace reads and output
-// writes are contiguous.
+// Merges the two key-half states of every row left by the PARTS = 2 walks,
+// with the arithmetic of the in-workgroup merge of the key-group kernel
+// (and its epilogue), so both give the same bits. One thread per 4
+// head-dim elements of a row; a row's threads are consecutive.
 template <int D, bool kOutBf16>
-__global__ __launch_bounds__(256) void attn_merge_kernel(Params p) {
+__global__ __launch_bounds__(256) void attn_merge_halves(Params p) {
   constexpr int CH = D / 4;
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= int64_t(p.n_tail) * kBM * CH) return;
+  if (idx >= int64_t(p.n_tiles) * kTileRows * CH) return;
   const int ch = int(idx % CH);
   const int64_t tr = idx / CH;
-  const int r = int(tr % kBM), i = int(tr / kBM);
-  const int lid = p.n_full + i;
+  const int r = int(tr % kTileRows), lid = int(tr / kTileRows);
   const int qt = lid % p.n_qtiles, bh = lid / p.n_qtiles;
   const int head = p.head_lo + bh % p.nheads, b = bh / p.nheads;
-  const int row = qt * kBM + r;
+  const int row = qt * kTileRows + r;
   if (row >= p.S) return;
-
-  float l2[kMaxSplit];
-  float m = -INFINITY;
+  const size_t u0 = size_t(lid) * kTileRows + r, u1 = (size_t(p.n_tiles) + lid) * kTileRows + r;
+  const float m0 = p.ws_m[u0], m1 = p.ws_m[u1];
+  const float mx = fmaxf(m0, m1);
+  const float a0 = __builtin_amdgcn_exp2f((m0 - mx) * p.c);
+  const float a1 = __builtin_amdgcn_exp2f((m1 - mx) * p.c);
+  const float lg0 = fmaf(p.ws_l[u1 * 2], a1, p.ws_l[u0 * 2] * a0);
+  const float lg1 = fmaf(p.ws_l[u1 * 2 + 1], a1, p.ws_l[u0 * 2 + 1] * a0);
+  const float lt = lg0 + lg1;
+  const float inv = 1.0f / lt;
+  const f32x4 x0 = *reinterpret_cast<const f32x4*>(p.ws_o + u0 * D + ch * 4);
+  const f32x4 x1 = *reinterpret_cast<const f32x4*>(p.ws_o + u1 * D + ch * 4);
+  f32x4 y;
 #pragma unroll
-  for (int j = 0; j < kMaxSplit; ++j) {
-    if (j < p.nsplit) {
-      l2[j] = p.ws_lse[(size_t(j) * p.n_tail + i) * kBM + r];
-      m = fmaxf(m, l2[j]);
-    }
-  }
-  float wsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kMaxSplit; ++j) {
-    if (j < p.nsplit) {
-      const float wj = __builtin_amdgcn_exp2f(l2[j] - m);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(
-          p.ws + ((size_t(j) * p.n_tail + i) * kBM + r) * D + ch * 4);
-      wsum += wj;
-      acc += wj * x;
-    }
-  }
-  acc *= 1.0f / wsum;
+  for (int e = 0; e < 4; ++e) y[e] = fmaf(x1[e], a1, x0[e] * a0) * inv;
   const size_t ob = ((size_t(b) * p.S + row) * p.h + head) * D + ch * 4;
   if (kOutBf16)
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ob) = __builtin_convertvector(acc, bf16x4);
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ob) = __builtin_convertvector(y, bf16x4);
   else
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + ob) = acc;
-  if (p.lse && ch == 0)
-    p.lse[(size_t(b) * p.h + head) * p.S + row] = (m + log2f(wsum)) * 0.69314718055994531f;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + ob) = y;
+  if (p.lse && ch == 0) p.lse[(size_t(b) * p.h + head) * p.S + row] = fmaf(mx, p.scale, logf(lt));
 }
 
-// Workgroups of one kernel resident at once on the current device (CUs x
-// workgroups per CU), cached per device.
-template <typename K>
-int resident_slots(K kernel, int threads) {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int cus = 0, per = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  v = cus * per;
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
+// Bytes of the key-half workspace for `tiles` tiles of 256 rows.
+size_t halves_ws_bytes(int64_t tiles, int D) {
+  return size_t(tiles) * 2 * kTileRows * (size_t(D) + 3) * sizeof(float);
 }
 
-template <int D, int NW, int QB, int BN, bool kOutBf16>
-int launch_split(Params& p, int64_t tiles, hipStream_t s) {
-  constexpr int kThreads = NW * 64;
-  auto* kern = attn_bf16_kernel<D, NW, QB, BN, kOutBf16>;
-  // plan the tail split
-  const int nkt = (p.S + BN - 1) / BN;
-  const int slots = resident_slots(kern, kThreads);
-  int64_t tail = 0;
-  int f = 1;
-  if (slots > 0) {
-    tail = tiles % slots;
-    if (tail > 0 && 2 * tail <= slots) f = int(std::min<int64_t>({slots / tail, kMaxSplit, nkt}));
+template <int D, int BN, bool kOutBf16>
+int launch_tiles(Params& p, int64_t tiles, void* ws, hipStream_t s) {
+  if (!ws) {
+    // key groups: two 128-row workgroups per tile
+    attn_bf16_kernel<D, 8, 2, 1, BN, kOutBf16><<<unsigned(tiles * 2), 512, 0, s>>>(p);
+    return check_launch("attn_bf16_kernel");
   }
-  if (f >= 2) {
-    // room for any plan on this device: f * tail <= slots parts
-    const size_t bytes = size_t(slots) * kBM * (128 + 1) * sizeof(float);
-    float* ws = static_cast<float*>(stream_workspace(bytes, s));
-    if (ws) {
-      p.ws = ws;
-      p.ws_lse = ws + size_t(slots) * kBM * 128;
-    } else {
-      f = 1;  // no workspace (e.g. under stream capture): run every tile whole
-    }
-  }
-  if (f < 2) tail = 0;
-  p.n_full = int(tiles - tail);
-  p.n_tail = int(tail);
-  p.nsplit = f;
-  const int64_t grid = p.n_full + int64_t(f) * tail;
-  if (grid > 0x7fffffff) return fail(USP_ESHAPE, "attention grid too large");
-  kern<<<unsigned(grid), kThreads, 0, s>>>(p);
-  if (int st = check_launch("attn_bf16_kernel")) return st;
-  if (tail > 0) {
-    const int64_t threads = tail * kBM * (D / 4);
-    attn_merge_kernel<D, kOutBf16><<<unsigned((threads + 255) / 256), 256, 0, s>>>(p);
-    if (int st = check_launch("attn_merge_kernel")) return st;
-  }
-  return USP_OK;
+  // key halves in separate 256-row workgroups, then the merge
+  p.n_tiles = int(tiles);
+  p.ws_o = static_cast<float*>(ws);
+  p.ws_m = p.ws_o + size_t(tiles) * 2 * kTileRows * D;
+  p.ws_l = p.ws_m + size_t(tiles) * 2 * kTileRows;
+  attn_bf16_kernel<D, 8, 1, 2, BN, kOutBf16><<<unsigned(tiles * 2), 512, 0, s>>>(p);
+  if (int st = check_launch("attn_bf16_kernel (key halves)")) return st;
+  const int64_t threads = tiles * kTileRows * (D / 4);
+  attn_merge_halves<D, kOutBf16><<<unsigned((threads + 255) / 256), 256, 0, s>>>(p);
+  return check_launch("attn_merge_halves");
 }
 
-template <int D, int NW, int QB, int BN>
+template <int D, int BN>
 int launch(const AttnArgs& a, hipStream_t s) {
-  constexpr int BM = NW * QB * 32;
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -647,26 +656,32 @@ int launch(const AttnArgs& a, hipStream_t s) {
   p.h = a.h;
   p.head_lo = a.head_lo;
   p.nheads = a.head_hi - a.head_lo;
-  p.n_qtiles = int((a.S + BM - 1) / BM);
+  p.n_qtiles = int((a.S + kTileRows - 1) / kTileRows);
   p.c = a.scale * 1.4426950408889634f;
   p.scale = a.scale;
-  p.n_full = p.n_tail = 0;
-  p.nsplit = 1;
-  p.ws = p.ws_lse = nullptr;
+  p.n_tiles = 0;
+  p.ws_o = p.ws_m = p.ws_l = nullptr;
   const int64_t tiles = int64_t(p.n_qtiles) * p.nheads * a.B;
-  if (tiles > 0x7fffffff) return fail(USP_ESHAPE, "attention grid too large");
-  return a.out_dt == USP_BF16 ? launch_split<D, NW, QB, BN, true>(p, tiles, s)
-                              : launch_split<D, NW, QB, BN, false>(p, tiles, s);
+  if (tiles > 0x3fffffff) return fail(USP_ESHAPE, "attention grid too large");
+  if (a.ws && a.ws_bytes < halves_ws_bytes(tiles, a.D))
+    return fail(USP_EINVAL, "workspace of %zu bytes is below the %zu this call needs", a.ws_bytes,
+                halves_ws_bytes(tiles, a.D));
+  return a.out_dt == USP_BF16 ? launch_tiles<D, BN, true>(p, tiles, a.ws, s)
+                              : launch_tiles<D, BN, false>(p, tiles, a.ws, s);
 }
 
 }  // namespace
 
+size_t attention_bf16_ws_bytes(int64_t B, int64_t S, int32_t heads, int32_t D) {
+  return halves_ws_bytes((S + kTileRows - 1) / kTileRows * heads * B, D);
+}
+
 int launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   switch (a.D) {
     case 128:
-      return launch<128, USP_D128_WAVES, USP_D128_QB, USP_D128_BN>(a, s);
+      return launch<128, USP_D128_BN>(a, s);
     case 64:
-      return launch<64, USP_D64_WAVES, USP_D64_QB, USP_D64_BN>(a, s);
+      return launch<64, USP_D64_BN>(a, s);
     default:
       return fail(USP_ENOSYS, "bf16 attention: unsupported D %d", a.D);
   }

@@ -4,10 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include <map>
-#include <mutex>
 #include <string>
-#include <utility>
 
 #include "usp_internal.h"
 
@@ -34,39 +31,6 @@ int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(USP_EHIP, "%s: %s", what, hipGetErrorString(e));
   return USP_OK;
-}
-
-void* stream_workspace(size_t bytes, hipStream_t s) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> buffers;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> lock(mu);
-  auto& e = buffers[{dev, s}];
-  if (e.first && e.second >= bytes) return e.first;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  if (e.first) {
-    // earlier launches on this stream may still read the old buffer
-    if (hipStreamSynchronize(s) != hipSuccess || hipFree(e.first) != hipSuccess) {
-      (void)hipGetLastError();
-      return nullptr;
-    }
-    e = {nullptr, 0};
-  }
-  void* ptr = nullptr;
-  if (hipMalloc(&ptr, bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  e = {ptr, bytes};
-  return ptr;
 }
 
 // Balanced contiguous ranges (h3-blackwell-runtime distributed.py,
@@ -218,8 +182,40 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
 int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
                       usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
                       int32_t head_lo, int32_t head_hi, float scale, float* lse, void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt};
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0};
   if (int st = check_attention(a)) return st;
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_attention_workspace_bytes(usp_dtype in_dt, int64_t B, int64_t S, int32_t heads,
+                                  int32_t D, size_t* bytes) {
+  if (!bytes) return fail(USP_EINVAL, "bytes is null");
+  if (B < 1 || S < 1 || heads < 1 || D < 1) return fail(USP_ESHAPE, "B, S, heads and D must be positive");
+  if (in_dt == USP_F32) {
+    *bytes = 0;
+    return ok();
+  }
+  if (in_dt != USP_BF16) return fail(USP_EDTYPE, "unsupported input dtype %d", (int)in_dt);
+  if (S > (int64_t(1) << 31) - 1024 || B * heads > (int64_t(1) << 31) - 1)
+    return fail(USP_ESHAPE, "S or B * heads too large for one launch");
+  *bytes = attention_bf16_ws_bytes(B, S, heads, D);
+  return ok();
+}
+
+int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
+                         usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
+                         int32_t head_lo, int32_t head_hi, float scale, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes};
+  if (int st = check_attention(a)) return st;
+  if (in_dt == USP_BF16) {
+    if (!ws) return fail(USP_EINVAL, "workspace is null");
+    if (!aligned16(ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
+  } else {
+    a.ws = nullptr;  // the fp32 path needs none
+  }
   if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
   if (int st = run_attention(a, (hipStream_t)stream)) return st;
   return ok();
@@ -229,7 +225,7 @@ int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void*
                               usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
                               int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
                               void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, 0, h, scale, in_dt, out_dt};
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0};
   if (int st = check_attention(a)) return st;
   if (chunks < 1 || chunks > h)
     return fail(USP_EINVAL, "cannot run %d heads in %d non-empty chunks", h, chunks);

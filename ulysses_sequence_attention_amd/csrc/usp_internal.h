@@ -35,13 +35,6 @@ struct FastDiv {
   }
 };
 
-// Device scratch owned by the library, one buffer per (current device,
-// stream), grown to at least `bytes` on first need and kept until the process
-// ends. Work on one stream is ordered, so its launches share the buffer
-// safely. Returns nullptr (and allocates nothing) when the buffer must grow
-// while the stream is being captured into a graph, or when hipMalloc fails.
-void* stream_workspace(size_t bytes, hipStream_t s);
-
 // Kernel launchers (one per translation unit).
 int launch_ranges_device(int64_t total, int32_t parts, int64_t* d_bounds, hipStream_t s);
 
@@ -63,8 +56,12 @@ struct AttnArgs {
   int32_t h, D, head_lo, head_hi;
   float scale;
   usp_dtype in_dt, out_dt;
+  void* ws;         // bf16 path: key-half workspace, or nullptr for the key-group kernel
+  size_t ws_bytes;
 };
 int launch_attention_f32(const AttnArgs& a, hipStream_t s);
 int launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+// Workspace bytes the bf16 key-half path needs for B x heads x S rows.
+size_t attention_bf16_ws_bytes(int64_t B, int64_t S, int32_t heads, int32_t D);
 
 }  // namespace usp
