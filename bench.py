@@ -10,8 +10,12 @@ path, every row of it:
   pack     rank 0's token shard [1, 4095, 40, 128] of Q, K and V into the 8
            head-group blocks [1, 32760, 5, 128] (the data rank 0 sends in the
            first all-to-all; the other ranks' rows were placed beforehand)
-  attn     non-causal attention over the full sequence on block 0 (h = 5)
+  attn     non-causal attention over the full sequence on block 0 (h = 5),
+           usp_attention_fwd_ws with its workspace allocated beforehand
   unpack   rank 0's rows of the 8 output blocks back to [1, 4095, 40, 128]
+
+The attention of usp_attention_fwd (no workspace; the same bits) is timed
+on its own as well and reported as "attention_no_workspace".
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
 Also reported: each kernel alone (HIP events around each launch on the
@@ -23,9 +27,9 @@ launch stream), the world-tensor pack / unpack bandwidth of the full
 cpu_baseline: the float64 CPU oracle on a bounded sample of query rows of
 the same attention, on every host core this process may use.
 
-roofline: the attention call (usp_attention_fwd: the flash kernel plus, when
-the last round of query tiles is split over keys, the small merge kernel) is
-the dominant step; ``achieved`` is its flops over its event-timed duration.
+roofline: the attention call (usp_attention_fwd_ws: the key-half flash
+kernel, then the merge kernel) is the dominant step; ``achieved`` is its
+flops over its event-timed duration.
 roofline.traffic: HBM bytes per attention call from rocprofv3 FETCH_SIZE /
 WRITE_SIZE counter runs (both kernels), each scaled by what the counter reads
 for the plain copy kernel of known size in the same run (``--pmc-summary``);
@@ -114,8 +118,9 @@ def pmc_summary(dirs, out_json):
             with open(path) as f:
                 for r in csv.DictReader(f):
                     name = r["Kernel_Name"]
-                    kind = ("attention" if "attn_bf16_kernel" in name else
-                            "merge" if "attn_merge_kernel" in name else
+                    kind = ("attention" if "attn_bf16_kernel<128, 8, 1, 2," in name else
+                            "attention_groups" if "attn_bf16_kernel<128, 8, 2, 1," in name else
+                            "merge" if "attn_merge_halves" in name else
                             "copy" if "copyBuffer" in name else
                             "pack" if "relayout_kernel<true>" in name else
                             "unpack" if "relayout_kernel<false>" in name else None)
@@ -136,7 +141,7 @@ def pmc_summary(dirs, out_json):
                  f"FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}" if ff and fw else
                  "copy calibration missing")
     res = {"source_sha256": source_digest(), "fetch_factor": ff, "write_factor": fw}
-    for kind in ("attention", "merge", "pack", "unpack"):
+    for kind in ("attention", "merge", "attention_groups", "pack", "unpack"):
         f_k, w_k = avg.get((kind, "FETCH_SIZE")), avg.get((kind, "WRITE_SIZE"))
         if f_k is not None and w_k is not None and ff and fw:
             rb, wb = f_k * 1024 * ff, w_k * 1024 * fw
@@ -144,7 +149,7 @@ def pmc_summary(dirs, out_json):
             lines.append(f"{kind}: HBM read {rb / 1e6:.1f} MB + write {wb / 1e6:.1f} MB per "
                          f"dispatch (calibrated)")
     if "attention" in res:
-        # one attention call = one flash-kernel dispatch (+ one merge dispatch)
+        # one usp_attention_fwd_ws call = one key-half flash dispatch + one merge
         res["traffic_bytes_per_launch"] = sum(
             res[k]["read_bytes"] + res[k]["write_bytes"] for k in ("attention", "merge")
             if k in res)
@@ -212,6 +217,8 @@ def main():
     oblocks = [torch.zeros((B, S, hb[j + 1] - hb[j], D), dtype=torch.bfloat16, device=dev)
                for j in range(P)]
     oshard = torch.empty((B, len0, H, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, B, S, h0, D) // 4,
+                     dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step(e=None):
@@ -221,7 +228,7 @@ def main():
             usp.usp_pack_seq_to_heads(x, bl, rank=0)
         if e is not None:
             e[1].record()
-        usp.usp_attention_fwd(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0])
+        usp.usp_attention_fwd_ws(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0], ws)
         if e is not None:
             e[2].record()
         usp.usp_unpack_heads_to_seq(oblocks, oshard, rank=0)
@@ -248,6 +255,20 @@ def main():
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     elem = 2  # bf16
     share_bytes = 2 * B * len0 * H * D * elem   # one tensor, read + write
+
+    # usp_attention_fwd (no workspace) on the same block, for comparison
+    print("[bench] attention without workspace", file=sys.stderr, flush=True)
+    for _ in range(3):
+        usp.usp_attention_fwd(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0])
+    reps = max(3, args.steps // 10)
+    a, b_ = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        usp.usp_attention_fwd(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0])
+    b_.record()
+    torch.cuda.synchronize()
+    nows_ms = a.elapsed_time(b_) / reps
 
     # plain device copy of 1 GiB: practical HBM reference and counter calibration
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -306,7 +327,11 @@ def main():
                    "step": "pack rank-0 shard of q,k,v -> attention on head group 0 over "
                            "the full sequence -> unpack rank-0 rows"},
         "attention": {"ms": attn_ms, "TFLOP/s": attn_tflops,
-                      "frac_peak": attn_tflops / PEAK_BF16_TFLOPS, "flop": attn_flops},
+                      "frac_peak": attn_tflops / PEAK_BF16_TFLOPS, "flop": attn_flops,
+                      "entry": "usp_attention_fwd_ws"},
+        "attention_no_workspace": {"ms": nows_ms,
+                                   "TFLOP/s": attn_flops / (nows_ms * 1e-3) / 1e12,
+                                   "entry": "usp_attention_fwd"},
         "step_pack_qkv": {"us": pack_ms * 1e3,
                           "GB/s": 3 * share_bytes / (pack_ms * 1e-3) / 1e9},
         "step_unpack_o": {"us": unpack_ms * 1e3,
@@ -316,7 +341,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": stored_traffic(),
-                     "kernel": "usp_attention_fwd: attn_bf16_kernel + attn_merge_kernel"},
+                     "kernel": "usp_attention_fwd_ws: attn_bf16_kernel (key halves) + "
+                               "attn_merge_halves"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
