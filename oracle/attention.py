@@ -14,6 +14,13 @@ scaled dot-product attention, non-causal, per head:
 with sigma = 1/sqrt(D) unless another scale is given (the pages never state
 the scale; 1/sqrt(D) is the standard choice).
 
+Grouped K/V heads (m-star ``ulysses_attention``: q has Hq heads, k and v Hkv,
+both divisible by the SP degree): query head n attends with key/value head
+floor(n / G), G = Hq / Hkv, i.e. each run of G consecutive query heads shares
+one K/V head. The pages do not spell out the mapping; this is the one under
+which contiguous head sharding keeps every rank's query heads with its own
+K/V heads, which the divisibility rule requires.
+
 The oracle evaluates it directly and in two passes (not online): scores,
 row maximum, exponentials, row sum, then the weighted sum divided by the row
 sum, all in float64, over blocks of query rows. ``lse`` is the natural-log
@@ -31,6 +38,13 @@ def _scale(D: int, scale) -> float:
     return 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
 
 
+def kv_head(h: int, hkv: int, head: int) -> int:
+    """K/V head of query ``head`` when ``h`` query heads share ``hkv``."""
+    if hkv < 1 or h % hkv:
+        raise ValueError(f"{h} query heads cannot share {hkv} key/value heads evenly")
+    return head // (h // hkv)
+
+
 def _rows_one_head(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, sigma: float):
     """Two-pass softmax attention of query rows ``Qh [n, D]`` against
     ``Kh, Vh [S, D]`` (all float64). Returns ``(O [n, D], lse [n])``."""
@@ -44,19 +58,22 @@ def _rows_one_head(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, sigma: float)
 
 
 def attention(q, k, v, scale=None, row_block: int = 256, return_lse: bool = False):
-    """Attention over every head of ``q, k, v [B, S, h, D]`` (any float
-    dtype; computed in float64). Returns ``O [B, S, h, D]`` float64 and, if
-    asked, ``lse [B, h, S]``."""
+    """Attention over every head of ``q [B, S, h, D]`` with ``k, v
+    [B, S, hkv, D]`` (``hkv`` divides ``h``; any float dtype, computed in
+    float64). Returns ``O [B, S, h, D]`` float64 and, if asked, ``lse
+    [B, h, S]``."""
     B, S, h, D = q.shape
-    assert k.shape == (B, S, h, D) and v.shape == (B, S, h, D)
+    hkv = k.shape[2]
+    assert k.shape == (B, S, hkv, D) and v.shape == (B, S, hkv, D)
     sigma = _scale(D, scale)
     out = np.empty((B, S, h, D), dtype=np.float64)
     lse = np.empty((B, h, S), dtype=np.float64)
     for b in range(B):
         for hd in range(h):
+            kh = kv_head(h, hkv, hd)
             Qh = np.ascontiguousarray(q[b, :, hd, :], dtype=np.float64)
-            Kh = np.ascontiguousarray(k[b, :, hd, :], dtype=np.float64)
-            Vh = np.ascontiguousarray(v[b, :, hd, :], dtype=np.float64)
+            Kh = np.ascontiguousarray(k[b, :, kh, :], dtype=np.float64)
+            Vh = np.ascontiguousarray(v[b, :, kh, :], dtype=np.float64)
             for r0 in range(0, S, row_block):
                 r1 = min(S, r0 + row_block)
                 o, ls = _rows_one_head(Qh[r0:r1], Kh, Vh, sigma)
@@ -69,10 +86,11 @@ def attention_rows(q, k, v, b: int, head: int, rows, scale=None):
     """Attention for selected query ``rows`` of one ``(b, head)``; returns
     ``(O [len(rows), D], lse [len(rows)])`` in float64."""
     D = q.shape[3]
+    kh = kv_head(q.shape[2], k.shape[2], head)
     rows = np.asarray(rows, dtype=np.int64)
     Qh = np.asarray(q[b, rows, head, :], dtype=np.float64)
-    Kh = np.ascontiguousarray(k[b, :, head, :], dtype=np.float64)
-    Vh = np.ascontiguousarray(v[b, :, head, :], dtype=np.float64)
+    Kh = np.ascontiguousarray(k[b, :, kh, :], dtype=np.float64)
+    Vh = np.ascontiguousarray(v[b, :, kh, :], dtype=np.float64)
     return _rows_one_head(Qh, Kh, Vh, _scale(D, scale))
 
 
@@ -80,16 +98,18 @@ def attention_bruteforce(q, k, v, scale=None):
     """Pure-Python triple loops with ``math.exp`` (tiny inputs only). Same
     definition, no NumPy arithmetic: independent check of ``attention``."""
     B, S, h, D = q.shape
+    G = h // k.shape[2]
     sigma = _scale(D, scale)
     out = np.zeros((B, S, h, D), dtype=np.float64)
     for b in range(B):
         for hd in range(h):
+            kh = hd // G
             for s in range(S):
                 scores = []
                 for t in range(S):
                     dot = 0.0
                     for d in range(D):
-                        dot += float(q[b, s, hd, d]) * float(k[b, t, hd, d])
+                        dot += float(q[b, s, hd, d]) * float(k[b, t, kh, d])
                     scores.append(sigma * dot)
                 mx = max(scores)
                 weights = [math.exp(x - mx) for x in scores]
@@ -97,7 +117,7 @@ def attention_bruteforce(q, k, v, scale=None):
                 for d in range(D):
                     acc = 0.0
                     for t in range(S):
-                        acc += weights[t] * float(v[b, t, hd, d])
+                        acc += weights[t] * float(v[b, t, kh, d])
                     out[b, s, hd, d] = acc / total
     return out
 
@@ -122,11 +142,12 @@ def _pool_init():
 def _pool_task(task):
     b, hd, rows, sigma = task
     q, k, v = _POOL_INPUTS
-    key = (b, hd)
+    kh = kv_head(q.shape[2], k.shape[2], hd)
+    key = (b, kh)
     if key not in _POOL_CACHE:
         _POOL_CACHE.clear()
-        _POOL_CACHE[key] = (np.ascontiguousarray(k[b, :, hd, :], dtype=np.float64),
-                            np.ascontiguousarray(v[b, :, hd, :], dtype=np.float64))
+        _POOL_CACHE[key] = (np.ascontiguousarray(k[b, :, kh, :], dtype=np.float64),
+                            np.ascontiguousarray(v[b, :, kh, :], dtype=np.float64))
     Kh, Vh = _POOL_CACHE[key]
     Qh = np.asarray(q[b, rows, hd, :], dtype=np.float64)
     o, lse = _rows_one_head(Qh, Kh, Vh, sigma)

@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import relayout
-from .attention import attention
+from .attention import attention, kv_head
 from .ranges import head_chunk_ranges
 
 
@@ -22,8 +22,13 @@ def ulysses_world(q, k, v, P: int, scale=None, attn=attention):
 
     ``attn`` maps ``(q_blk, k_blk, v_blk) -> o_blk`` for one block
     ``[B, S, h_j, D]``; it defaults to the oracle attention (a layout-only
-    mock such as ``lambda q, k, v: v`` isolates the relayouts)."""
-    H = q.shape[2]
+    mock such as ``lambda q, k, v: v`` isolates the relayouts). With grouped
+    K/V heads (k, v ``[B, S, Hkv, D]``, Hkv < H) both head counts must be
+    divisible by P, so that block j's query heads share block j's K/V heads
+    (m-star ``ulysses_attention``)."""
+    H, Hkv = q.shape[2], k.shape[2]
+    if Hkv != H and (H % P or Hkv % P or H % Hkv):
+        raise ValueError(f"grouped heads need H ({H}) and Hkv ({Hkv}) divisible by P ({P})")
     qb = relayout.pack_seq_to_heads(q, P)
     kb = relayout.pack_seq_to_heads(k, P)
     vb = relayout.pack_seq_to_heads(v, P)
@@ -35,13 +40,16 @@ def ulysses_world(q, k, v, P: int, scale=None, attn=attention):
 
 
 def attention_chunked(q, k, v, chunks: int, scale=None):
-    """Attention of ``[B, S, h, D]`` run as ``chunks`` head-chunk passes, each
-    pass over heads ``[k_c, k_{c+1})`` of the plan, assembled side by side."""
-    h = q.shape[2]
+    """Attention of ``q [B, S, h, D]`` run as ``chunks`` head-chunk passes,
+    each pass over query heads ``[k_c, k_{c+1})`` of the plan, assembled side
+    by side. With grouped K/V heads a pass need not start on a group
+    boundary: each query head takes its own K/V head."""
+    h, hkv = q.shape[2], k.shape[2]
     hb = head_chunk_ranges(h, chunks)
     out = np.empty(q.shape, dtype=np.float64)
     for c in range(chunks):
-        lo, hi = hb[c], hb[c + 1]
-        out[:, :, lo:hi, :] = attention(q[:, :, lo:hi, :], k[:, :, lo:hi, :],
-                                        v[:, :, lo:hi, :], scale=scale)
+        for n in range(hb[c], hb[c + 1]):
+            j = kv_head(h, hkv, n)
+            out[:, :, n:n + 1, :] = attention(q[:, :, n:n + 1, :], k[:, :, j:j + 1, :],
+                                              v[:, :, j:j + 1, :], scale=scale)
     return out

@@ -159,3 +159,71 @@ def test_chunked_equals_single_shot(h):
         except ValueError:
             continue
         assert np.array_equal(out, ref)
+
+
+# ---- grouped K/V heads (Hkv < Hq): query head n uses K/V head n // (Hq / Hkv)
+
+@pytest.mark.parametrize("B,S,h,hkv,D,seed", [(1, 5, 4, 2, 3, 7), (2, 7, 6, 1, 2, 8),
+                                              (1, 6, 6, 3, 4, 9)])
+def test_grouped_matches_bruteforce(B, S, h, hkv, D, seed):
+    q = _rand((B, S, h, D), seed)
+    k, v = (_rand((B, S, hkv, D), seed + i) for i in (1, 2))
+    assert np.max(np.abs(A.attention(q, k, v, row_block=4) - A.attention_bruteforce(q, k, v))) <= 1e-12
+
+
+@pytest.mark.parametrize("B,S,h,hkv,D", [(2, 90, 8, 2, 16), (1, 257, 6, 3, 64), (1, 40, 5, 1, 8)])
+def test_grouped_matches_torch_sdpa(B, S, h, hkv, D):
+    # torch's enable_gqa repeats each K/V head for consecutive query heads
+    rng = np.random.default_rng(S + h)
+    q = rng.standard_normal((B, S, h, D))
+    k, v = (rng.standard_normal((B, S, hkv, D)) for _ in range(2))
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, enable_gqa=True)
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(A.attention(q, k, v) - ref)) <= 1e-12
+
+
+def test_grouped_is_attention_over_repeated_heads():
+    q = _rand((1, 33, 6, 5), 1)
+    k, v = (_rand((1, 33, 2, 5), i) for i in (2, 3))
+    rep = A.attention(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2))
+    assert np.array_equal(A.attention(q, k, v), rep)
+    # the other plausible convention (head n with K/V head n mod Hkv) differs
+    tiled = A.attention(q, np.tile(k, (1, 1, 3, 1)), np.tile(v, (1, 1, 3, 1)))
+    assert np.max(np.abs(tiled - rep)) > 1e-3
+
+
+def test_grouped_rows_and_parallel_agree_with_full():
+    q = _rand((2, 50, 4, 8), 4)
+    k, v = (_rand((2, 50, 2, 8), i) for i in (5, 6))
+    full, lse = A.attention(q, k, v, return_lse=True)
+    o, ls = A.attention_rows(q, k, v, 1, 3, [0, 7, 49])
+    assert np.max(np.abs(o - full[1, [0, 7, 49], 3])) <= 1e-13
+    par = A.attention_parallel(q, k, v, workers=2)
+    for (b, hd), (rows, o, ls) in par.items():
+        assert np.max(np.abs(o - full[b, rows, hd])) <= 1e-13
+        assert np.max(np.abs(ls - lse[b, hd, rows])) <= 1e-13
+
+
+@pytest.mark.parametrize("B,S,H,Hkv,D,P", [(1, 10, 8, 4, 4, 4), (2, 9, 6, 2, 3, 2), (1, 12, 4, 4, 2, 2)])
+def test_grouped_ulysses_equals_single_device(B, S, H, Hkv, D, P):
+    q = _rand((B, S, H, D), 1)
+    k, v = (_rand((B, S, Hkv, D), i) for i in (2, 3))
+    assert np.array_equal(U.ulysses_world(q, k, v, P), A.attention(q, k, v))
+
+
+def test_grouped_ulysses_needs_divisible_heads():
+    q = _rand((1, 8, 6, 2), 1)
+    k, v = (_rand((1, 8, 2, 2), i) for i in (2, 3))
+    with pytest.raises(ValueError):
+        U.ulysses_world(q, k, v, 4)  # 6 and 2 heads over 4 ranks
+    with pytest.raises(ValueError):
+        A.kv_head(6, 4, 0)
+
+
+def test_grouped_chunks_across_group_boundaries():
+    # 8 query heads over 2 K/V heads in 3 passes (3/3/2): the middle pass
+    # holds query heads 3-5, i.e. both K/V heads
+    q = _rand((1, 21, 8, 4), 1)
+    k, v = (_rand((1, 21, 2, 4), i) for i in (2, 3))
+    assert np.array_equal(U.attention_chunked(q, k, v, 3), A.attention(q, k, v))
