@@ -192,6 +192,27 @@ int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, u
                          size_t ws_bytes, void* stream);
 
 /*
+ * Attention with grouped key/value heads (m-star ulysses_attention: q holds
+ * Hq heads, k and v Hkv, both divisible by the SP degree, so each rank's head
+ * group is [seq, Hq/P, D] against [seq, Hkv/P, D]): as usp_attention_fwd over
+ * query heads [head_lo, head_hi) of q and o [B][S][h][D], with k and v
+ * [B][S][h_kv][D]; query head n attends with key/value head n / (h / h_kv),
+ * i.e. each run of h / h_kv consecutive query heads shares one K/V head.
+ * h_kv = h is usp_attention_fwd. The result of a query head depends only on
+ * its inputs (bitwise, as for usp_attention_fwd), so a caller may run head
+ * chunks over any query-head ranges.
+ *   ws, ws_bytes: NULL for the no-workspace kernels, or a workspace as for
+ *                 usp_attention_fwd_ws (sized by usp_attention_workspace_bytes
+ *                 for head_hi - head_lo heads); both give the same bits.
+ * Errors as usp_attention_fwd_ws, plus: h_kv < 1, h_kv > h or h not a
+ * multiple of h_kv -> USP_EINVAL.
+ */
+int usp_attention_fwd_gqa(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
+                          usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t h_kv,
+                          int32_t D, int32_t head_lo, int32_t head_hi, float scale, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Head-chunked attention (maxdiffusion PR #428, two-phase Ulysses: attention
  * over head sub-groups in turn, mathematically the single-shot result since
  * heads are independent): runs usp_attention_fwd over each range of

@@ -148,3 +148,17 @@ def test_single_hip_runtime_in_process():
     with open(f"/proc/{os.getpid()}/maps") as f:
         paths = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+def _attn_gqa(h=4, hkv=2, lo=0, hi=4, ws=None, nbytes=0, D=64):
+    return L.usp_attention_fwd_gqa(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, h, hkv, D, lo, hi, 0.0,
+                                   None, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hkv=0), -1), (dict(hkv=3), -1), (dict(hkv=5, h=4), -1), (dict(h=6, hkv=4, hi=6), -1),
+    (dict(ws=FAKE + 4, nbytes=1 << 30), -4), (dict(ws=FAKE, nbytes=100), -1), (dict(D=80), -5),
+])
+def test_attention_gqa_rejects(kw, status):
+    assert _attn_gqa(**kw) == status
+    assert usp.usp_last_error()

@@ -198,6 +198,84 @@ def test_workspace_path_fp32_inputs():
     assert _run_ws(q, k, v, F, F).tobytes() == _run(q, k, v, F, F).tobytes()
 
 
+def _run_gqa(q, k, v, dtype, out_dtype, lo=0, hi=None, want_lse=False, use_ws=False):
+    import torch
+    B, S, h, D = q.shape
+    hi = h if hi is None else hi
+    dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
+    o = poisoned((B, S, h, D), out_dtype)
+    lse = torch.full((B, h, S), float("nan"), device=DEV) if want_lse else None
+    ws = None
+    if use_ws:
+        nb = usp.usp_attention_workspace_bytes(usp.USP_BF16 if dtype == BF else usp.USP_F32,
+                                               B, S, hi - lo, D)
+        ws = torch.full((max(nb, 16) // 4,), float("nan"), device=DEV)
+    usp.usp_attention_fwd_gqa(dq, dk, dv, o, head_lo=lo, head_hi=hi, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    out = to_host(o)
+    return (out, lse.cpu().numpy()) if want_lse else out
+
+
+GQA_CASES = [  # B, S, h, hkv, D
+    (1, 300, 4, 2, 128), (2, 257, 6, 1, 64), (1, 1000, 8, 4, 128), (1, 65, 5, 5, 64),
+    (3, 130, 4, 1, 128),
+]
+
+
+@pytest.mark.parametrize("B,S,h,hkv,D", GQA_CASES)
+def test_gqa_parity_and_bitwise_forms(B, S, h, hkv, D):
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=51 + S, hkv=hkv)
+    ref, ref_lse = A.attention(*(widen(x, BF) for x in (q, k, v)), return_lse=True)
+    log(f"attention gqa B={B} S={S} h={h} hkv={hkv} D={D}")
+    out, lse = _run_gqa(q, k, v, BF, F, want_lse=True)
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lse - ref_lse)) <= BF16_LSE_ABS
+    # the workspace form, and query-head ranges cutting through a group
+    assert _run_gqa(q, k, v, BF, F, use_ws=True).tobytes() == out.tobytes()
+    cut = max(1, h // 2 + (1 if h > 2 else 0))
+    parts = np.concatenate([_run_gqa(q, k, v, BF, F, lo=0, hi=cut)[:, :, :cut],
+                            _run_gqa(q, k, v, BF, F, lo=cut, hi=h)[:, :, cut:]], axis=2)
+    if cut < h:
+        assert parts.tobytes() == out.tobytes()
+    if hkv == h:
+        assert _run(q, k, v, BF, F).tobytes() == out.tobytes()
+
+
+def test_gqa_fp32_parity():
+    q, k, v = synth.draw_qkv(1, 200, 6, 64, seed=57, dtype=F, hkv=2)
+    ref = A.attention(q, k, v)
+    log("attention gqa fp32 S=200 h=6 hkv=2")
+    ma, rf = err(_run_gqa(q, k, v, F, F), ref)
+    assert ma <= F32_MAX_ABS and rf <= F32_REL_FROB, (ma, rf)
+
+
+def test_gqa_small_workload_full():
+    """pack q (16 heads) and k, v (4 heads) into 4 head groups -> attention
+    per group -> unpack, against the oracle's Ulysses composition."""
+    import torch
+    from oracle import ulysses as U
+    w = synth.WORKLOADS["gqa_small"]
+    q, k, v = synth.draw_workload(w)
+    B, S, H, Hkv, D, P = w.B, w.S, w.H, w.kv_heads, w.D, w.P
+    hq, hk = R.balanced_ranges(H, P), R.balanced_ranges(Hkv, P)
+    log("workload gqa_small: pack -> attention x4 -> unpack")
+    blocks = []
+    for x, hb_ in ((q, hq), (k, hk), (v, hk)):
+        bl = [poisoned((B, S, hb_[j + 1] - hb_[j], D), BF) for j in range(P)]
+        usp.usp_pack_seq_to_heads(to_dev(x, BF), bl)
+        blocks.append(bl)
+    ob = [poisoned((B, S, hq[j + 1] - hq[j], D), F) for j in range(P)]
+    for j in range(P):
+        usp.usp_attention_fwd_gqa(blocks[0][j], blocks[1][j], blocks[2][j], ob[j])
+    out = poisoned((B, S, H, D), F)
+    usp.usp_unpack_heads_to_seq(ob, out)
+    torch.cuda.synchronize()
+    ref = U.ulysses_world(*(widen(x, BF) for x in (q, k, v)), P)
+    ma, rf = err(to_host(out), ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+
+
 def _ulysses_gpu(w: synth.Workload, q, k, v, out_dtype):
     """pack (world) -> attention per head-group block -> unpack, on the GPU."""
     import torch
@@ -347,3 +425,19 @@ def test_indivisible_long_full_size():
             rows[(b, hd)] = r
     del kf, qf
     _check_sampled(out, q, k, v, BF, w.B, w.S, rows)
+
+
+def test_gqa_video_share_full_size():
+    """Rank 0's share of the grouped video-DiT workload: 5 query heads over
+    one K/V head at S = 32760, sampled rows against the oracle."""
+    import torch
+    w = synth.WORKLOADS["gqa_video_share"]
+    q, k, v = synth.draw_workload(w)
+    hq, hk = R.balanced_ranges(w.H, w.P), R.balanced_ranges(w.kv_heads, w.P)
+    qs = q[:, :, hq[0]:hq[1]]
+    ks, vs = (x[:, :, hk[0]:hk[1]] for x in (k, v))
+    log("workload gqa_video_share: attention on head group 0 (5 query heads, 1 K/V head)")
+    out, lse = _run_gqa(qs, ks, vs, BF, F, want_lse=True, use_ws=True)
+    assert not np.any(np.isnan(out))
+    rows = {(0, hd): _sample_rows(w.S, 200, 60 + hd) for hd in range(hq[1] - hq[0])}
+    _check_sampled(out, qs, ks, vs, BF, w.B, w.S, rows, lse=lse)

@@ -69,10 +69,13 @@ def lib() -> ctypes.CDLL:
         L.usp_attention_fwd_ws.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
                                            _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                            ctypes.c_size_t, _vp]
+        L.usp_attention_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
+                                            _i64, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+                                            ctypes.c_size_t, _vp]
         for name in ("usp_balanced_ranges", "usp_balanced_ranges_device", "usp_head_chunk_ranges",
                      "usp_pack_seq_to_heads", "usp_unpack_heads_to_seq", "usp_attention_fwd",
                      "usp_attention_fwd_chunked", "usp_attention_workspace_bytes",
-                     "usp_attention_fwd_ws"):
+                     "usp_attention_fwd_ws", "usp_attention_fwd_gqa"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -196,6 +199,19 @@ def usp_attention_fwd_ws(q, k, v, o, ws, head_lo: int = 0, head_hi=None, scale: 
     _check(lib().usp_attention_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B,
                                       S, h, D, head_lo, hi, scale, _ptr(lse), _ptr(ws), nbytes,
                                       _stream(q, stream)), "usp_attention_fwd_ws")
+
+
+def usp_attention_fwd_gqa(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
+                          lse=None, ws=None, stream=None) -> None:
+    """Attention over query heads [head_lo, head_hi) of q, o [B,S,h,D] with
+    k, v [B,S,h_kv,D] (query head n uses K/V head n // (h // h_kv));
+    ``ws`` an optional workspace tensor as for usp_attention_fwd_ws."""
+    B, S, h, D = q.shape
+    hi = h if head_hi is None else head_hi
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().usp_attention_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B,
+                                       S, h, k.shape[2], D, head_lo, hi, scale, _ptr(lse), _ptr(ws),
+                                       nbytes, _stream(q, stream)), "usp_attention_fwd_gqa")
 
 
 def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=None,

@@ -3,7 +3,8 @@
 //
 // What it computes (m-star ulysses_attention: the unchanged attention kernel
 // run on the full sequence of the rank's head group): per head n,
-//   O[s] = sum_t softmax_t(scale * <Q[s], K[t]>) V[t].
+//   O[s] = sum_t softmax_t(scale * <Q[s], K[t]>) V[t],
+// with K and V of head n / grp when grp query heads share each K/V head.
 //
 // Work decomposition. A workgroup of NW waves owns BM = NW * QB * 32 query
 // rows of one (batch, head); each wave owns QB blocks of 32 rows (one MFMA
@@ -101,6 +102,7 @@ struct Params {
   void* o;
   float* lse;
   int S, h, head_lo, nheads, n_qtiles;
+  int h_kv, grp;  // heads of k and v; query heads per K/V head (h = grp * h_kv)
   float c;      // scale * log2(e)
   float scale;  // softmax scale (for the natural-log normaliser)
   // key-half walks (PARTS = 2): unit (part, tile) = part * n_tiles + tile
@@ -197,8 +199,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   const int grp = (tid >> 6) / GW, w = (tid >> 6) % GW;  // key group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
   char* const glds = lds + grp * 4 * TB;  // this group's tile buffers
-  const size_t rs = size_t(p.h) * D;                             // token row stride
+  const size_t rs = size_t(p.h) * D;                             // q / o token row stride
   const size_t hb = size_t(b) * S * rs + size_t(head) * D;       // (b, token 0, head)
+  // K/V: query head n reads K/V head n / grp (grouped K/V heads)
+  const size_t rsk = size_t(p.h_kv) * D;
+  const size_t hbk = size_t(b) * S * rsk + size_t(head / p.grp) * D;
   const int qrow0 = qt * kTileRows + sub * BM + w * (QB * 32);
   const float c = p.c;
 
@@ -232,21 +237,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
-    kgo[i] = uint32_t(r * rs + (pos ^ swz_k(r)) * 8);
-    vgo[i] = uint32_t(r * rs + (pos ^ swz_v(r)) * 8);
+    kgo[i] = uint32_t(r * rsk + (pos ^ swz_k(r)) * 8);
+    vgo[i] = uint32_t(r * rsk + (pos ^ swz_v(r)) * 8);
   }
   // A tile that runs past S loads row S - 1 in place of the missing rows:
   // finite data whose scores the mask sets to -inf (weight 0).
   auto issue = [&](const uint16_t* src, const uint32_t (&go)[NI], int lbase, int t0, bool guard,
                    bool is_v) {
-    const uint16_t* base = src + hb + size_t(t0) * rs;
+    const uint16_t* base = src + hbk + size_t(t0) * rsk;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       uint32_t off = go[i];
       if (guard) {
         const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
         const int rc = min(r, S - 1 - t0);
-        off = uint32_t(rc * rs + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8);
+        off = uint32_t(rc * rsk + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8);
       }
       load_lds16(base + off, glds + lbase + (w + GW * i) * 1024);
     }
@@ -656,6 +661,8 @@ int launch(const AttnArgs& a, hipStream_t s) {
   p.h = a.h;
   p.head_lo = a.head_lo;
   p.nheads = a.head_hi - a.head_lo;
+  p.h_kv = a.h_kv;
+  p.grp = a.h / a.h_kv;
   p.n_qtiles = int((a.S + kTileRows - 1) / kTileRows);
   p.c = a.scale * 1.4426950408889634f;
   p.scale = a.scale;

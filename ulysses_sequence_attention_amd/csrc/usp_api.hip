@@ -86,6 +86,8 @@ static int check_relayout(const void* seq, const void* const* blk, usp_dtype dt,
 static int check_attention(const AttnArgs& a) {
   if (!a.q || !a.k || !a.v || !a.o) return fail(USP_EINVAL, "null q, k, v or o");
   if (a.h < 1) return fail(USP_EINVAL, "h must be positive");
+  if (a.h_kv < 1 || a.h_kv > a.h || a.h % a.h_kv)
+    return fail(USP_EINVAL, "%d query heads cannot share %d key/value heads evenly", a.h, a.h_kv);
   if (a.head_lo < 0 || a.head_hi > a.h || a.head_lo >= a.head_hi)
     return fail(USP_EINVAL, "head range [%d, %d) is empty or outside [0, %d)", a.head_lo,
                 a.head_hi, a.h);
@@ -182,7 +184,7 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
 int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
                       usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
                       int32_t head_lo, int32_t head_hi, float scale, float* lse, void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0};
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0, h};
   if (int st = check_attention(a)) return st;
   if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
   if (int st = run_attention(a, (hipStream_t)stream)) return st;
@@ -208,7 +210,7 @@ int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, u
                          usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
                          int32_t head_lo, int32_t head_hi, float scale, float* lse, void* ws,
                          size_t ws_bytes, void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes};
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes, h};
   if (int st = check_attention(a)) return st;
   if (in_dt == USP_BF16) {
     if (!ws) return fail(USP_EINVAL, "workspace is null");
@@ -221,11 +223,24 @@ int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, u
   return ok();
 }
 
+int usp_attention_fwd_gqa(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
+                          usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t h_kv,
+                          int32_t D, int32_t head_lo, int32_t head_hi, float scale, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes, h_kv};
+  if (int st = check_attention(a)) return st;
+  if (in_dt != USP_BF16) a.ws = nullptr;
+  if (a.ws && !aligned16(a.ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
 int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,
                               usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
                               int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
                               void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0};
+  AttnArgs a{q, k, v, o, lse, B, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0, h};
   if (int st = check_attention(a)) return st;
   if (chunks < 1 || chunks > h)
     return fail(USP_EINVAL, "cannot run %d heads in %d non-empty chunks", h, chunks);

@@ -58,6 +58,7 @@ struct AttnArgs {
   usp_dtype in_dt, out_dt;
   void* ws;         // bf16 path: key-half workspace, or nullptr for the key-group kernel
   size_t ws_bytes;
+  int32_t h_kv;     // heads of k and v (h for plain multi-head attention); divides h
 };
 int launch_attention_f32(const AttnArgs& a, hipStream_t s);
 int launch_attention_bf16(const AttnArgs& a, hipStream_t s);

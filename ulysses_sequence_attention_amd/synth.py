@@ -6,7 +6,8 @@ both the CPU oracle's tests and the HIP path's tests and benchmark may use it.
 
 Recipe (same for every workload):
   * NumPy ``default_rng(seed)`` (PCG64), ``standard_normal`` drawn in float32,
-    in the order Q, K, V, each of the full ``[B, S, H, D]`` shape;
+    in the order Q, K, V, Q of the full ``[B, S, H, D]`` shape and K, V of
+    ``[B, S, Hkv, D]`` (Hkv = H unless the workload groups K/V heads);
   * an optional per-tensor float32 multiplier (Q scaled by 1/sqrt(D) for the
     video-DiT share, all three scaled by 0.5 for the long chunked share);
   * for the "peaky" workload, after V is drawn: per batch row b = 0, 1, ...
@@ -36,8 +37,8 @@ class Workload:
 
     B, S, H, D: batch, full sequence length, heads of the seq-sharded tensor,
     head dim. P: sequence-parallel degree (token ranges and head groups).
-    attn_heads: heads of head-group block 0 that the attention runs on.
-    chunks: number of head-chunk passes (1 = single shot).
+    chunks: number of head-chunk passes (1 = single shot). Hkv: heads of K
+    and V (0: same as H); with Hkv < H, H / Hkv query heads share each.
     """
 
     name: str
@@ -52,6 +53,11 @@ class Workload:
     kv_mult: float = 1.0
     peaky_frac: float = 0.0
     chunks: int = 1
+    Hkv: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def esize(self) -> int:
@@ -67,6 +73,12 @@ WORKLOADS = {
                              dtype=BF16, seed=4, q_mult=0.5, kv_mult=0.5, chunks=3),
     "indivisible_long": Workload("indivisible_long", B=2, S=65537, H=12, D=64, P=4,
                                  dtype=BF16, seed=5, peaky_frac=0.01),
+    # grouped K/V heads: the video-DiT share with 8 K/V heads (5 query heads
+    # per K/V head), and a smaller one that the oracle covers in full
+    "gqa_video_share": Workload("gqa_video_share", B=1, S=32760, H=40, D=128, P=8,
+                                dtype=BF16, seed=6, q_mult=1.0 / math.sqrt(128.0), Hkv=8),
+    "gqa_small": Workload("gqa_small", B=2, S=1500, H=16, D=64, P=4, dtype=BF16, seed=7,
+                          Hkv=4),
 }
 
 
@@ -88,16 +100,18 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def draw_qkv(B: int, S: int, H: int, D: int, seed: int, *, dtype: str = BF16,
-             q_mult: float = 1.0, kv_mult: float = 1.0, peaky_frac: float = 0.0):
-    """Draw Q, K, V ``[B, S, H, D]`` per the recipe above.
+             q_mult: float = 1.0, kv_mult: float = 1.0, peaky_frac: float = 0.0,
+             hkv: int = 0):
+    """Draw Q ``[B, S, H, D]`` and K, V ``[B, S, hkv or H, D]`` per the recipe
+    above.
 
     Returns three arrays: float32 for ``dtype == "f32"``, uint16 bfloat16 bits
     for ``dtype == "bf16"``.
     """
     rng = np.random.default_rng(seed)
-    shape = (B, S, H, D)
+    kv_shape = (B, S, hkv or H, D)
     out = []
-    for mult in (q_mult, kv_mult, kv_mult):
+    for shape, mult in (((B, S, H, D), q_mult), (kv_shape, kv_mult), (kv_shape, kv_mult)):
         t = rng.standard_normal(shape, dtype=np.float32)
         if mult != 1.0:
             t *= np.float32(mult)
@@ -115,7 +129,7 @@ def draw_qkv(B: int, S: int, H: int, D: int, seed: int, *, dtype: str = BF16,
 def draw_workload(w: Workload):
     """Q, K, V of a named workload at its full size."""
     return draw_qkv(w.B, w.S, w.H, w.D, w.seed, dtype=w.dtype, q_mult=w.q_mult,
-                    kv_mult=w.kv_mult, peaky_frac=w.peaky_frac)
+                    kv_mult=w.kv_mult, peaky_frac=w.peaky_frac, hkv=w.Hkv)
 
 
 def index_coded(shape, dtype: str) -> np.ndarray:
