@@ -15,7 +15,10 @@ path, every row of it:
   unpack   rank 0's rows of the 8 output blocks back to [1, 4095, 40, 128]
 
 The attention of usp_attention_fwd (no workspace; the same bits) is timed
-on its own as well and reported as "attention_no_workspace".
+on its own as well and reported as "attention_no_workspace", and
+usp_attention_fwd_gqa (with a workspace) on rank 0's share of the grouped
+video-DiT workload (40 query heads over 8 K/V heads: 5 query heads and one
+K/V head per rank) as "attention_gqa".
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
 Also reported: each kernel alone (HIP events around each launch on the
@@ -168,6 +171,7 @@ def main():
                     help="target wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-relayout-bw", action="store_true")
+    ap.add_argument("--skip-gqa", action="store_true", help="skip the grouped-head attention timing")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     args = ap.parse_args()
@@ -270,6 +274,37 @@ def main():
     torch.cuda.synchronize()
     nows_ms = a.elapsed_time(b_) / reps
 
+    # grouped K/V heads: rank 0's share of the grouped video-DiT workload
+    gqa = None
+    if not args.skip_gqa:
+        print("[bench] attention with grouped K/V heads", file=sys.stderr, flush=True)
+        gw = synth.WORKLOADS["gqa_video_share"]
+        gq, gk, gv = synth.draw_workload(gw)
+        ghq = usp.usp_balanced_ranges(gw.H, gw.P)
+        ghk = usp.usp_balanced_ranges(gw.kv_heads, gw.P)
+        q0 = bf(gq[:, :, ghq[0]:ghq[1]])
+        k0, v0 = (bf(x[:, :, ghk[0]:ghk[1]]) for x in (gk, gv))
+        del gq, gk, gv
+        o0 = torch.empty_like(q0)
+        gh, ghkv = ghq[1] - ghq[0], ghk[1] - ghk[0]
+        gws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, gw.B, gw.S, gh, gw.D) // 4,
+                          dtype=torch.float32, device=dev)
+        for _ in range(3):
+            usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws)
+        a, b_ = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws)
+        b_.record()
+        torch.cuda.synchronize()
+        g_ms = a.elapsed_time(b_) / reps
+        g_flops = 4.0 * gw.B * gh * gw.S * gw.S * gw.D
+        gqa = {"workload": "gqa_video_share", "h": gh, "h_kv": ghkv, "S": gw.S, "D": gw.D,
+               "ms": g_ms, "TFLOP/s": g_flops / (g_ms * 1e-3) / 1e12,
+               "entry": "usp_attention_fwd_gqa (workspace)"}
+        del q0, k0, v0, o0, gws
+
     # plain device copy of 1 GiB: practical HBM reference and counter calibration
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -332,6 +367,7 @@ def main():
         "attention_no_workspace": {"ms": nows_ms,
                                    "TFLOP/s": attn_flops / (nows_ms * 1e-3) / 1e12,
                                    "entry": "usp_attention_fwd"},
+        "attention_gqa": gqa,
         "step_pack_qkv": {"us": pack_ms * 1e3,
                           "GB/s": 3 * share_bytes / (pack_ms * 1e-3) / 1e9},
         "step_unpack_o": {"us": unpack_ms * 1e3,
