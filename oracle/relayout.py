@@ -134,3 +134,20 @@ def gather_sequence(shards: list[np.ndarray]) -> np.ndarray:
     """m-star ``gather_sequence``: concatenate per-rank token shards (axis 1)
     in rank order."""
     return np.concatenate(shards, axis=1)
+
+
+def reduce_scatter_rows(partials: list[np.ndarray], rank: int) -> np.ndarray:
+    """h3 ``reduce_scatter_rows``: each of the P ranks holds a partial sum of
+    the full sequence ``[B, S, ...]`` (tensor-parallel partials); rank r
+    receives rows [t_r, t_{r+1}) (balanced ranges of S) of their sum, added
+    in rank order, in float64."""
+    P = len(partials)
+    S = partials[0].shape[1]
+    for x in partials:
+        if x.shape != partials[0].shape:
+            raise ValueError("partials must all cover the same [B, S, ...] rows")
+    tb = balanced_ranges(S, P)
+    acc = np.zeros(partials[0][:, tb[rank]:tb[rank + 1]].shape, dtype=np.float64)
+    for j in range(P):
+        acc += np.asarray(partials[j][:, tb[rank]:tb[rank + 1]], dtype=np.float64)
+    return acc

@@ -100,3 +100,48 @@ def test_scatter_gather_identity(S, P):
     shards = [X.scatter_sequence(x, P, r) for r in range(P)]
     assert [s.shape[1] for s in shards] == [len(t) for t in np.array_split(np.arange(S), P)]
     assert np.array_equal(X.gather_sequence(shards), x)
+
+
+# ---- reduce-scatter of rows (h3 reduce_scatter_rows) ----------------------
+
+@pytest.mark.parametrize("S,P", [(10, 3), (9, 4), (17, 1), (64, 8)])
+def test_reduce_scatter_integer_partials_exact(S, P):
+    rng = np.random.default_rng(S * P)
+    parts = [rng.integers(-1000, 1000, size=(2, S, 5)).astype(np.float64) for _ in range(P)]
+    total = np.zeros((2, S, 5))
+    for x in parts:
+        total = total + x
+    for r in range(P):
+        assert np.array_equal(X.reduce_scatter_rows(parts, r), X.scatter_sequence(total, P, r))
+
+
+def test_reduce_scatter_single_rank_is_passthrough():
+    x = np.random.default_rng(1).standard_normal((1, 7, 3))
+    assert np.array_equal(X.reduce_scatter_rows([x], 0), x)
+
+
+def test_reduce_scatter_matches_loops():
+    rng = np.random.default_rng(3)
+    S, P, W = 11, 3, 4
+    parts = [rng.standard_normal((1, S, W)) for _ in range(P)]
+    bounds = [0, 4, 8, 11]  # 11 rows over 3 ranks: 4, 4, 3
+    for r in range(P):
+        got = X.reduce_scatter_rows(parts, r)
+        for i, s in enumerate(range(bounds[r], bounds[r + 1])):
+            for w in range(W):
+                ref = 0.0
+                for j in range(P):
+                    ref += float(parts[j][0, s, w])
+                assert abs(got[0, i, w] - ref) <= 1e-15
+
+
+def test_reduce_scatter_ranges_tile_the_sum():
+    rng = np.random.default_rng(4)
+    parts = [rng.standard_normal((2, 13, 3)) for _ in range(5)]
+    out = X.gather_sequence([X.reduce_scatter_rows(parts, r) for r in range(5)])
+    assert np.max(np.abs(out - sum(parts))) <= 1e-14
+
+
+def test_reduce_scatter_rejects_mismatched_partials():
+    with pytest.raises(ValueError):
+        X.reduce_scatter_rows([np.zeros((1, 8, 2)), np.zeros((1, 7, 2))], 0)
