@@ -18,7 +18,11 @@ The attention of usp_attention_fwd (no workspace; the same bits) is timed
 on its own as well and reported as "attention_no_workspace", and
 usp_attention_fwd_gqa (with a workspace) on rank 0's share of the grouped
 video-DiT workload (40 query heads over 8 K/V heads: 5 query heads and one
-K/V head per rank) as "attention_gqa".
+K/V head per rank) as "attention_gqa". "rows_world" reports the model-boundary
+row movements at the same share's hidden size ([1, 32760, 5120] bf16 over 8
+ranks, world mode): scatter and gather (read + write of the tensor) and the
+reduce-scatter of 8 partials (8 reads + 1 write), buffers rotated like the
+relayouts'.
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
 Also reported: each kernel alone (HIP events around each launch on the
@@ -172,6 +176,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-relayout-bw", action="store_true")
     ap.add_argument("--skip-gqa", action="store_true", help="skip the grouped-head attention timing")
+    ap.add_argument("--skip-rows", action="store_true", help="skip the row-movement timings")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     args = ap.parse_args()
@@ -320,6 +325,41 @@ def main():
     copy_gbs = 2.0 * COPY_BYTES / (a.elapsed_time(b_) / 4 * 1e-3) / 1e9
     del src, dst
 
+    rows_bw = {}
+    if not args.skip_rows:
+        print("[bench] model-boundary row movements", file=sys.stderr, flush=True)
+        W = H * D
+        tbr = usp.usp_balanced_ranges(S, P)
+        nbytes = B * S * W * elem
+        fulls = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(3)]
+        shard_sets = [[torch.empty((B, tbr[r + 1] - tbr[r], W), dtype=torch.bfloat16, device=dev)
+                       for r in range(P)] for _ in range(3)]
+        partials = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(P)]
+
+        def timed(fn, reps):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            a, b_ = ev(), ev()
+            a.record()
+            for i in range(reps):
+                fn(i)
+            b_.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_) / reps
+
+        for name, fn, moved in (
+                ("scatter", lambda i: usp.usp_scatter_rows(fulls[i % 3], shard_sets[i % 3]), 2 * nbytes),
+                ("gather", lambda i: usp.usp_gather_rows(shard_sets[i % 3], fulls[i % 3]), 2 * nbytes),
+                ("reduce_scatter", lambda i: usp.usp_reduce_scatter_rows(partials, shard_sets[i % 3]),
+                 (P + 1) * nbytes)):
+            ms = timed(fn, args.relayout_reps)
+            gbs = moved / (ms * 1e-3) / 1e9
+            rows_bw[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
+                             "bytes": moved}
+        rows_bw["shape"] = {"B": B, "S": S, "W": W, "P": P, "dtype": "bf16"}
+        del fulls, shard_sets, partials
+
     rel = {}
     if not args.skip_relayout_bw:
         # world pack / unpack of the full [1, 32760, 40, 128] tensor, 3 rotating buffer sets
@@ -373,6 +413,7 @@ def main():
         "step_unpack_o": {"us": unpack_ms * 1e3,
                           "GB/s": share_bytes / (unpack_ms * 1e-3) / 1e9},
         "relayout_world": rel,
+        "rows_world": rows_bw,
         "copy_reference_GB/s": copy_gbs,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,

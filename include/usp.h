@@ -128,6 +128,47 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
                             void* stream);
 
 /*
+ * Ragged token rows at the model boundary, without padding. A tensor
+ * [B][S][W] (W = elements per token row, e.g. H * D) is split along S into
+ * P contiguous balanced ranges [t_r, t_{r+1}) (usp_balanced_ranges(S, P));
+ * shard r is [B][len_r][W], row-major, contiguous. All pointers are device
+ * pointers owned by the caller, 16-byte aligned, and W * element size must
+ * be a multiple of 16. Errors (all three): P outside [1, USP_MAX_PARTS],
+ * S < P, rank >= P, null pointers -> USP_EINVAL; B < 1, W < 1 or sizes
+ * overflowing -> USP_ESHAPE; unknown dtype -> USP_EDTYPE; misalignment ->
+ * USP_EALIGN; a HIP launch error -> USP_EHIP.
+ *
+ * usp_scatter_rows (m-star scatter_sequence: with the full tensor replicated
+ * on every rank, each narrows to its own window, no communication): copies
+ * rows [t_r, t_{r+1}) of `full` into shards[r], for every r (rank < 0; all P
+ * pointers set) or for r = rank only (only shards[rank] need be set).
+ */
+int usp_scatter_rows(const void* full, void* const* shards, usp_dtype dtype, int64_t B, int64_t S,
+                     int64_t W, int32_t P, int32_t rank, void* stream);
+
+/*
+ * usp_gather_rows (m-star gather_sequence, h3-blackwell-runtime
+ * SequenceParallelContext.all_gather_rows: the rank shards back into the
+ * full tensor in rank order, padding never visible): full[b][t_r + i] =
+ * shards[r][b][i] for every r.
+ */
+int usp_gather_rows(const void* const* shards, void* full, usp_dtype dtype, int64_t B, int64_t S,
+                    int64_t W, int32_t P, void* stream);
+
+/*
+ * usp_reduce_scatter_rows (h3-blackwell-runtime
+ * SequenceParallelContext.reduce_scatter_rows: every rank holds a partial
+ * sum of the full sequence, e.g. a tensor-parallel partial, and receives its
+ * own rows of the total): out[r][b][i] = sum_{j=0}^{P-1} partials[j][b][t_r + i]
+ * for every r (rank < 0) or r = rank, the P partials [B][S][W] added in
+ * rank order in fp32 and rounded once to the dtype (round to nearest even
+ * for USP_BF16). Only out[rank] need be set when rank >= 0.
+ */
+int usp_reduce_scatter_rows(const void* const* partials, void* const* out, usp_dtype dtype,
+                            int64_t B, int64_t S, int64_t W, int32_t P, int32_t rank,
+                            void* stream);
+
+/*
  * Non-causal multi-head attention over the full sequence for heads
  * [head_lo, head_hi) of one head-group block (m-star ulysses_attention: the
  * rank runs the unchanged attention kernel on [seq, H/P, D]). For each b,

@@ -162,3 +162,32 @@ def _attn_gqa(h=4, hkv=2, lo=0, hi=4, ws=None, nbytes=0, D=64):
 def test_attention_gqa_rejects(kw, status):
     assert _attn_gqa(**kw) == status
     assert usp.usp_last_error()
+
+
+def _rows(fn, full=FAKE, ptrs=(FAKE, FAKE), dt=1, B=1, S=8, W=64, P=2, rank=-1, parts=None):
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+    if fn == "scatter":
+        return L.usp_scatter_rows(full, arr, dt, B, S, W, P, rank, None)
+    if fn == "gather":
+        return L.usp_gather_rows(arr, full, dt, B, S, W, P, None)
+    parr = (ctypes.c_void_p * max(len(parts or ptrs), 1))(*(parts or ptrs))
+    return L.usp_reduce_scatter_rows(parr, arr, dt, B, S, W, P, rank, None)
+
+
+@pytest.mark.parametrize("fn", ["scatter", "gather", "reduce"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), -1), (dict(P=65, ptrs=(FAKE,) * 65, S=65), -1), (dict(S=1), -1),
+    (dict(B=0), -2), (dict(W=0), -2), (dict(dt=7), -3), (dict(W=4), -4), (dict(dt=0, W=2), -4),
+    (dict(ptrs=(FAKE, FAKE + 8)), -4), (dict(ptrs=(FAKE, None)), -1), (dict(B=2**40, S=2**40), -2),
+])
+def test_rows_reject(fn, kw, status):
+    assert _rows(fn, **kw) == status
+    assert usp.usp_last_error()
+
+
+def test_rows_reject_rank_and_full():
+    assert _rows("scatter", rank=2) == -1
+    assert _rows("reduce", rank=2) == -1
+    assert _rows("scatter", full=None) == -1
+    assert _rows("gather", full=FAKE + 4) == -4
+    assert _rows("reduce", parts=(FAKE, None)) == -1

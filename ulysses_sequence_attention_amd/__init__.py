@@ -7,6 +7,8 @@ One rank's share of the work behind a small C ABI (``include/usp.h``,
     token and head ranges, head-chunk plans;
   * ``usp_pack_seq_to_heads`` / ``usp_unpack_heads_to_seq`` — the
     sequence-sharded <-> head-sharded relayouts around the all-to-alls;
+  * ``usp_scatter_rows`` / ``usp_gather_rows`` / ``usp_reduce_scatter_rows``
+    — ragged token rows at the model boundary;
   * ``usp_attention_fwd`` / ``usp_attention_fwd_chunked`` — flash-style
     non-causal attention over the full sequence for a head group;
     ``usp_attention_fwd_ws`` the same with a caller workspace (faster, same
@@ -21,5 +23,5 @@ from ._binding import (  # noqa: F401
     usp_attention_fwd_chunked, usp_attention_fwd_gqa, usp_attention_fwd_ws,
     usp_attention_workspace_bytes,
     usp_balanced_ranges, usp_balanced_ranges_device,
-    usp_head_chunk_ranges, usp_last_error, usp_pack_seq_to_heads, usp_unpack_heads_to_seq,
-    usp_version)
+    usp_gather_rows, usp_head_chunk_ranges, usp_last_error, usp_pack_seq_to_heads,
+    usp_reduce_scatter_rows, usp_scatter_rows, usp_unpack_heads_to_seq, usp_version)

@@ -72,10 +72,15 @@ def lib() -> ctypes.CDLL:
         L.usp_attention_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
                                             _i64, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                             ctypes.c_size_t, _vp]
+        rows = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _vp]
+        L.usp_scatter_rows.argtypes = rows
+        L.usp_reduce_scatter_rows.argtypes = rows
+        L.usp_gather_rows.argtypes = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _vp]
         for name in ("usp_balanced_ranges", "usp_balanced_ranges_device", "usp_head_chunk_ranges",
                      "usp_pack_seq_to_heads", "usp_unpack_heads_to_seq", "usp_attention_fwd",
                      "usp_attention_fwd_chunked", "usp_attention_workspace_bytes",
-                     "usp_attention_fwd_ws", "usp_attention_fwd_gqa"):
+                     "usp_attention_fwd_ws", "usp_attention_fwd_gqa", "usp_scatter_rows",
+                     "usp_gather_rows", "usp_reduce_scatter_rows"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -169,6 +174,45 @@ def usp_unpack_heads_to_seq(blocks, seq, rank: int = -1, stream=None) -> None:
     B, S, H, D = _relayout_dims(seq, blocks, rank)
     _check(lib().usp_unpack_heads_to_seq(arr, _ptr(seq), _dtype(seq), B, S, H, D, P, rank,
                                          _stream(seq, stream)), "usp_unpack_heads_to_seq")
+
+
+def _row_dims(full_like):
+    B, S = full_like.shape[0], full_like.shape[1]
+    W = 1
+    for n in full_like.shape[2:]:
+        W *= n
+    return B, S, W
+
+
+def _ptr_array(tensors, P):
+    return (_vp * max(P, 1))(*[_ptr(t) if t is not None else None for t in tensors])
+
+
+def usp_scatter_rows(full, shards, rank: int = -1, stream=None) -> None:
+    """full [B,S,...] -> shards[r] [B,len_r,...] for every rank (rank < 0) or
+    for ``rank`` only (the other entries may be None)."""
+    P = len(shards)
+    B, S, W = _row_dims(full)
+    _check(lib().usp_scatter_rows(_ptr(full), _ptr_array(shards, P), _dtype(full), B, S, W, P,
+                                  rank, _stream(full, stream)), "usp_scatter_rows")
+
+
+def usp_gather_rows(shards, full, stream=None) -> None:
+    """shards[r] [B,len_r,...] -> full [B,S,...] in rank order."""
+    P = len(shards)
+    B, S, W = _row_dims(full)
+    _check(lib().usp_gather_rows(_ptr_array(shards, P), _ptr(full), _dtype(full), B, S, W, P,
+                                 _stream(full, stream)), "usp_gather_rows")
+
+
+def usp_reduce_scatter_rows(partials, out, rank: int = -1, stream=None) -> None:
+    """out[r] = rank r's rows of sum(partials) (P partials [B,S,...]), for
+    every rank (rank < 0) or ``rank`` only."""
+    P = len(partials)
+    B, S, W = _row_dims(partials[0])
+    _check(lib().usp_reduce_scatter_rows(_ptr_array(partials, P), _ptr_array(out, P),
+                                         _dtype(partials[0]), B, S, W, P, rank,
+                                         _stream(partials[0], stream)), "usp_reduce_scatter_rows")
 
 
 def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,

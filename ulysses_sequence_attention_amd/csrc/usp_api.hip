@@ -83,6 +83,41 @@ static int check_relayout(const void* seq, const void* const* blk, usp_dtype dt,
   return USP_OK;
 }
 
+// Arguments of the row movements; `ptrs` are the P shard/partial/output
+// pointers, of which only ptrs[rank] must be set when rank >= 0 and the
+// array is written per rank (scatter, reduce-scatter outputs).
+static int check_rows(const void* full, bool need_full, const void* const* ptrs, bool all_ptrs,
+                      const void* const* ptrs2, usp_dtype dt, int64_t B, int64_t S, int64_t W,
+                      int32_t P, int32_t rank) {
+  if (P < 1 || P > USP_MAX_PARTS)
+    return fail(USP_EINVAL, "P must be in [1, %d] (got %d)", USP_MAX_PARTS, P);
+  if (S < P) return fail(USP_EINVAL, "cannot split %lld rows over %d ranks", (long long)S, P);
+  if (rank >= P) return fail(USP_EINVAL, "rank %d out of range for P = %d", rank, P);
+  if (B < 1 || W < 1) return fail(USP_ESHAPE, "B and W must be positive");
+  const int es = esize_of(dt);
+  if (!es) return fail(USP_EDTYPE, "unsupported dtype %d", (int)dt);
+  if ((W * es) % 16)
+    return fail(USP_EALIGN, "W * element size (%lld bytes) must be a multiple of 16",
+                (long long)(W * es));
+  int64_t n;
+  if (!mul_ok(B, S, &n) || !mul_ok(n, W, &n) || !mul_ok(n, es, &n))
+    return fail(USP_ESHAPE, "tensor size overflows");
+  if (need_full) {
+    if (!full) return fail(USP_EINVAL, "null full tensor");
+    if (!aligned16(full)) return fail(USP_EALIGN, "full tensor is not 16-byte aligned");
+  }
+  for (const void* const* arr : {ptrs, ptrs2}) {
+    if (!arr) continue;
+    const bool all = arr == ptrs ? all_ptrs : true;
+    for (int32_t j = 0; j < P; ++j) {
+      if (!all && j != rank) continue;
+      if (!arr[j]) return fail(USP_EINVAL, "pointer %d is null", j);
+      if (!aligned16(arr[j])) return fail(USP_EALIGN, "pointer %d is not 16-byte aligned", j);
+    }
+  }
+  return USP_OK;
+}
+
 static int check_attention(const AttnArgs& a) {
   if (!a.q || !a.k || !a.v || !a.o) return fail(USP_EINVAL, "null q, k, v or o");
   if (a.h < 1) return fail(USP_EINVAL, "h must be positive");
@@ -178,6 +213,36 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
   RelayoutArgs a{nullptr, seq, blk, nullptr, B, S, H, D, P, rank < 0 ? -1 : rank,
                  esize_of(dtype)};
   if (int st = launch_relayout(a, false, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_scatter_rows(const void* full, void* const* shards, usp_dtype dtype, int64_t B, int64_t S,
+                     int64_t W, int32_t P, int32_t rank, void* stream) {
+  if (!shards) return fail(USP_EINVAL, "null shard array");
+  if (int st = check_rows(full, true, shards, rank < 0, nullptr, dtype, B, S, W, P, rank)) return st;
+  RowArgs a{const_cast<void*>(full), nullptr, shards, B, S, W, P, rank < 0 ? -1 : rank,
+            esize_of(dtype)};
+  if (int st = launch_rows(a, RowOp::kScatter, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_gather_rows(const void* const* shards, void* full, usp_dtype dtype, int64_t B, int64_t S,
+                    int64_t W, int32_t P, void* stream) {
+  if (!shards) return fail(USP_EINVAL, "null shard array");
+  if (int st = check_rows(full, true, shards, true, nullptr, dtype, B, S, W, P, -1)) return st;
+  RowArgs a{full, shards, nullptr, B, S, W, P, -1, esize_of(dtype)};
+  if (int st = launch_rows(a, RowOp::kGather, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_reduce_scatter_rows(const void* const* partials, void* const* out, usp_dtype dtype,
+                            int64_t B, int64_t S, int64_t W, int32_t P, int32_t rank,
+                            void* stream) {
+  if (!partials || !out) return fail(USP_EINVAL, "null partial or output array");
+  if (int st = check_rows(nullptr, false, out, rank < 0, partials, dtype, B, S, W, P, rank))
+    return st;
+  RowArgs a{nullptr, partials, out, B, S, W, P, rank < 0 ? -1 : rank, esize_of(dtype)};
+  if (int st = launch_rows(a, RowOp::kReduceScatter, (hipStream_t)stream)) return st;
   return ok();
 }
 

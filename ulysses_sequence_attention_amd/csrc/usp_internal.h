@@ -48,6 +48,17 @@ struct RelayoutArgs {
 };
 int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s);
 
+// Ragged token rows of [B][S][W] tensors over P balanced ranges.
+enum class RowOp { kScatter, kGather, kReduceScatter };
+struct RowArgs {
+  void* full;                 // scatter: source; gather: destination; else unused
+  const void* const* in;      // gather: P shards; reduce-scatter: P partials
+  void* const* out;           // scatter: P shards; reduce-scatter: P outputs
+  int64_t B, S, W;
+  int32_t P, rank, esize;     // rank < 0: every rank's rows
+};
+int launch_rows(const RowArgs& a, RowOp op, hipStream_t s);
+
 struct AttnArgs {
   const void *q, *k, *v;
   void* o;

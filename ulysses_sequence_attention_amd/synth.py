@@ -126,6 +126,13 @@ def draw_qkv(B: int, S: int, H: int, D: int, seed: int, *, dtype: str = BF16,
     return tuple(out)
 
 
+def draw_rows(B: int, S: int, W: int, seed: int, dtype: str = BF16) -> np.ndarray:
+    """One ``[B, S, W]`` tensor of token rows: ``default_rng(seed)``
+    ``standard_normal`` in float32, rounded to bf16 (RNE) for bf16."""
+    t = np.random.default_rng(seed).standard_normal((B, S, W), dtype=np.float32)
+    return f32_to_bf16_bits(t) if dtype == BF16 else t
+
+
 def draw_workload(w: Workload):
     """Q, K, V of a named workload at its full size."""
     return draw_qkv(w.B, w.S, w.H, w.D, w.seed, dtype=w.dtype, q_mult=w.q_mult,
