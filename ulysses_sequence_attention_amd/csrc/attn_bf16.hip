@@ -146,12 +146,20 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane i's bytes land at lds_base + 16 i, with
-// lds_base uniform over the wave. The builtin exists for the device target
+// (buffer_load_dwordx4 ... lds): lane i reads base + voff (a 32-bit byte
+// offset; base wave-uniform, the buffer descriptor built from it in scalar
+// registers) and its bytes land at lds_base + 16 i, lds_base uniform over
+// the wave. Per-lane addressing is a fixed 32-bit offset, so a load costs no
+// per-lane address arithmetic. The builtins exist for the device target
 // only; the host pass sees an empty body.
-__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+  // raw buffer: stride 0, no range clamp in practice (offsets stay inside the
+  // tensor), 32-bit data format in the descriptor's last word
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, 0, 0, 0);
 #endif
 }
 
@@ -196,7 +204,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 
   const int S = p.S;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int grp = (tid >> 6) / GW, w = (tid >> 6) % GW;  // key group, wave within it
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int grp = wid / GW, w = wid % GW;                    // key group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
   char* const glds = lds + grp * 4 * TB;  // this group's tile buffers
   const size_t rs = size_t(p.h) * D;                             // q / o token row stride
@@ -233,12 +242,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   // (rows [q RPI, q RPI + RPI)).
   auto swz_k = [](int r) { return (r / RPL) % CPR; };
   auto swz_v = [](int r) { return 4 * ((r / RPL) % (CPR / 4)); };
-  uint32_t kgo[NI], vgo[NI];  // per-lane element offsets from the tile's first row
+  uint32_t kgo[NI], vgo[NI];  // per-lane byte offsets from the tile's first row
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
-    kgo[i] = uint32_t(r * rsk + (pos ^ swz_k(r)) * 8);
-    vgo[i] = uint32_t(r * rsk + (pos ^ swz_v(r)) * 8);
+    kgo[i] = uint32_t((r * rsk + (pos ^ swz_k(r)) * 8) * 2);
+    vgo[i] = uint32_t((r * rsk + (pos ^ swz_v(r)) * 8) * 2);
   }
   // A tile that runs past S loads row S - 1 in place of the missing rows:
   // finite data whose scores the mask sets to -inf (weight 0).
@@ -251,9 +260,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
       if (guard) {
         const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
         const int rc = min(r, S - 1 - t0);
-        off = uint32_t(rc * rsk + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8);
+        off = uint32_t((rc * rsk + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8) * 2);
       }
-      load_lds16(base + off, glds + lbase + (w + GW * i) * 1024);
+      load_lds16(base, off, glds + lbase + (w + GW * i) * 1024);
     }
   };
   auto load_k = [&](int buf, int t0, bool guard) { issue(p.k, kgo, buf * TB, t0, guard, false); };
