@@ -21,6 +21,10 @@ one K/V head. The pages do not spell out the mapping; this is the one under
 which contiguous head sharding keeps every rank's query heads with its own
 K/V heads, which the divisibility rule requires.
 
+The query rows and the keys may come from different sequence blocks (a
+query block of Sq rows against a key/value block of Sk rows): the formula is
+the same with t running over the Sk keys of the block.
+
 The oracle evaluates it directly and in two passes (not online): scores,
 row maximum, exponentials, row sum, then the weighted sum divided by the row
 sum, all in float64, over blocks of query rows. ``lse`` is the natural-log
@@ -59,12 +63,12 @@ def _rows_one_head(Qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, sigma: float)
 
 def attention(q, k, v, scale=None, row_block: int = 256, return_lse: bool = False):
     """Attention over every head of ``q [B, S, h, D]`` with ``k, v
-    [B, S, hkv, D]`` (``hkv`` divides ``h``; any float dtype, computed in
-    float64). Returns ``O [B, S, h, D]`` float64 and, if asked, ``lse
-    [B, h, S]``."""
+    [B, Sk, hkv, D]`` (``hkv`` divides ``h``; ``Sk`` defaults to the query
+    length but may differ; any float dtype, computed in float64). Returns
+    ``O [B, S, h, D]`` float64 and, if asked, ``lse [B, h, S]``."""
     B, S, h, D = q.shape
-    hkv = k.shape[2]
-    assert k.shape == (B, S, hkv, D) and v.shape == (B, S, hkv, D)
+    Sk, hkv = k.shape[1], k.shape[2]
+    assert k.shape == (B, Sk, hkv, D) and v.shape == (B, Sk, hkv, D) and Sk >= 1
     sigma = _scale(D, scale)
     out = np.empty((B, S, h, D), dtype=np.float64)
     lse = np.empty((B, h, S), dtype=np.float64)
@@ -98,6 +102,7 @@ def attention_bruteforce(q, k, v, scale=None):
     """Pure-Python triple loops with ``math.exp`` (tiny inputs only). Same
     definition, no NumPy arithmetic: independent check of ``attention``."""
     B, S, h, D = q.shape
+    Sk = k.shape[1]
     G = h // k.shape[2]
     sigma = _scale(D, scale)
     out = np.zeros((B, S, h, D), dtype=np.float64)
@@ -106,7 +111,7 @@ def attention_bruteforce(q, k, v, scale=None):
             kh = hd // G
             for s in range(S):
                 scores = []
-                for t in range(S):
+                for t in range(Sk):
                     dot = 0.0
                     for d in range(D):
                         dot += float(q[b, s, hd, d]) * float(k[b, t, kh, d])
@@ -116,7 +121,7 @@ def attention_bruteforce(q, k, v, scale=None):
                 total = sum(weights)
                 for d in range(D):
                     acc = 0.0
-                    for t in range(S):
+                    for t in range(Sk):
                         acc += weights[t] * float(v[b, t, kh, d])
                     out[b, s, hd, d] = acc / total
     return out

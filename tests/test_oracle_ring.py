@@ -1,0 +1,198 @@
+"""Pins for the oracle's block attention (query and key blocks of different
+lengths), the log-sum-exp merge and the Ulysses+Ring composition (CPU only).
+
+The references are independent of the oracle's formulas: PyTorch's CPU
+scaled_dot_product_attention and logsumexp in float64 over the concatenated
+keys, pure-Python brute force, and closed forms of the merge."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import ring as RG
+from oracle import ulysses as U
+from oracle.ranges import balanced_ranges
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _sdpa(q, k, v, scale=None):
+    """torch SDPA (float64, CPU) on [B, S, h, D] arrays; grouped K/V heads
+    are expanded with repeat_interleave, the library's own convention."""
+    G = q.shape[2] // k.shape[2]
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).permute(0, 2, 1, 3).contiguous()
+                  for x in (q, k, v))
+    if G > 1:
+        tk = tk.repeat_interleave(G, dim=1)
+        tv = tv.repeat_interleave(G, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    return out.permute(0, 2, 1, 3).numpy()
+
+
+def _torch_lse(q, k, scale=None):
+    """log sum_t exp(scale <q, k_t>) per (b, head, row) via torch.logsumexp."""
+    D = q.shape[3]
+    G = q.shape[2] // k.shape[2]
+    sigma = 1.0 / math.sqrt(D) if scale is None else scale
+    tq = torch.from_numpy(np.ascontiguousarray(q)).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.ascontiguousarray(k)).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    return torch.logsumexp(sigma * (tq @ tk.transpose(-1, -2)), dim=-1).numpy()
+
+
+# ---- block attention: Sq != Sk --------------------------------------------
+
+@pytest.mark.parametrize("B,Sq,Sk,h,hkv,D,seed", [(1, 3, 7, 2, 2, 3, 0), (2, 6, 1, 2, 1, 4, 1),
+                                                  (1, 1, 9, 3, 3, 2, 2), (1, 8, 5, 4, 2, 2, 3)])
+def test_block_matches_bruteforce(B, Sq, Sk, h, hkv, D, seed):
+    q = _rand((B, Sq, h, D), seed)
+    k = _rand((B, Sk, hkv, D), seed + 10)
+    v = _rand((B, Sk, hkv, D), seed + 20)
+    ref = A.attention_bruteforce(q, k, v)
+    assert np.max(np.abs(A.attention(q, k, v, row_block=2) - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("B,Sq,Sk,h,hkv,D,scale", [(2, 100, 37, 3, 3, 16, None),
+                                                   (1, 50, 301, 4, 2, 64, None),
+                                                   (1, 257, 256, 2, 1, 8, 0.7)])
+def test_block_matches_torch(B, Sq, Sk, h, hkv, D, scale):
+    rng = np.random.default_rng(Sq * 7 + Sk)
+    q = rng.standard_normal((B, Sq, h, D))
+    k = rng.standard_normal((B, Sk, hkv, D))
+    v = rng.standard_normal((B, Sk, hkv, D))
+    out, lse = A.attention(q, k, v, scale=scale, return_lse=True)
+    assert np.max(np.abs(out - _sdpa(q, k, v, scale))) <= 1e-12
+    assert np.max(np.abs(lse - _torch_lse(q, k, scale))) <= 1e-12
+
+
+def test_block_rows_and_parallel_agree_with_full():
+    q = _rand((2, 40, 2, 8), 5)
+    k = _rand((2, 13, 1, 8), 6)
+    v = _rand((2, 13, 1, 8), 7)
+    out, lse = A.attention(q, k, v, return_lse=True)
+    rows = np.array([0, 17, 39])
+    o_r, l_r = A.attention_rows(q, k, v, 1, 1, rows)
+    assert np.array_equal(o_r, out[1, rows, 1]) and np.array_equal(l_r, lse[1, 1, rows])
+    par = A.attention_parallel(q, k, v, workers=2, row_block=16)
+    for (b, hd), (r, o, ls) in par.items():
+        assert np.array_equal(o, out[b, r, hd]) and np.array_equal(ls, lse[b, hd, r])
+
+
+# ---- the merge --------------------------------------------------------------
+
+@pytest.mark.parametrize("Sk_parts", [(5, 7), (1, 1, 1), (30, 1, 12, 4), (64,)])
+def test_ring_over_blocks_is_attention_over_union(Sk_parts):
+    """Merging per-block results equals attention over the concatenated keys
+    (torch SDPA and torch.logsumexp on the concatenation)."""
+    B, Sq, h, D = 2, 11, 3, 8
+    q = _rand((B, Sq, h, D), 1)
+    blocks = [(_rand((B, n, h, D), 100 + i), _rand((B, n, h, D), 200 + i))
+              for i, n in enumerate(Sk_parts)]
+    k = np.concatenate([b[0] for b in blocks], axis=1)
+    v = np.concatenate([b[1] for b in blocks], axis=1)
+    o, lse = RG.ring_attention(q, blocks)
+    assert np.max(np.abs(o - _sdpa(q, k, v))) <= 1e-12
+    assert np.max(np.abs(lse - _torch_lse(q, k))) <= 1e-12
+
+
+def test_merge_with_copy_of_itself():
+    """Two identical blocks: the output is unchanged and lse grows by log 2."""
+    o = _rand((1, 6, 2, 4), 3)
+    lse = _rand((1, 2, 6), 4, 5.0)
+    mo, ml = RG.merge(o, lse, o, lse)
+    assert np.max(np.abs(mo - o)) <= 1e-15 * np.max(np.abs(o)) * 4
+    assert np.max(np.abs(ml - (lse + math.log(2.0)))) <= 1e-14
+
+
+def test_merge_with_empty_block_is_identity():
+    o = _rand((2, 5, 3, 4), 5)
+    lse = _rand((2, 3, 5), 6)
+    ob = _rand((2, 5, 3, 4), 7)
+    empty = np.full_like(lse, -np.inf)
+    mo, ml = RG.merge(o, lse, ob, empty)
+    assert np.array_equal(mo, o) and np.array_equal(ml, lse)
+
+
+def test_merge_of_two_single_keys_is_logistic():
+    """One key per block: the weight of block a is the logistic function of
+    the score difference, and lse is log(e^sa + e^sb)."""
+    rng = np.random.default_rng(8)
+    sa, sb = rng.standard_normal(4) * 3, rng.standard_normal(4) * 3
+    va, vb = rng.standard_normal((4, 5)), rng.standard_normal((4, 5))
+    o_a = va[None, :, None, :]          # attention over one key returns its value
+    o_b = vb[None, :, None, :]
+    mo, ml = RG.merge(o_a, sa[None, None, :], o_b, sb[None, None, :])
+    w = 1.0 / (1.0 + np.exp(sb - sa))
+    assert np.max(np.abs(mo[0, :, 0, :] - (w[:, None] * va + (1 - w[:, None]) * vb))) <= 1e-14
+    assert np.max(np.abs(ml[0, 0] - np.log(np.exp(sa) + np.exp(sb)))) <= 1e-14
+
+
+def test_merge_is_commutative_and_associative():
+    q = _rand((1, 9, 2, 4), 9)
+    blk = [(_rand((1, n, 2, 4), 30 + n), _rand((1, n, 2, 4), 40 + n)) for n in (3, 5, 2)]
+    res = [A.attention(q, k, v, return_lse=True) for k, v in blk]
+    ab = RG.merge(*res[0], *res[1])
+    ba = RG.merge(*res[1], *res[0])
+    assert np.array_equal(ab[0], ba[0]) and np.array_equal(ab[1], ba[1])
+    left = RG.merge(*ab, *res[2])
+    right = RG.merge(*res[0], *RG.merge(*res[1], *res[2]))
+    assert np.max(np.abs(left[0] - right[0])) <= 1e-14
+    assert np.max(np.abs(left[1] - right[1])) <= 1e-14
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5])
+def test_ring_order_is_a_rotation(R):
+    for r in range(R):
+        order = RG.ring_order(r, R)
+        assert order[0] == r and sorted(order) == list(range(R))
+        assert all(order[i + 1] == (order[i] - 1) % R for i in range(R - 1))
+
+
+def test_ring_result_does_not_depend_on_order():
+    q = _rand((1, 7, 2, 4), 11)
+    blocks = [(_rand((1, n, 2, 4), 50 + n), _rand((1, n, 2, 4), 60 + n)) for n in (4, 1, 6)]
+    ref = RG.ring_attention(q, blocks)
+    for order in ([2, 1, 0], [1, 0, 2], [0, 2, 1]):
+        o, lse = RG.ring_attention(q, blocks, order=order)
+        assert np.max(np.abs(o - ref[0])) <= 1e-14 and np.max(np.abs(lse - ref[1])) <= 1e-14
+
+
+# ---- the Ulysses+Ring composition -------------------------------------------
+
+@pytest.mark.parametrize("B,S,H,Hkv,D,Uu,R", [(1, 23, 4, 4, 8, 2, 3), (2, 40, 6, 6, 4, 3, 2),
+                                               (1, 17, 8, 4, 4, 2, 4), (1, 9, 3, 3, 4, 1, 3),
+                                               (1, 31, 6, 2, 8, 2, 1)])
+def test_ulysses_ring_equals_single_device(B, S, H, Hkv, D, Uu, R):
+    q = _rand((B, S, H, D), 70)
+    k = _rand((B, S, Hkv, D), 71)
+    v = _rand((B, S, Hkv, D), 72)
+    out = RG.ulysses_ring_world(q, k, v, Uu, R)
+    assert np.max(np.abs(out - _sdpa(q, k, v))) <= 1e-12
+
+
+def test_one_ring_block_is_plain_ulysses():
+    q, k, v = (_rand((2, 19, 6, 4), 80 + i) for i in range(3))
+    assert np.array_equal(RG.ulysses_ring_world(q, k, v, 3, 1), U.ulysses_world(q, k, v, 3))
+
+
+def test_ring_blocks_follow_balanced_ranges():
+    """Each ring block's query rows see exactly the keys of all blocks: a
+    value tensor that records the token index returns, for a uniform
+    softmax (all keys equal), the mean token index over the whole sequence."""
+    S, R = 29, 4
+    q = _rand((1, S, 2, 4), 90)
+    k = np.zeros((1, S, 2, 4))
+    v = np.broadcast_to(np.arange(S, dtype=np.float64)[None, :, None, None], (1, S, 2, 4)).copy()
+    out = RG.ulysses_ring_world(q, k, v, 2, R)
+    assert np.max(np.abs(out - (S - 1) / 2.0)) <= 1e-12
+    assert balanced_ranges(S, R) == [0, 8, 15, 22, 29]
+
+
+def test_grouped_ring_needs_divisible_heads():
+    q = _rand((1, 8, 6, 4), 1)
+    k = _rand((1, 8, 3, 4), 2)
+    with pytest.raises(ValueError):
+        RG.ulysses_ring_world(q, k, k, 2, 2)
