@@ -254,6 +254,64 @@ int usp_attention_fwd_gqa(const void* q, const void* k, const void* v, void* o, 
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Attention of a query block against one key/value block of another length
+ * (Ulysses+Ring, maxdiffusion PR #428 description: under a ring over a second
+ * sequence axis, rank (r, j) of a U x R grid holds the query rows of ring
+ * block r for head group j and attends them to the K/V block of every ring
+ * member in turn; the per-block results combine by usp_attention_merge).
+ * For each b, query head n in [head_lo, head_hi), query row s < Sq:
+ *   O[b][s][n][:] = sum_{t < Sk} softmax_t(scale * <Q[b][s][n][:], K[b][t][m][:]>)
+ *                   * V[b][t][m][:],   m = n / (h / h_kv)
+ *   q, o: device [B][Sq][h][D];  k, v: device [B][Sk][h_kv][D].
+ *   lse:  NULL, or device fp32 [B][h][Sq] receiving the natural-log
+ *         normaliser over this block's Sk keys (what the merge needs).
+ *   ws, ws_bytes: NULL, or a workspace as for usp_attention_fwd_ws sized by
+ *         usp_attention_workspace_bytes(in_dt, B, Sq, head_hi - head_lo, D)
+ *         (it depends on the query rows only); both give the same bits.
+ * Sq = Sk with the same tensors is usp_attention_fwd_gqa, bit for bit, and a
+ * query row's result depends only on its own row and the key block: running
+ * a query block as any split of its rows gives the same bits.
+ * Other arguments and dtypes as usp_attention_fwd_gqa. Errors as
+ * usp_attention_fwd_gqa, plus: Sk < 1 or k/v sizes overflowing ->
+ * USP_ESHAPE.
+ */
+int usp_attention_fwd_block(const void* q, const void* k, const void* v, void* o,
+                            usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t Sq, int64_t Sk,
+                            int32_t h, int32_t h_kv, int32_t D, int32_t head_lo, int32_t head_hi,
+                            float scale, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Log-sum-exp merge of two attention results of the same query rows over
+ * disjoint key blocks (the fold of one Ulysses+Ring step; softmax over the
+ * union of the two key sets). For heads n in [head_lo, head_hi):
+ *   lse = log(exp(lse_a) + exp(lse_b)),
+ *   O   = exp(lse_a - lse) * O_a + exp(lse_b - lse) * O_b,
+ * computed in fp32 as M = max(lse_a, lse_b), e_x = exp(lse_x - M),
+ * lse = M + log(e_a + e_b), O = (e_a / (e_a + e_b)) O_a + (e_b / (e_a + e_b)) O_b.
+ * A block with lse = -inf counts with weight 0; rows whose two lse are both
+ * -inf get O = 0, lse = -inf.
+ *   o_a, o_b: device fp32 [B][S][h][D] (block outputs, normalised per block).
+ *   lse_a, lse_b: device fp32 [B][h][S] (their normalisers, as usp_attention_*
+ *             write them).
+ *   o:        device [B][S][h][D] of out_dt (USP_F32 or USP_BF16, rounded
+ *             to nearest even); may be exactly o_a or o_b when out_dt is
+ *             USP_F32 (in-place accumulation), else must not overlap them.
+ *   lse:      NULL, or device fp32 [B][h][S]; may be exactly lse_a or lse_b,
+ *             else must not overlap them.
+ * Heads outside the range are neither read nor written. The fold order of
+ * several blocks changes the result only by rounding.
+ * Errors: a NULL pointer other than lse, h < 1 or an empty/outside head
+ *   range, or a bf16 o equal to o_a or o_b -> USP_EINVAL; B < 1, S < 1 or
+ *   sizes too large -> USP_ESHAPE; out_dt unknown -> USP_EDTYPE; D not in
+ *   {32, 64, 128} -> USP_ENOSYS; o_a, o_b or o not 16-byte aligned, or an
+ *   lse pointer not 4-byte aligned -> USP_EALIGN.
+ */
+int usp_attention_merge(const float* o_a, const float* lse_a, const float* o_b,
+                        const float* lse_b, void* o, float* lse, usp_dtype out_dt, int64_t B,
+                        int64_t S, int32_t h, int32_t D, int32_t head_lo, int32_t head_hi,
+                        void* stream);
+
+/*
  * Head-chunked attention (maxdiffusion PR #428, two-phase Ulysses: attention
  * over head sub-groups in turn, mathematically the single-shot result since
  * heads are independent): runs usp_attention_fwd over each range of

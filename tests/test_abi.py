@@ -191,3 +191,37 @@ def test_rows_reject_rank_and_full():
     assert _rows("scatter", full=None) == -1
     assert _rows("gather", full=FAKE + 4) == -4
     assert _rows("reduce", parts=(FAKE, None)) == -1
+
+
+def _attn_block(q=FAKE, k=FAKE, Sq=16, Sk=40, h=4, hkv=2, lo=0, hi=4, ws=None, nbytes=0, D=64,
+                i=1, out=0):
+    return L.usp_attention_fwd_block(q, k, FAKE, FAKE, i, out, 1, Sq, Sk, h, hkv, D, lo, hi, 0.0,
+                                     None, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Sk=0), -2), (dict(Sq=0), -2), (dict(Sk=2**31), -2), (dict(hkv=3), -1),
+    (dict(lo=2, hi=2), -1), (dict(k=None), -1), (dict(k=FAKE + 8), -4), (dict(D=80), -5),
+    (dict(i=0, out=1), -3), (dict(ws=FAKE + 4, nbytes=1 << 30), -4),
+    (dict(ws=FAKE, nbytes=2 * 256 * 67 * 4 * 4 - 1), -1),
+])
+def test_attention_block_rejects(kw, status):
+    assert _attn_block(**kw) == status
+    assert usp.usp_last_error()
+
+
+def _merge(oa=FAKE, la=FAKE, ob=FAKE + 256, lb=FAKE + 512, o=FAKE + 1024, lse=None, out=0, B=1,
+           S=16, h=2, D=64, lo=0, hi=2):
+    return L.usp_attention_merge(oa, la, ob, lb, o, lse, out, B, S, h, D, lo, hi, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(oa=None), -1), (dict(lb=None), -1), (dict(o=None), -1), (dict(h=0, hi=0), -1),
+    (dict(lo=2, hi=2), -1), (dict(hi=3), -1), (dict(B=0), -2), (dict(S=0), -2), (dict(out=4), -3),
+    (dict(D=48), -5), (dict(D=256), -5), (dict(oa=FAKE + 8), -4), (dict(o=FAKE + 4), -4),
+    (dict(la=FAKE + 2), -4), (dict(lse=FAKE + 1), -4), (dict(out=1, o=FAKE), -1),
+    (dict(out=1, o=FAKE + 256), -1), (dict(B=2**40, S=2**20), -2),
+])
+def test_attention_merge_rejects(kw, status):
+    assert _merge(**kw) == status
+    assert usp.usp_last_error()

@@ -13,14 +13,18 @@ One rank's share of the work behind a small C ABI (``include/usp.h``,
     non-causal attention over the full sequence for a head group;
     ``usp_attention_fwd_ws`` the same with a caller workspace (faster, same
     bits), sized by ``usp_attention_workspace_bytes``; ``usp_attention_fwd_gqa``
-    with grouped key/value heads.
+    with grouped key/value heads;
+  * ``usp_attention_fwd_block`` / ``usp_attention_merge`` — a query block
+    against one key/value block with its log-sum-exp, and the merge of such
+    results: one ring step of Ulysses+Ring attention.
 
 The Python functions of the same names only marshal arguments (PyTorch
 tensors for device memory, PyTorch streams); ``synth`` draws seeded inputs.
 """
 from ._binding import (  # noqa: F401
     USP_BF16, USP_F32, USP_MAX_PARTS, UspError, header_symbols, lib, usp_attention_fwd,
-    usp_attention_fwd_chunked, usp_attention_fwd_gqa, usp_attention_fwd_ws,
+    usp_attention_fwd_block, usp_attention_fwd_chunked, usp_attention_fwd_gqa,
+    usp_attention_fwd_ws, usp_attention_merge,
     usp_attention_workspace_bytes,
     usp_balanced_ranges, usp_balanced_ranges_device,
     usp_gather_rows, usp_head_chunk_ranges, usp_last_error, usp_pack_seq_to_heads,

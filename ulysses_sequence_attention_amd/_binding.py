@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.usp_attention_fwd_gqa.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
                                             _i64, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                             ctypes.c_size_t, _vp]
+        L.usp_attention_fwd_block.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                              _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                                              _f32, _vp, _vp, ctypes.c_size_t, _vp]
+        L.usp_attention_merge.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i64,
+                                          _i32, _i32, _i32, _i32, _vp]
         rows = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _vp]
         L.usp_scatter_rows.argtypes = rows
         L.usp_reduce_scatter_rows.argtypes = rows
@@ -79,7 +84,8 @@ def lib() -> ctypes.CDLL:
         for name in ("usp_balanced_ranges", "usp_balanced_ranges_device", "usp_head_chunk_ranges",
                      "usp_pack_seq_to_heads", "usp_unpack_heads_to_seq", "usp_attention_fwd",
                      "usp_attention_fwd_chunked", "usp_attention_workspace_bytes",
-                     "usp_attention_fwd_ws", "usp_attention_fwd_gqa", "usp_scatter_rows",
+                     "usp_attention_fwd_ws", "usp_attention_fwd_gqa", "usp_attention_fwd_block",
+                     "usp_attention_merge", "usp_scatter_rows",
                      "usp_gather_rows", "usp_reduce_scatter_rows"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
@@ -256,6 +262,33 @@ def usp_attention_fwd_gqa(q, k, v, o, head_lo: int = 0, head_hi=None, scale: flo
     _check(lib().usp_attention_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B,
                                        S, h, k.shape[2], D, head_lo, hi, scale, _ptr(lse), _ptr(ws),
                                        nbytes, _stream(q, stream)), "usp_attention_fwd_gqa")
+
+
+def usp_attention_fwd_block(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
+                            lse=None, ws=None, stream=None) -> None:
+    """Attention of the query block q, o [B,Sq,h,D] against the key/value
+    block k, v [B,Sk,h_kv,D] for query heads [head_lo, head_hi); ``lse``
+    fp32 [B,h,Sq] or None; ``ws`` an optional workspace tensor sized for
+    Sq query rows."""
+    B, Sq, h, D = q.shape
+    hi = h if head_hi is None else head_hi
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().usp_attention_fwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o),
+                                         B, Sq, k.shape[1], h, k.shape[2], D, head_lo, hi, scale,
+                                         _ptr(lse), _ptr(ws), nbytes, _stream(q, stream)),
+           "usp_attention_fwd_block")
+
+
+def usp_attention_merge(o_a, lse_a, o_b, lse_b, o, lse=None, head_lo: int = 0, head_hi=None,
+                        stream=None) -> None:
+    """Log-sum-exp merge of (o_a, lse_a) and (o_b, lse_b) — fp32 [B,S,h,D]
+    and [B,h,S] — into o (fp32 or bf16; may be o_a itself when fp32) and
+    lse (may be lse_a itself, or None)."""
+    B, S, h, D = o_a.shape
+    hi = h if head_hi is None else head_hi
+    _check(lib().usp_attention_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o),
+                                     _ptr(lse), _dtype(o), B, S, h, D, head_lo, hi,
+                                     _stream(o_a, stream)), "usp_attention_merge")
 
 
 def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=None,

@@ -5,6 +5,8 @@
 // run on the full sequence of the rank's head group): per head n,
 //   O[s] = sum_t softmax_t(scale * <Q[s], K[t]>) V[t],
 // with K and V of head n / grp when grp query heads share each K/V head.
+// The Sq query rows and the Sk keys may be different sequence blocks (a
+// ring step of Ulysses+Ring attends a query block to another rank's keys).
 //
 // Work decomposition. A workgroup of NW waves owns BM = NW * QB * 32 query
 // rows of one (batch, head); each wave owns QB blocks of 32 rows (one MFMA
@@ -44,11 +46,11 @@
 // cancels between numerator and denominator.
 //
 // Key halves. Every row's key range is split once, at key tile
-// floor(nkt / 2) (nkt = ceil(S / BN)), into two walks whose softmax states
+// floor(nkt / 2) (nkt = ceil(Sk / BN)), into two walks whose softmax states
 // (reference maximum m, row sum l, unnormalised O) are merged at the end
 // with weights 2^(c (m_i - M)), M the larger maximum. The split point
-// depends on S and D only, so a row's bits never depend on the launch (its
-// head range, batch or the device); splitting the work this way gives 2x
+// depends on Sk and D only, so a row's bits never depend on the launch (its
+// head range, batch, the query block it sits in or the device); splitting the work this way gives 2x
 // as many work units, which keeps the last round of a launch from running
 // half empty (a workgroup fills a CU, and at S = 32760, 128 tiles of 256
 // rows per head, a head is exactly one round of 256 half-walks). Two forms:
@@ -79,11 +81,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Key groups per workgroup (1: 8 waves over all keys for 256 rows; 2: two
-// groups of 4 waves over the two key halves for 128 rows).
-#ifndef USP_KEY_GROUPS
-#define USP_KEY_GROUPS 2
-#endif
 // Keys per K/V tile, per head dim.
 #ifndef USP_D128_BN
 #define USP_D128_BN 64
@@ -101,7 +98,8 @@ struct Params {
   const uint16_t* v;
   void* o;
   float* lse;
-  int S, h, head_lo, nheads, n_qtiles;
+  int Sq, Sk;  // query rows (q, o, lse) and keys (k, v) per batch row
+  int h, head_lo, nheads, n_qtiles;
   int h_kv, grp;  // heads of k and v; query heads per K/V head (h = grp * h_kv)
   float c;      // scale * log2(e)
   float scale;  // softmax scale (for the natural-log normaliser)
@@ -202,17 +200,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   const int head = p.head_lo + bh % p.nheads;
   const int b = bh / p.nheads;
 
-  const int S = p.S;
+  const int Sq = p.Sq, Sk = p.Sk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int grp = wid / GW, w = wid % GW;                    // key group, wave within it
   const int l32 = lane & 31, g = lane >> 5;
   char* const glds = lds + grp * 4 * TB;  // this group's tile buffers
   const size_t rs = size_t(p.h) * D;                             // q / o token row stride
-  const size_t hb = size_t(b) * S * rs + size_t(head) * D;       // (b, token 0, head)
+  const size_t hb = size_t(b) * Sq * rs + size_t(head) * D;       // (b, token 0, head)
   // K/V: query head n reads K/V head n / grp (grouped K/V heads)
   const size_t rsk = size_t(p.h_kv) * D;
-  const size_t hbk = size_t(b) * S * rsk + size_t(head / p.grp) * D;
+  const size_t hbk = size_t(b) * Sk * rsk + size_t(head / p.grp) * D;
   const int qrow0 = qt * kTileRows + sub * BM + w * (QB * 32);
   const float c = p.c;
 
@@ -224,7 +222,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < S) x = *reinterpret_cast<const uint4*>(p.q + hb + size_t(row) * rs + s * 16 + g * 8);
+      if (row < Sq) x = *reinterpret_cast<const uint4*>(p.q + hb + size_t(row) * rs + s * 16 + g * 8);
       qf[qb][s] = as_bf16x8(x);
     }
   }
@@ -249,7 +247,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     kgo[i] = uint32_t((r * rsk + (pos ^ swz_k(r)) * 8) * 2);
     vgo[i] = uint32_t((r * rsk + (pos ^ swz_v(r)) * 8) * 2);
   }
-  // A tile that runs past S loads row S - 1 in place of the missing rows:
+  // A tile that runs past Sk loads key row Sk - 1 in place of the missing rows:
   // finite data whose scores the mask sets to -inf (weight 0).
   auto issue = [&](const uint16_t* src, const uint32_t (&go)[NI], int lbase, int t0, bool guard,
                    bool is_v) {
@@ -259,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
       uint32_t off = go[i];
       if (guard) {
         const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
-        const int rc = min(r, S - 1 - t0);
+        const int rc = min(r, Sk - 1 - t0);
         off = uint32_t((rc * rsk + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8) * 2);
       }
       load_lds16(base, off, glds + lbase + (w + GW * i) * 1024);
@@ -405,14 +403,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     }
   };
 
-  // keys at or past S get score -inf (weight 0); t0 is the tile's first key
+  // keys at or past Sk get score -inf (weight 0); t0 is the tile's first key
   auto mask = [&](f32x16 (&sacc)[NKB][QB], int t0) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = t0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-        if (key >= S) {
+        if (key >= Sk) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) sacc[kb][qb][r] = -INFINITY;
         }
@@ -422,14 +420,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   // key tiles [kt_lo, kt_lo + nkt) of this group or part: half 0 is the
   // first nkt_all / 2 tiles (rounded down), half 1 the rest; tile indices
   // below are relative to kt_lo, so only the last tile of half 1 can be
-  // partial. The halves depend on S and BN only.
-  const int nkt_all = (S + BN - 1) / BN;
+  // partial. The halves depend on Sk and BN only.
+  const int nkt_all = (Sk + BN - 1) / BN;
   constexpr bool kHalves = KG == 2 || PARTS == 2;
   const int half = KG == 2 ? grp : part;
   const int kt_lo = kHalves ? half * (nkt_all / 2) : 0;
   const int nkt = !kHalves ? nkt_all : half == 0 ? nkt_all / 2 : nkt_all - nkt_all / 2;
   auto key0 = [&](int kt) { return (kt_lo + kt) * BN; };      // first key of tile kt
-  auto partial = [&](int kt) { return key0(kt) + BN > S; };   // tile runs past S
+  auto partial = [&](int kt) { return key0(kt) + BN > Sk; };  // tile runs past Sk
 
   // ---- the key walk: 2 + (nkt - 1) barriers when nkt > 0 ------------------
   if (nkt > 0) {
@@ -449,7 +447,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   // loads K of tile kt + 2 into the K buffer tile kt used (read in the
   // previous step) and V of tile kt + 1 into the V buffer tile kt - 1 used;
   // the barrier at its end publishes both. With `full` true both tiles lie
-  // wholly before S, so the loads carry no row guards.
+  // wholly before Sk, so the loads carry no row guards.
   auto step = [&](auto full, int kt, f32x16 (&cur)[NKB][QB], f32x16 (&nxt)[NKB][QB]) {
     constexpr bool kFull = decltype(full)::value;
     if (kFull) {
@@ -547,7 +545,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 
   // ---- epilogue: normalise and store ------------------------------------------
   if constexpr (PARTS == 2) {
-    // a key-half walk: the raw state goes to the workspace (rows past S too:
+    // a key-half walk: the raw state goes to the workspace (rows past Sq too:
     // the merge skips them)
     const size_t ur = size_t(part) * p.n_tiles + lid;  // unit
     const int rloc = w * 32 + l32;                      // row within the tile
@@ -570,7 +568,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
     const float lt = sum_halves(lrow[qb]);
     const float inv = 1.0f / lt;
     const int row = qrow0 + qb * 32 + l32;
-    if (row < S) {
+    if (row < Sq) {
       const size_t ob = hb + size_t(row) * rs;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -591,7 +589,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
         }
       }
       if (p.lse && g == 0)
-        p.lse[(size_t(b) * p.h + head) * S + row] = fmaf(mrow[qb], p.scale, logf(lt));
+        p.lse[(size_t(b) * p.h + head) * Sq + row] = fmaf(mrow[qb], p.scale, logf(lt));
     }
   }
 }
@@ -611,7 +609,7 @@ __global__ __launch_bounds__(256) void attn_merge_halves(Params p) {
   const int qt = lid % p.n_qtiles, bh = lid / p.n_qtiles;
   const int head = p.head_lo + bh % p.nheads, b = bh / p.nheads;
   const int row = qt * kTileRows + r;
-  if (row >= p.S) return;
+  if (row >= p.Sq) return;
   const size_t u0 = size_t(lid) * kTileRows + r, u1 = (size_t(p.n_tiles) + lid) * kTileRows + r;
   const float m0 = p.ws_m[u0], m1 = p.ws_m[u1];
   const float mx = fmaxf(m0, m1);
@@ -626,12 +624,12 @@ __global__ __launch_bounds__(256) void attn_merge_halves(Params p) {
   f32x4 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[e] = fmaf(x1[e], a1, x0[e] * a0) * inv;
-  const size_t ob = ((size_t(b) * p.S + row) * p.h + head) * D + ch * 4;
+  const size_t ob = ((size_t(b) * p.Sq + row) * p.h + head) * D + ch * 4;
   if (kOutBf16)
     *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + ob) = __builtin_convertvector(y, bf16x4);
   else
     *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + ob) = y;
-  if (p.lse && ch == 0) p.lse[(size_t(b) * p.h + head) * p.S + row] = fmaf(mx, p.scale, logf(lt));
+  if (p.lse && ch == 0) p.lse[(size_t(b) * p.h + head) * p.Sq + row] = fmaf(mx, p.scale, logf(lt));
 }
 
 // Bytes of the key-half workspace for `tiles` tiles of 256 rows.
@@ -666,7 +664,8 @@ int launch(const AttnArgs& a, hipStream_t s) {
   p.v = static_cast<const uint16_t*>(a.v);
   p.o = a.o;
   p.lse = a.lse;
-  p.S = int(a.S);
+  p.Sq = int(a.S);
+  p.Sk = int(a.Sk);
   p.h = a.h;
   p.head_lo = a.head_lo;
   p.nheads = a.head_hi - a.head_lo;

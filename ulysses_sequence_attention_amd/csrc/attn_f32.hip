@@ -7,7 +7,8 @@
 // (running maximum and sum, rescaled per tile) in fp32. Scores are kept in the
 // base-2 domain (Q is pre-multiplied by scale * log2(e)) so each weight is a
 // single exp2. With grouped K/V heads (h_kv < h, m-star ulysses_attention)
-// query head n reads K/V head n / (h / h_kv).
+// query head n reads K/V head n / (h / h_kv). The query rows (Sq) and the
+// keys (Sk) may be different sequence blocks.
 #include "usp_internal.h"
 
 namespace usp {
@@ -20,7 +21,7 @@ constexpr int kKeys = 16;  // keys per LDS tile
 template <int D>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int S, int h, int h_kv, int head_lo,
+    float* __restrict__ o, float* __restrict__ lse, int S, int Sk, int h, int h_kv, int head_lo,
     int nheads, int n_qtiles, float c_log2, float scale) {
   __shared__ float4 ks[kKeys][D / 4];
   __shared__ float4 vs[kKeys][D / 4];
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
   const size_t rs = size_t(h) * D;  // q / o row stride in elements
   const size_t base = size_t(b) * S * rs + size_t(head) * D;
   const size_t rsk = size_t(h_kv) * D;  // k / v row stride
-  const size_t basek = size_t(b) * S * rsk + size_t(head / (h / h_kv)) * D;
+  const size_t basek = size_t(b) * Sk * rsk + size_t(head / (h / h_kv)) * D;
 
   float qr[D], acc[D];
 #pragma unroll
@@ -50,17 +51,17 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(
   }
   float m = -INFINITY, l = 0.f;
 
-  for (int t0 = 0; t0 < S; t0 += kKeys) {
+  for (int t0 = 0; t0 < Sk; t0 += kKeys) {
     __syncthreads();
     for (int e = threadIdx.x; e < kKeys * (D / 4); e += kRows) {
       const int t = e / (D / 4), dc = e % (D / 4);
-      const bool in = t0 + t < S;
+      const bool in = t0 + t < Sk;
       const size_t off = basek + size_t(t0 + t) * rsk + dc * 4;
       ks[t][dc] = in ? *reinterpret_cast<const float4*>(k + off) : make_float4(0.f, 0.f, 0.f, 0.f);
       vs[t][dc] = in ? *reinterpret_cast<const float4*>(v + off) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
-    const int nk = S - t0 < kKeys ? S - t0 : kKeys;
+    const int nk = Sk - t0 < kKeys ? Sk - t0 : kKeys;
     float sc[kKeys];
     float mt = -INFINITY;
 #pragma unroll
@@ -124,15 +125,15 @@ int launch_attention_f32(const AttnArgs& a, hipStream_t s) {
   float* o = static_cast<float*>(a.o);
   switch (a.D) {
     case 32:
-      attn_f32_kernel<32><<<unsigned(grid), kRows, 0, s>>>(q, k, v, o, a.lse, S, a.h, a.h_kv, a.head_lo,
+      attn_f32_kernel<32><<<unsigned(grid), kRows, 0, s>>>(q, k, v, o, a.lse, S, int(a.Sk), a.h, a.h_kv, a.head_lo,
                                                           nheads, n_qtiles, c, a.scale);
       break;
     case 64:
-      attn_f32_kernel<64><<<unsigned(grid), kRows, 0, s>>>(q, k, v, o, a.lse, S, a.h, a.h_kv, a.head_lo,
+      attn_f32_kernel<64><<<unsigned(grid), kRows, 0, s>>>(q, k, v, o, a.lse, S, int(a.Sk), a.h, a.h_kv, a.head_lo,
                                                           nheads, n_qtiles, c, a.scale);
       break;
     case 128:
-      attn_f32_kernel<128><<<unsigned(grid), kRows, 0, s>>>(q, k, v, o, a.lse, S, a.h, a.h_kv,
+      attn_f32_kernel<128><<<unsigned(grid), kRows, 0, s>>>(q, k, v, o, a.lse, S, int(a.Sk), a.h, a.h_kv,
                                                            a.head_lo, nheads, n_qtiles, c,
                                                            a.scale);
       break;

@@ -126,7 +126,7 @@ static int check_attention(const AttnArgs& a) {
   if (a.head_lo < 0 || a.head_hi > a.h || a.head_lo >= a.head_hi)
     return fail(USP_EINVAL, "head range [%d, %d) is empty or outside [0, %d)", a.head_lo,
                 a.head_hi, a.h);
-  if (a.B < 1 || a.S < 1) return fail(USP_ESHAPE, "B and S must be positive");
+  if (a.B < 1 || a.S < 1 || a.Sk < 1) return fail(USP_ESHAPE, "B, S and Sk must be positive");
   const int es = esize_of(a.in_dt);
   if (!es) return fail(USP_EDTYPE, "unsupported input dtype %d", (int)a.in_dt);
   if (a.out_dt != USP_F32 && a.out_dt != USP_BF16)
@@ -139,10 +139,12 @@ static int check_attention(const AttnArgs& a) {
     return fail(USP_ENOSYS, "fp32 attention supports D in {32, 64, 128} (got %d)", a.D);
   int64_t n;
   if (!mul_ok(a.B, a.S, &n) || !mul_ok(n, a.h, &n) || !mul_ok(n, a.D, &n) ||
-      !mul_ok(n, 4, &n))
+      !mul_ok(n, 4, &n) || !mul_ok(a.B, a.Sk, &n) || !mul_ok(n, a.h_kv, &n) ||
+      !mul_ok(n, a.D, &n) || !mul_ok(n, 4, &n))
     return fail(USP_ESHAPE, "tensor size overflows");
-  if (a.S > (int64_t(1) << 31) - 1024 || a.B * a.h > (int64_t(1) << 31) - 1)
-    return fail(USP_ESHAPE, "S or B * h too large for one launch");
+  if (a.S > (int64_t(1) << 31) - 1024 || a.Sk > (int64_t(1) << 31) - 1024 ||
+      a.B * a.h > (int64_t(1) << 31) - 1)
+    return fail(USP_ESHAPE, "S, Sk or B * h too large for one launch");
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.o))
     return fail(USP_EALIGN, "q, k, v and o must be 16-byte aligned");
   if (a.lse && (reinterpret_cast<uintptr_t>(a.lse) & 3u))
@@ -249,7 +251,7 @@ int usp_reduce_scatter_rows(const void* const* partials, void* const* out, usp_d
 int usp_attention_fwd(const void* q, const void* k, const void* v, void* o, usp_dtype in_dt,
                       usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
                       int32_t head_lo, int32_t head_hi, float scale, float* lse, void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0, h};
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0, h};
   if (int st = check_attention(a)) return st;
   if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
   if (int st = run_attention(a, (hipStream_t)stream)) return st;
@@ -275,7 +277,7 @@ int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, u
                          usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t D,
                          int32_t head_lo, int32_t head_hi, float scale, float* lse, void* ws,
                          size_t ws_bytes, void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes, h};
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes, h};
   if (int st = check_attention(a)) return st;
   if (in_dt == USP_BF16) {
     if (!ws) return fail(USP_EINVAL, "workspace is null");
@@ -292,7 +294,7 @@ int usp_attention_fwd_gqa(const void* q, const void* k, const void* v, void* o, 
                           usp_dtype out_dt, int64_t B, int64_t S, int32_t h, int32_t h_kv,
                           int32_t D, int32_t head_lo, int32_t head_hi, float scale, float* lse,
                           void* ws, size_t ws_bytes, void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes, h_kv};
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes, h_kv};
   if (int st = check_attention(a)) return st;
   if (in_dt != USP_BF16) a.ws = nullptr;
   if (a.ws && !aligned16(a.ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
@@ -301,11 +303,53 @@ int usp_attention_fwd_gqa(const void* q, const void* k, const void* v, void* o, 
   return ok();
 }
 
+int usp_attention_fwd_block(const void* q, const void* k, const void* v, void* o,
+                            usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t Sq, int64_t Sk,
+                            int32_t h, int32_t h_kv, int32_t D, int32_t head_lo, int32_t head_hi,
+                            float scale, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, Sq, Sk, h, D, head_lo, head_hi, scale, in_dt, out_dt, ws, ws_bytes,
+             h_kv};
+  if (int st = check_attention(a)) return st;
+  if (in_dt != USP_BF16) a.ws = nullptr;
+  if (a.ws && !aligned16(a.ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_attention_merge(const float* o_a, const float* lse_a, const float* o_b,
+                        const float* lse_b, void* o, float* lse, usp_dtype out_dt, int64_t B,
+                        int64_t S, int32_t h, int32_t D, int32_t head_lo, int32_t head_hi,
+                        void* stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return fail(USP_EINVAL, "null o_a, lse_a, o_b, lse_b or o");
+  if (h < 1) return fail(USP_EINVAL, "h must be positive");
+  if (head_lo < 0 || head_hi > h || head_lo >= head_hi)
+    return fail(USP_EINVAL, "head range [%d, %d) is empty or outside [0, %d)", head_lo, head_hi, h);
+  if (B < 1 || S < 1) return fail(USP_ESHAPE, "B and S must be positive");
+  if (out_dt != USP_F32 && out_dt != USP_BF16)
+    return fail(USP_EDTYPE, "unsupported output dtype %d", (int)out_dt);
+  if (D != 32 && D != 64 && D != 128)
+    return fail(USP_ENOSYS, "attention merge supports D in {32, 64, 128} (got %d)", D);
+  if (out_dt == USP_BF16 && (o == static_cast<const void*>(o_a) || o == static_cast<const void*>(o_b)))
+    return fail(USP_EINVAL, "a bf16 output cannot overwrite an fp32 input");
+  int64_t n;
+  if (!mul_ok(B, S, &n) || !mul_ok(n, h, &n) || !mul_ok(n, D, &n) || !mul_ok(n, 4, &n))
+    return fail(USP_ESHAPE, "tensor size overflows");
+  if (n / 16 > (int64_t(1) << 31) - 1) return fail(USP_ESHAPE, "tensor too large for one launch");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o))
+    return fail(USP_EALIGN, "o_a, o_b and o must be 16-byte aligned");
+  for (const float* p : {lse_a, lse_b, static_cast<const float*>(lse)})
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(USP_EALIGN, "lse arrays must be 4-byte aligned");
+  MergeArgs a{o_a, lse_a, o_b, lse_b, o, lse, B, S, h, D, head_lo, head_hi, out_dt};
+  if (int st = launch_attention_merge(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
 int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,
                               usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
                               int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
                               void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0, h};
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0, h};
   if (int st = check_attention(a)) return st;
   if (chunks < 1 || chunks > h)
     return fail(USP_EINVAL, "cannot run %d heads in %d non-empty chunks", h, chunks);

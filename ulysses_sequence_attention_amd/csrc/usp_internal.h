@@ -63,7 +63,8 @@ struct AttnArgs {
   const void *q, *k, *v;
   void* o;
   float* lse;
-  int64_t B, S;
+  int64_t B, S;      // S: query rows (q, o, lse) per batch row
+  int64_t Sk;        // keys (k, v) per batch row
   int32_t h, D, head_lo, head_hi;
   float scale;
   usp_dtype in_dt, out_dt;
@@ -72,6 +73,17 @@ struct AttnArgs {
   int32_t h_kv;     // heads of k and v (h for plain multi-head attention); divides h
 };
 int launch_attention_f32(const AttnArgs& a, hipStream_t s);
+// Log-sum-exp merge of two attention results (fp32 o and lse) for heads
+// [head_lo, head_hi) of [B][S][h][D] tensors.
+struct MergeArgs {
+  const float *o_a, *lse_a, *o_b, *lse_b;
+  void* o;
+  float* lse;       // may be nullptr
+  int64_t B, S;
+  int32_t h, D, head_lo, head_hi;
+  usp_dtype out_dt;
+};
+int launch_attention_merge(const MergeArgs& a, hipStream_t s);
 int launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 // Workspace bytes the bf16 key-half path needs for B x heads x S rows.
 size_t attention_bf16_ws_bytes(int64_t B, int64_t S, int32_t heads, int32_t D);
