@@ -1,0 +1,306 @@
+"""GPU parity of the Ulysses+Ring pieces: attention of a query block against a
+key/value block of another length (usp_attention_fwd_block) and the
+log-sum-exp merge (usp_attention_merge), alone and composed into ring passes.
+
+Tolerances: block attention as plain attention (bf16 inputs graded on the fp32
+output, max-abs <= 1e-2 and relative Frobenius <= 5e-3; fp32 <= 1e-5; lse
+within 2^-8 + 1e-5 on the bf16 path). The merge against the float64 merge of
+the same fp32 inputs: per element within 4e-6 of the larger input magnitude
+(about 30 fp32 unit roundoffs: exp, one sum, one division, one product and
+one fused multiply-add, each within a few roundoffs), lse within
+2e-6 (1 + |lse|)."""
+import numpy as np
+import pytest
+
+import ulysses_sequence_attention_amd as usp
+from oracle import attention as A
+from oracle import ranges as R
+from oracle import ring as RG
+from ulysses_sequence_attention_amd import synth
+
+from gpu_util import (BF16_LSE_ABS, BF16_MAX_ABS, BF16_REL_FROB, DEV, F32_MAX_ABS, F32_REL_FROB,
+                      bf16_ulp, err, log, poisoned, to_dev, to_host, widen)
+
+pytestmark = pytest.mark.gpu
+BF, F = synth.BF16, synth.F32
+MERGE_REL, MERGE_LSE = 4e-6, 2e-6
+
+
+def _ws(dtype, B, Sq, heads, D):
+    import torch
+    nb = usp.usp_attention_workspace_bytes(usp.USP_BF16 if dtype == BF else usp.USP_F32,
+                                           B, Sq, heads, D)
+    return torch.full((max(nb, 16) // 4,), float("nan"), device=DEV)
+
+
+def _block(dq, dk, dv, out_dtype, use_ws, lo=0, hi=None):
+    """One usp_attention_fwd_block call on device tensors; returns (o, lse)."""
+    import torch
+    B, Sq, h, D = dq.shape
+    hi = h if hi is None else hi
+    o = poisoned((B, Sq, h, D), out_dtype)
+    lse = torch.full((B, h, Sq), float("nan"), device=DEV)
+    ws = _ws(BF if dq.dtype == torch.bfloat16 else F, B, Sq, hi - lo, D) if use_ws else None
+    usp.usp_attention_fwd_block(dq, dk, dv, o, head_lo=lo, head_hi=hi, lse=lse, ws=ws)
+    return o, lse
+
+
+def _draw_block(B, Sq, Sk, h, hkv, D, seed, dtype=BF):
+    q = synth.draw_qkv(B, Sq, h, D, seed, dtype=dtype)[0]
+    _, k, v = synth.draw_qkv(B, Sk, h, D, seed + 1, dtype=dtype, hkv=hkv)
+    return q, k, v
+
+
+BLOCK_CASES = [  # B, Sq, Sk, h, hkv, D: ragged tails on both sides, one-tile and tiny key blocks
+    (1, 1, 1, 1, 1, 64), (1, 300, 65, 2, 1, 128), (2, 257, 1000, 2, 2, 64),
+    (1, 100, 513, 4, 2, 128), (1, 513, 129, 1, 1, 64), (1, 700, 64, 2, 2, 128),
+    (1, 64, 2, 1, 1, 128), (1, 1, 777, 3, 3, 64), (2, 600, 300, 4, 4, 128),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,h,hkv,D", BLOCK_CASES)
+def test_block_bf16_full_compare(B, Sq, Sk, h, hkv, D):
+    import torch
+    q, k, v = _draw_block(B, Sq, Sk, h, hkv, D, seed=300 + Sq + Sk)
+    ref, ref_lse = A.attention(*(widen(x, BF) for x in (q, k, v)), return_lse=True)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    log(f"block bf16->f32 ws B={B} Sq={Sq} Sk={Sk} h={h} hkv={hkv} D={D}")
+    o_ws, l_ws = _block(dq, dk, dv, F, True)
+    log(f"block bf16->f32 no-ws B={B} Sq={Sq} Sk={Sk} h={h} hkv={hkv} D={D}")
+    o_g, l_g = _block(dq, dk, dv, F, False)
+    log(f"block bf16->bf16 ws B={B} Sq={Sq} Sk={Sk}")
+    o_b, _ = _block(dq, dk, dv, BF, True)
+    torch.cuda.synchronize()
+    out, lse = to_host(o_ws), l_ws.cpu().numpy()
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lse - ref_lse)) <= BF16_LSE_ABS
+    # the two kernels split the keys at the same point: same bits
+    assert np.array_equal(to_host(o_g), out) and np.array_equal(l_g.cpu().numpy(), lse)
+    ob = widen(to_host(o_b), BF)
+    assert np.all(np.abs(ob - ref) <= np.maximum(BF16_MAX_ABS, bf16_ulp(ref)))
+
+
+@pytest.mark.parametrize("B,Sq,Sk,h,hkv,D", [(1, 70, 33, 2, 1, 64), (2, 17, 129, 2, 2, 128),
+                                             (1, 1, 50, 3, 3, 32)])
+def test_block_f32_full_compare(B, Sq, Sk, h, hkv, D):
+    import torch
+    q, k, v = _draw_block(B, Sq, Sk, h, hkv, D, seed=400 + Sq, dtype=F)
+    ref, ref_lse = A.attention(q, k, v, return_lse=True)
+    log(f"block f32 B={B} Sq={Sq} Sk={Sk} h={h} hkv={hkv} D={D}")
+    o, lse = _block(*(to_dev(x, F) for x in (q, k, v)), F, False)
+    torch.cuda.synchronize()
+    ma, rf = err(to_host(o), ref)
+    assert ma <= F32_MAX_ABS and rf <= F32_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-5
+
+
+@pytest.mark.parametrize("use_ws", [True, False])
+@pytest.mark.parametrize("S,h,hkv,D", [(1000, 4, 2, 128), (777, 2, 2, 64)])
+def test_block_with_equal_lengths_is_attention_bitwise(S, h, hkv, D, use_ws):
+    import torch
+    q, k, v = synth.draw_qkv(1, S, h, D, seed=500 + S, hkv=hkv)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    log(f"block vs gqa bitwise S={S} h={h} hkv={hkv} D={D} ws={use_ws}")
+    o, lse = _block(dq, dk, dv, F, use_ws)
+    o2 = poisoned((1, S, h, D), F)
+    lse2 = torch.full((1, h, S), float("nan"), device=DEV)
+    usp.usp_attention_fwd_gqa(dq, dk, dv, o2, lse=lse2, ws=_ws(BF, 1, S, h, D) if use_ws else None)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("use_ws", [True, False])
+def test_query_rows_split_bitwise(use_ws):
+    """A query row's result does not depend on the query block it sits in."""
+    import torch
+    Sq, Sk, h, D = 900, 1300, 2, 128
+    q, k, v = _draw_block(1, Sq, Sk, h, h, D, seed=600)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    log(f"query split bitwise ws={use_ws}")
+    o, lse = _block(dq, dk, dv, F, use_ws)
+    for a, b in ((0, 1), (1, 300), (257, 900), (511, 512)):
+        part, lp = _block(dq[:, a:b].contiguous(), dk, dv, F, use_ws)
+        torch.cuda.synchronize()
+        assert torch.equal(part, o[:, a:b]) and torch.equal(lp, lse[:, :, a:b]), (a, b)
+
+
+def _merge_inputs(B, S, h, D, seed):
+    """fp32 block outputs and normalisers, with lse spread widely, a row where
+    one side is empty (-inf) and a row where both are."""
+    rng = np.random.default_rng(seed)
+    o_a = rng.standard_normal((B, S, h, D)).astype(np.float32)
+    o_b = rng.standard_normal((B, S, h, D)).astype(np.float32) * np.float32(3.0)
+    l_a = (rng.standard_normal((B, h, S)) * 20).astype(np.float32)
+    l_b = (l_a + rng.standard_normal((B, h, S)) * 4).astype(np.float32)
+    l_b[0, 0, 0] = -np.inf
+    l_a[-1, -1, -1] = -np.inf
+    if S > 2:
+        l_a[0, 0, 2] = l_b[0, 0, 2] = -np.inf
+    return o_a, l_a, o_b, l_b
+
+
+@pytest.mark.parametrize("B,S,h,D,lo,hi", [(1, 5, 1, 32, 0, 1), (2, 300, 3, 64, 0, 3),
+                                           (1, 257, 4, 128, 1, 3), (3, 77, 2, 128, 0, 2)])
+def test_merge_parity(B, S, h, D, lo, hi):
+    import torch
+    o_a, l_a, o_b, l_b = _merge_inputs(B, S, h, D, seed=700 + S)
+    ref_o, ref_l = RG.merge(o_a, l_a, o_b, l_b)
+    both_empty = np.isneginf(l_a) & np.isneginf(l_b)          # [B, h, S]
+    ref_o[both_empty.transpose(0, 2, 1)] = 0.0                 # no keys: O = 0 by definition
+    da, db = to_dev(o_a, F), to_dev(o_b, F)
+    dla, dlb = to_dev(l_a, F), to_dev(l_b, F)
+    log(f"merge f32 B={B} S={S} h={h} D={D} heads [{lo},{hi})")
+    o = poisoned((B, S, h, D), F)
+    lse = torch.full((B, h, S), float("nan"), device=DEV)
+    usp.usp_attention_merge(da, dla, db, dlb, o, lse, head_lo=lo, head_hi=hi)
+    log("merge bf16 out")
+    ob = poisoned((B, S, h, D), BF)
+    usp.usp_attention_merge(da, dla, db, dlb, ob, None, head_lo=lo, head_hi=hi)
+    log("merge in place")
+    ia, il = da.clone(), dla.clone()
+    usp.usp_attention_merge(ia, il, db, dlb, ia, il, head_lo=lo, head_hi=hi)
+    torch.cuda.synchronize()
+    out, lout = to_host(o), lse.cpu().numpy()
+    sel = slice(lo, hi)
+    mag = np.maximum(np.abs(o_a), np.abs(o_b)).astype(np.float64)[:, :, sel]
+    assert np.all(np.abs(out[:, :, sel] - ref_o[:, :, sel]) <= MERGE_REL * mag + 1e-30)
+    lr = ref_l[:, sel]
+    fin = np.isfinite(lr)
+    assert np.all(np.isneginf(lout[:, sel][~fin]))
+    assert np.all(np.abs(lout[:, sel][fin] - lr[fin]) <= MERGE_LSE * (1 + np.abs(lr[fin])))
+    # heads outside the range untouched
+    assert np.all(np.isnan(out[:, :, :lo])) and np.all(np.isnan(out[:, :, hi:]))
+    assert np.all(np.isnan(lout[:, :lo])) and np.all(np.isnan(lout[:, hi:]))
+    # bf16 output: the fp32 result rounded once (within one bf16 ulp of the reference)
+    bo = widen(to_host(ob), BF)[:, :, sel]
+    assert np.all(np.abs(bo - ref_o[:, :, sel]) <= bf16_ulp(ref_o[:, :, sel]) + MERGE_REL * mag)
+    # in place: the same bits as out of place
+    assert np.array_equal(to_host(ia)[:, :, sel], out[:, :, sel])
+    assert np.array_equal(il.cpu().numpy()[:, sel], lout[:, sel])
+
+
+def _ring_pass(dq, kv_blocks, order, out_dtype, use_ws=True):
+    """One rank's ring pass on the GPU: block attention over each K/V block
+    in ``order`` folded by usp_attention_merge; the last fold writes
+    ``out_dtype``. Returns (o, lse)."""
+    import torch
+    B, Sq, h, D = dq.shape
+    o_acc, l_acc = _block(dq, *kv_blocks[order[0]], F, use_ws)
+    if len(order) == 1:
+        if out_dtype == F:
+            return o_acc, l_acc
+        return _block(dq, *kv_blocks[order[0]], BF, use_ws)
+    for n, i in enumerate(order[1:]):
+        o_i, l_i = _block(dq, *kv_blocks[i], F, use_ws)
+        last = n == len(order) - 2
+        if last and out_dtype == BF:
+            o = poisoned((B, Sq, h, D), BF)
+            usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o, l_acc)
+            o_acc = o
+        else:
+            usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o_acc, l_acc)
+    return o_acc, l_acc
+
+
+def _ring_world(w, q, k, v, out_dtype):
+    """The U x R composition on one GPU: for each ring block r, pack it into
+    U head groups, run every rank's ring pass, unpack. Returns the full
+    [B, S, H, D] output on the host."""
+    import torch
+    B, S, H, D, U, Rr = w.B, w.S, w.H, w.D, w.P, w.ring
+    Hkv = w.kv_heads
+    T = R.balanced_ranges(S, Rr)
+    c = R.balanced_ranges(H, U)
+    ck = R.balanced_ranges(Hkv, U)
+    dq, dk, dv = (to_dev(x, w.dtype) for x in (q, k, v))
+
+    def pack(x, r, heads, cb):
+        seq = x[:, T[r]:T[r + 1]].contiguous()
+        blks = [torch.empty((B, T[r + 1] - T[r], cb[j + 1] - cb[j], D), dtype=x.dtype, device=DEV)
+                for j in range(U)]
+        usp.usp_pack_seq_to_heads(seq, blks)
+        return blks
+
+    qb = [pack(dq, r, H, c) for r in range(Rr)]
+    kb = [pack(dk, r, Hkv, ck) for r in range(Rr)]
+    vb = [pack(dv, r, Hkv, ck) for r in range(Rr)]
+    out = torch.empty((B, S, H, D), dtype=torch.float32 if out_dtype == F else torch.bfloat16,
+                      device=DEV)
+    for r in range(Rr):
+        ob = []
+        for j in range(U):
+            log(f"ring pass {w.name} ring block {r} head group {j}")
+            o, _ = _ring_pass(qb[r][j], [(kb[i][j], vb[i][j]) for i in range(Rr)],
+                              RG.ring_order(r, Rr), out_dtype)
+            ob.append(o)
+        seq = torch.empty((B, T[r + 1] - T[r], H, D), dtype=out.dtype, device=DEV)
+        usp.usp_unpack_heads_to_seq(ob, seq)
+        out[:, T[r]:T[r + 1]] = seq
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def test_ring_small_world_full_compare():
+    w = synth.WORKLOADS["ring_small"]
+    q, k, v = synth.draw_workload(w)
+    ref = A.attention(*(widen(x, BF) for x in (q, k, v)))
+    out = _ring_world(w, q, k, v, F)
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    ob = widen(_ring_world(w, q, k, v, BF), BF)
+    assert np.all(np.abs(ob - ref) <= np.maximum(BF16_MAX_ABS, bf16_ulp(ref)))
+
+
+def test_one_ring_block_is_the_block_call():
+    import torch
+    q, k, v = _draw_block(1, 500, 500, 2, 2, 128, seed=800)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    log("ring pass of one block")
+    o, lse = _ring_pass(dq, [(dk, dv)], [0], F)
+    o2, l2 = _block(dq, dk, dv, F, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_video_dit_ring_share_sampled():
+    """One rank's share of the 4 x 2 video-DiT grid at its real size: ring
+    block 1, head group 2 (10 heads, 16380 query rows, two K/V blocks of
+    16380), the launches the benchmark times; 48 sampled rows per head
+    against the oracle over the whole sequence's keys."""
+    import torch
+    w = synth.WORKLOADS["video_dit_ring"]
+    q, k, v = synth.draw_workload(w)
+    T = R.balanced_ranges(w.S, w.ring)
+    c = R.balanced_ranges(w.H, w.P)
+    r, j = 1, 2
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    h = c[j + 1] - c[j]
+
+    def blk(x, i):
+        seq = x[:, T[i]:T[i + 1]]
+        bl = [torch.empty((1, T[i + 1] - T[i], c[u + 1] - c[u], w.D), dtype=x.dtype, device=DEV)
+              for u in range(w.P)]
+        usp.usp_pack_seq_to_heads(seq, bl)
+        return bl[j]
+
+    qj = blk(dq, r)
+    kv = [(blk(dk, i), blk(dv, i)) for i in range(w.ring)]
+    del dq, dk, dv
+    log("video_dit_ring share: ring pass")
+    o, lse = _ring_pass(qj, kv, RG.ring_order(r, w.ring), F)
+    torch.cuda.synchronize()
+    out, lout = to_host(o), lse.cpu().numpy()
+    rng = np.random.default_rng(9)
+    Sq = T[r + 1] - T[r]
+    rows = np.unique(np.concatenate([[0, Sq - 1, 255, 256], rng.choice(Sq, 44, replace=False)]))
+    qf, kf, vf = (widen(x, BF) for x in (q, k, v))
+    worst = 0.0
+    for n in range(h):
+        ref_o, ref_l = A.attention_rows(qf[:, T[r]:T[r + 1]], kf, vf, 0, c[j] + n, rows)
+        ma, _ = err(out[0, rows, n], ref_o)
+        worst = max(worst, ma)
+        assert np.max(np.abs(lout[0, n, rows] - ref_l)) <= BF16_LSE_ABS
+        # the flat softmax of this workload keeps |O| tiny: grade relative too
+        assert np.linalg.norm(out[0, rows, n] - ref_o) <= BF16_REL_FROB * np.linalg.norm(ref_o)
+    assert worst <= BF16_MAX_ABS

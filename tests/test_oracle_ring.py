@@ -196,3 +196,14 @@ def test_grouped_ring_needs_divisible_heads():
     k = _rand((1, 8, 3, 4), 2)
     with pytest.raises(ValueError):
         RG.ulysses_ring_world(q, k, k, 2, 2)
+
+
+def test_ring_small_workload_composition():
+    """The small Ulysses+Ring workload (ragged ring blocks 501/500/500,
+    grouped K/V heads) through the composition equals plain attention."""
+    from ulysses_sequence_attention_amd import synth
+    w = synth.WORKLOADS["ring_small"]
+    q, k, v = (synth.bf16_bits_to_f32(x).astype(np.float64) for x in synth.draw_workload(w))
+    assert balanced_ranges(w.S, w.ring) == [0, 501, 1001, 1501]
+    out = RG.ulysses_ring_world(q, k, v, w.P, w.ring)
+    assert np.max(np.abs(out - A.attention(q, k, v))) <= 1e-12

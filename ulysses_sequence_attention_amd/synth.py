@@ -39,6 +39,8 @@ class Workload:
     head dim. P: sequence-parallel degree (token ranges and head groups).
     chunks: number of head-chunk passes (1 = single shot). Hkv: heads of K
     and V (0: same as H); with Hkv < H, H / Hkv query heads share each.
+    ring: ring blocks of the sequence for Ulysses+Ring (1: plain Ulysses);
+    with ring = R the P ranks of each ring group split one ring block.
     """
 
     name: str
@@ -54,6 +56,7 @@ class Workload:
     peaky_frac: float = 0.0
     chunks: int = 1
     Hkv: int = 0
+    ring: int = 1
 
     @property
     def kv_heads(self) -> int:
@@ -79,6 +82,14 @@ WORKLOADS = {
                                 dtype=BF16, seed=6, q_mult=1.0 / math.sqrt(128.0), Hkv=8),
     "gqa_small": Workload("gqa_small", B=2, S=1500, H=16, D=64, P=4, dtype=BF16, seed=7,
                           Hkv=4),
+    # Ulysses+Ring: the video-DiT sequence on a 4 (Ulysses) x 2 (ring) grid
+    # of 8 ranks, each rank holding 10 heads of a 16380-token ring block and
+    # attending them to both ring blocks; and a small ragged one (ring
+    # blocks 501/500/500, grouped K/V heads) that the oracle covers in full
+    "video_dit_ring": Workload("video_dit_ring", B=1, S=32760, H=40, D=128, P=4, dtype=BF16,
+                               seed=8, q_mult=1.0 / math.sqrt(128.0), ring=2),
+    "ring_small": Workload("ring_small", B=2, S=1501, H=12, D=64, P=2, dtype=BF16, seed=9,
+                           Hkv=4, ring=3),
 }
 
 
