@@ -22,7 +22,12 @@ K/V head per rank) as "attention_gqa". "rows_world" reports the model-boundary
 row movements at the same share's hidden size ([1, 32760, 5120] bf16 over 8
 ranks, world mode): scatter and gather (read + write of the tensor) and the
 reduce-scatter of 8 partials (8 reads + 1 write), buffers rotated like the
-relayouts'.
+relayouts'. "ring" reports one rank's ring pass of Ulysses+Ring on the
+video-DiT sequence over a 4 (Ulysses) x 2 (ring) grid: ring block 0, head
+group 0 (10 heads, 16380 query rows) attends to its own K/V block and then to
+ring block 1's (usp_attention_fwd_block, fp32 outputs and lse), and
+usp_attention_merge folds the two into the bf16 output; its flops are
+4 * Sq * S * D * h = 2.7474e12.
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
 Also reported: each kernel alone (HIP events around each launch on the
@@ -177,6 +182,7 @@ def main():
     ap.add_argument("--skip-relayout-bw", action="store_true")
     ap.add_argument("--skip-gqa", action="store_true", help="skip the grouped-head attention timing")
     ap.add_argument("--skip-rows", action="store_true", help="skip the row-movement timings")
+    ap.add_argument("--skip-ring", action="store_true", help="skip the Ulysses+Ring pass timing")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     args = ap.parse_args()
@@ -310,6 +316,68 @@ def main():
                "entry": "usp_attention_fwd_gqa (workspace)"}
         del q0, k0, v0, o0, gws
 
+    # one rank's Ulysses+Ring pass: two key blocks, then the merge
+    ring = None
+    if not args.skip_ring:
+        print("[bench] Ulysses+Ring pass", file=sys.stderr, flush=True)
+        rw = synth.WORKLOADS["video_dit_ring"]
+        rq, rk, rv = (bf(x) for x in synth.draw_workload(rw))
+        rT = usp.usp_balanced_ranges(rw.S, rw.ring)
+        rc = usp.usp_balanced_ranges(rw.H, rw.P)
+        rh = rc[1] - rc[0]
+
+        def head_group0(x, i):
+            bl = [torch.empty((rw.B, rT[i + 1] - rT[i], rc[j + 1] - rc[j], rw.D),
+                              dtype=torch.bfloat16, device=dev) for j in range(rw.P)]
+            usp.usp_pack_seq_to_heads(x[:, rT[i]:rT[i + 1]], bl)
+            return bl[0]
+
+        qr = head_group0(rq, 0)
+        kvr = [(head_group0(rk, i), head_group0(rv, i)) for i in range(rw.ring)]
+        del rq, rk, rv
+        Sq = rT[1] - rT[0]
+        rws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, rw.B, Sq, rh, rw.D) // 4,
+                          dtype=torch.float32, device=dev)
+        o_acc = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.float32, device=dev)
+        o_blk = torch.empty_like(o_acc)
+        l_acc = torch.empty((rw.B, rh, Sq), dtype=torch.float32, device=dev)
+        l_blk = torch.empty_like(l_acc)
+        o_out = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.bfloat16, device=dev)
+        order = [0] + [(0 - i) % rw.ring for i in range(1, rw.ring)]
+
+        def ring_pass(e=None):
+            if e is not None:
+                e[0].record()
+            usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws)
+            for n, i in enumerate(order[1:]):
+                usp.usp_attention_fwd_block(qr, *kvr[i], o_blk, lse=l_blk, ws=rws)
+                if e is not None:
+                    e[1].record()
+                last = n == len(order) - 2
+                usp.usp_attention_merge(o_acc, l_acc, o_blk, l_blk, o_out if last else o_acc,
+                                        None if last else l_acc)
+            if e is not None:
+                e[2].record()
+
+        for _ in range(3):
+            ring_pass()
+        revs = [[ev() for _ in range(3)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ring_pass(revs[i])
+        torch.cuda.synchronize()
+        r_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in revs]))
+        m_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in revs]))
+        r_flops = 4.0 * rw.B * rh * Sq * rw.S * rw.D
+        m_bytes = rw.B * Sq * rh * rw.D * (4 + 4 + 2) + 2 * rw.B * rh * Sq * 4
+        ring = {"workload": "video_dit_ring", "grid": f"{rw.P} ulysses x {rw.ring} ring",
+                "rank": "ring block 0, head group 0", "h": rh, "Sq": Sq, "S": rw.S, "D": rw.D,
+                "ms": r_ms, "TFLOP/s": r_flops / (r_ms * 1e-3) / 1e12,
+                "frac_peak": r_flops / (r_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": r_flops,
+                "merge_us": m_ms * 1e3, "merge_GB/s": m_bytes / (m_ms * 1e-3) / 1e9,
+                "entry": "usp_attention_fwd_block (workspace) x 2 + usp_attention_merge"}
+        del qr, kvr, rws, o_acc, o_blk, l_acc, l_blk, o_out
+
     # plain device copy of 1 GiB: practical HBM reference and counter calibration
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -408,6 +476,7 @@ def main():
                                    "TFLOP/s": attn_flops / (nows_ms * 1e-3) / 1e12,
                                    "entry": "usp_attention_fwd"},
         "attention_gqa": gqa,
+        "ring": ring,
         "step_pack_qkv": {"us": pack_ms * 1e3,
                           "GB/s": 3 * share_bytes / (pack_ms * 1e-3) / 1e9},
         "step_unpack_o": {"us": unpack_ms * 1e3,

@@ -12,7 +12,9 @@ path computes, written from the pages' description of the method:
                    pure-Python brute force for tiny inputs, and a process-pool
                    driver over host cores;
   * ``ulysses``  — the composition pack -> per-head-group attention -> unpack,
-                   and head-chunked passes.
+                   and head-chunked passes;
+  * ``ring``     — the log-sum-exp merge of attention over key blocks and the
+                   Ulysses+Ring composition on a U x R grid.
 
 Only the test suite, the smoke check in ``__graft_entry__`` and the CPU
 baseline leg of ``bench.py`` may import this package. The product path (the
@@ -24,4 +26,4 @@ Every function is pinned by tests that do not re-use its own formula: printed
 splits, library routines (``numpy.array_split``, PyTorch's CPU
 ``scaled_dot_product_attention``), closed forms, invariants and brute force.
 """
-from . import attention, ranges, relayout, ulysses  # noqa: F401
+from . import attention, ranges, relayout, ring, ulysses  # noqa: F401
