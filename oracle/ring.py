@@ -38,18 +38,24 @@ def merge(o_a, lse_a, o_b, lse_b):
 
     ``o_* [B, S, h, D]``, ``lse_* [B, h, S]``; returns ``(O, lse)`` of the
     union of the two blocks' keys. ``lse = -inf`` (a block with no keys)
-    gives that block weight 0."""
+    gives that block weight 0; a row with no keys in either block has no
+    softmax at all and is given O = 0, lse = -inf."""
     o_a = np.asarray(o_a, dtype=np.float64)
     o_b = np.asarray(o_b, dtype=np.float64)
     lse_a = np.asarray(lse_a, dtype=np.float64)
     lse_b = np.asarray(lse_b, dtype=np.float64)
     m = np.maximum(lse_a, lse_b)
-    wa = np.exp(lse_a - m)
-    wb = np.exp(lse_b - m)
-    lse = m + np.log(wa + wb)
+    none = np.isneginf(m)                     # no keys in either block
+    ms = np.where(none, 0.0, m)
+    wa = np.exp(lse_a - ms)                   # exp(-inf) = 0 for an empty block
+    wb = np.exp(lse_b - ms)
+    lse = np.where(none, -np.inf, ms + np.log(np.where(none, 1.0, wa + wb)))
+    ls = np.where(none, 0.0, lse)
+    fa = np.where(none, 0.0, np.exp(lse_a - ls))
+    fb = np.where(none, 0.0, np.exp(lse_b - ls))
     # weights per (b, head, row), laid out for o's [B, S, h, D]
-    fa = np.exp(lse_a - lse).transpose(0, 2, 1)[..., None]
-    fb = np.exp(lse_b - lse).transpose(0, 2, 1)[..., None]
+    fa = fa.transpose(0, 2, 1)[..., None]
+    fb = fb.transpose(0, 2, 1)[..., None]
     return fa * o_a + fb * o_b, lse
 
 

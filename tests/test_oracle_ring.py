@@ -116,6 +116,19 @@ def test_merge_with_empty_block_is_identity():
     assert np.array_equal(mo, o) and np.array_equal(ml, lse)
 
 
+def test_merge_of_two_empty_blocks_is_zero():
+    """No keys on either side: O = 0 and lse = -inf, with no NaN and no
+    floating-point warning; other rows of the same call are unaffected."""
+    o_a, o_b = _rand((1, 3, 2, 4), 12), _rand((1, 3, 2, 4), 13)
+    l_a, l_b = _rand((1, 2, 3), 14), _rand((1, 2, 3), 15)
+    l_a[0, 1, 2] = l_b[0, 1, 2] = -np.inf
+    with np.errstate(all="raise"):
+        mo, ml = RG.merge(o_a, l_a, o_b, l_b)
+    assert np.all(mo[0, 2, 1] == 0.0) and ml[0, 1, 2] == -np.inf
+    ref_o, ref_l = RG.merge(o_a[:, :2], l_a[:, :, :2], o_b[:, :2], l_b[:, :, :2])
+    assert np.array_equal(mo[:, :2], ref_o) and np.array_equal(ml[:, :, :2], ref_l)
+
+
 def test_merge_of_two_single_keys_is_logistic():
     """One key per block: the weight of block a is the logistic function of
     the score difference, and lse is log(e^sa + e^sb)."""
