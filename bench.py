@@ -27,7 +27,11 @@ video-DiT sequence over a 4 (Ulysses) x 2 (ring) grid: ring block 0, head
 group 0 (10 heads, 16380 query rows) attends to its own K/V block and then to
 ring block 1's (usp_attention_fwd_block, fp32 outputs and lse), and
 usp_attention_merge folds the two into the bf16 output; its flops are
-4 * Sq * S * D * h = 2.7474e12.
+4 * Sq * S * D * h = 2.7474e12. "chunked" times usp_attention_fwd_chunked on
+the long-sequence share (B=1, S=131072, h=8, D=128, 3 head-chunk passes of
+3/3/2 heads; 7.04e13 flop), and usp_attention_fwd_chunked_ws (workspace
+sized for the 3-head pass), next to the single-shot usp_attention_fwd on the
+same inputs (all the same bits).
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
 Also reported: each kernel alone (HIP events around each launch on the
@@ -183,6 +187,7 @@ def main():
     ap.add_argument("--skip-gqa", action="store_true", help="skip the grouped-head attention timing")
     ap.add_argument("--skip-rows", action="store_true", help="skip the row-movement timings")
     ap.add_argument("--skip-ring", action="store_true", help="skip the Ulysses+Ring pass timing")
+    ap.add_argument("--skip-chunked", action="store_true", help="skip the head-chunked timing")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     args = ap.parse_args()
@@ -378,6 +383,42 @@ def main():
                 "entry": "usp_attention_fwd_block (workspace) x 2 + usp_attention_merge"}
         del qr, kvr, rws, o_acc, o_blk, l_acc, l_blk, o_out
 
+    # head-chunked passes on the long-sequence share, against single shot
+    chunked = None
+    if not args.skip_chunked:
+        print("[bench] head-chunked passes (S=131072)", file=sys.stderr, flush=True)
+        cw = synth.WORKLOADS["long_chunked"]
+        cq, ck, cv = (bf(x) for x in synth.draw_workload(cw))
+        co = torch.empty_like(cq)
+        c_flops = 4.0 * cw.B * cw.H * cw.S * cw.S * cw.D
+        cmax = -(-cw.H // cw.chunks)   # heads of the largest pass
+        cws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cmax, cw.D) // 4,
+                          dtype=torch.float32, device=dev)
+        times = {}
+        for name, fn in (("chunked", lambda: usp.usp_attention_fwd_chunked(cq, ck, cv, co, cw.chunks)),
+                         ("chunked_ws", lambda: usp.usp_attention_fwd_chunked_ws(cq, ck, cv, co, cw.chunks,
+                                                                                 cws)),
+                         ("single_shot", lambda: usp.usp_attention_fwd(cq, ck, cv, co))):
+            fn()
+            torch.cuda.synchronize()
+            a, b_ = ev(), ev()
+            a.record()
+            for _ in range(3):
+                fn()
+            b_.record()
+            torch.cuda.synchronize()
+            times[name] = a.elapsed_time(b_) / 3
+        chunked = {"workload": "long_chunked", "h": cw.H, "S": cw.S, "D": cw.D,
+                   "chunks": usp.usp_head_chunk_ranges(cw.H, cw.chunks), "flop": c_flops,
+                   "ms": times["chunked"], "TFLOP/s": c_flops / (times["chunked"] * 1e-3) / 1e12,
+                   "ws_ms": times["chunked_ws"],
+                   "ws_TFLOP/s": c_flops / (times["chunked_ws"] * 1e-3) / 1e12,
+                   "single_shot_ms": times["single_shot"],
+                   "single_shot_TFLOP/s": c_flops / (times["single_shot"] * 1e-3) / 1e12,
+                   "entry": "usp_attention_fwd_chunked (3 passes; ws: usp_attention_fwd_chunked_ws) "
+                            "vs usp_attention_fwd"}
+        del cq, ck, cv, co, cws
+
     # plain device copy of 1 GiB: practical HBM reference and counter calibration
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -477,6 +518,7 @@ def main():
                                    "entry": "usp_attention_fwd"},
         "attention_gqa": gqa,
         "ring": ring,
+        "chunked": chunked,
         "step_pack_qkv": {"us": pack_ms * 1e3,
                           "GB/s": 3 * share_bytes / (pack_ms * 1e-3) / 1e9},
         "step_unpack_o": {"us": unpack_ms * 1e3,

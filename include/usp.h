@@ -324,6 +324,23 @@ int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void*
                               int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
                               void* stream);
 
+/*
+ * usp_attention_fwd_chunked with a caller workspace: each pass runs
+ * usp_attention_fwd_ws's kernels. Bitwise equal to usp_attention_fwd_chunked,
+ * usp_attention_fwd and usp_attention_fwd_ws.
+ *   ws, ws_bytes: device buffer, 16-byte aligned, of at least
+ *                 usp_attention_workspace_bytes(in_dt, B, S, c, D) bytes with
+ *                 c = ceil(h / chunks) (the largest pass), owned by the
+ *                 caller, reused by every pass; contents on entry do not
+ *                 matter. Ignored (may be NULL) for USP_F32 inputs.
+ * Errors: those of usp_attention_fwd_chunked, plus bf16 inputs with ws NULL
+ * or ws_bytes too small -> USP_EINVAL, ws misaligned -> USP_EALIGN.
+ */
+int usp_attention_fwd_chunked_ws(const void* q, const void* k, const void* v, void* o,
+                                 usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
+                                 int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -225,3 +225,15 @@ def _merge(oa=FAKE, la=FAKE, ob=FAKE + 256, lb=FAKE + 512, o=FAKE + 1024, lse=No
 def test_attention_merge_rejects(kw, status):
     assert _merge(**kw) == status
     assert usp.usp_last_error()
+
+
+def test_chunked_ws_rejects():
+    f = L.usp_attention_fwd_chunked_ws
+    need = 2 * 256 * 67 * 4 * 3   # S = 16, D = 64: one tile per head, largest pass 3 heads
+    args = (FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 64, 0.0, None)
+    assert f(*args, 2, None, need, None) == -1           # no workspace
+    assert f(*args, 2, FAKE + 4, need, None) == -4       # misaligned
+    assert f(*args, 2, FAKE, need - 1, None) == -1       # below the largest pass
+    assert f(*args, 4, FAKE, need, None) == -1           # 5 heads in 4 chunks leaves one empty
+    assert f(*args[:9], 80, *args[10:], 2, FAKE, need, None) == -5  # D = 80
+    assert usp.usp_last_error()

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 BF, F = synth.BF16, synth.F32
 
 
-def _run(q, k, v, dtype, out_dtype, lo=0, hi=None, scale=0.0, want_lse=False, chunks=None):
+def _run(q, k, v, dtype, out_dtype, lo=0, hi=None, scale=0.0, want_lse=False, chunks=None,
+         chunk_ws=False):
     import torch
     B, S, h, D = q.shape
     dq, dk, dv = (to_dev(x, dtype) for x in (q, k, v))
@@ -28,6 +29,12 @@ def _run(q, k, v, dtype, out_dtype, lo=0, hi=None, scale=0.0, want_lse=False, ch
     lse = torch.full((B, h, S), float("nan"), device=DEV) if want_lse else None
     if chunks is None:
         usp.usp_attention_fwd(dq, dk, dv, o, head_lo=lo, head_hi=hi, scale=scale, lse=lse)
+    elif chunk_ws:
+        # workspace for the largest pass, NaN-poisoned, exactly the size asked for
+        nb = usp.usp_attention_workspace_bytes(usp.USP_BF16 if dtype == BF else usp.USP_F32, B, S,
+                                               -(-h // chunks), D)
+        ws = torch.full((max(nb, 16) // 4,), float("nan"), device=DEV)
+        usp.usp_attention_fwd_chunked_ws(dq, dk, dv, o, chunks, ws, scale=scale, lse=lse)
     else:
         usp.usp_attention_fwd_chunked(dq, dk, dv, o, chunks, scale=scale, lse=lse)
     torch.cuda.synchronize()
@@ -114,6 +121,8 @@ def test_chunked_bitwise_equals_single_shot_small(h, chunks):
     one = _run(q, k, v, BF, F)
     many = _run(q, k, v, BF, F, chunks=chunks)
     assert one.tobytes() == many.tobytes()
+    log(f"attention chunked with workspace h={h} chunks={chunks}")
+    assert one.tobytes() == _run(q, k, v, BF, F, chunks=chunks, chunk_ws=True).tobytes()
     cb = usp.usp_head_chunk_ranges(h, chunks)
     by_range = np.concatenate([_run(q, k, v, BF, F, lo=cb[j], hi=cb[j + 1])[:, :, cb[j]:cb[j + 1]]
                                for j in range(chunks)], axis=2)
@@ -403,6 +412,8 @@ def test_long_chunked_full_size():
     many = _run(q, k, v, BF, F, chunks=w.chunks)
     assert usp.usp_head_chunk_ranges(w.H, w.chunks) == [0, 3, 6, 8]
     assert one.tobytes() == many.tobytes()
+    log("workload long_chunked: 3 head-chunk passes with a workspace")
+    assert one.tobytes() == _run(q, k, v, BF, F, chunks=w.chunks, chunk_ws=True).tobytes()
     assert not np.any(np.isnan(one))
     rows = {(0, hd): _sample_rows(w.S, 64, 40 + hd) for hd in range(w.H)}
     _check_sampled(one, q, k, v, BF, w.B, w.S, rows)

@@ -9,7 +9,7 @@ One rank's share of the work behind a small C ABI (``include/usp.h``,
     sequence-sharded <-> head-sharded relayouts around the all-to-alls;
   * ``usp_scatter_rows`` / ``usp_gather_rows`` / ``usp_reduce_scatter_rows``
     — ragged token rows at the model boundary;
-  * ``usp_attention_fwd`` / ``usp_attention_fwd_chunked`` — flash-style
+  * ``usp_attention_fwd`` / ``usp_attention_fwd_chunked`` (``_ws``) — flash-style
     non-causal attention over the full sequence for a head group;
     ``usp_attention_fwd_ws`` the same with a caller workspace (faster, same
     bits), sized by ``usp_attention_workspace_bytes``; ``usp_attention_fwd_gqa``
@@ -23,7 +23,8 @@ tensors for device memory, PyTorch streams); ``synth`` draws seeded inputs.
 """
 from ._binding import (  # noqa: F401
     USP_BF16, USP_F32, USP_MAX_PARTS, UspError, header_symbols, lib, usp_attention_fwd,
-    usp_attention_fwd_block, usp_attention_fwd_chunked, usp_attention_fwd_gqa,
+    usp_attention_fwd_block, usp_attention_fwd_chunked, usp_attention_fwd_chunked_ws,
+    usp_attention_fwd_gqa,
     usp_attention_fwd_ws, usp_attention_merge,
     usp_attention_workspace_bytes,
     usp_balanced_ranges, usp_balanced_ranges_device,

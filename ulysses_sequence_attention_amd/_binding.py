@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
                                         _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
         L.usp_attention_fwd_chunked.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
                                                 _i64, _i64, _i32, _i32, _f32, _vp, _i32, _vp]
+        L.usp_attention_fwd_chunked_ws.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                                   _i64, _i64, _i32, _i32, _f32, _vp, _i32, _vp,
+                                                   ctypes.c_size_t, _vp]
         L.usp_attention_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i32, _i32,
                                                     ctypes.POINTER(ctypes.c_size_t)]
         L.usp_attention_fwd_ws.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
@@ -83,7 +86,8 @@ def lib() -> ctypes.CDLL:
         L.usp_gather_rows.argtypes = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _vp]
         for name in ("usp_balanced_ranges", "usp_balanced_ranges_device", "usp_head_chunk_ranges",
                      "usp_pack_seq_to_heads", "usp_unpack_heads_to_seq", "usp_attention_fwd",
-                     "usp_attention_fwd_chunked", "usp_attention_workspace_bytes",
+                     "usp_attention_fwd_chunked", "usp_attention_fwd_chunked_ws",
+                     "usp_attention_workspace_bytes",
                      "usp_attention_fwd_ws", "usp_attention_fwd_gqa", "usp_attention_fwd_block",
                      "usp_attention_merge", "usp_scatter_rows",
                      "usp_gather_rows", "usp_reduce_scatter_rows"):
@@ -298,3 +302,15 @@ def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=N
     _check(lib().usp_attention_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
                                            _dtype(o), B, S, h, D, scale, _ptr(lse), chunks,
                                            _stream(q, stream)), "usp_attention_fwd_chunked")
+
+
+def usp_attention_fwd_chunked_ws(q, k, v, o, chunks: int, ws, scale: float = 0.0, lse=None,
+                                 stream=None) -> None:
+    """usp_attention_fwd_chunked with the caller's workspace tensor ``ws``
+    (sized for ceil(h / chunks) heads; None for fp32 inputs)."""
+    B, S, h, D = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().usp_attention_fwd_chunked_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
+                                              _dtype(o), B, S, h, D, scale, _ptr(lse), chunks,
+                                              _ptr(ws), nbytes, _stream(q, stream)),
+           "usp_attention_fwd_chunked_ws")

@@ -345,12 +345,10 @@ int usp_attention_merge(const float* o_a, const float* lse_a, const float* o_b,
   return ok();
 }
 
-int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,
-                              usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
-                              int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
-                              void* stream) {
-  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0, h};
-  if (int st = check_attention(a)) return st;
+// head-chunk passes of a (validated) attention call over all a.h heads; with
+// a workspace, the first (largest) chunk's size check covers every pass
+static int run_chunked(AttnArgs a, int32_t chunks, hipStream_t stream) {
+  const int32_t h = a.h;
   if (chunks < 1 || chunks > h)
     return fail(USP_EINVAL, "cannot run %d heads in %d non-empty chunks", h, chunks);
   int32_t bounds[USP_MAX_PARTS + 1];
@@ -361,13 +359,37 @@ int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void*
     hb = reinterpret_cast<int32_t*>(&heap[0]);
   }
   if (int st = usp_head_chunk_ranges(h, chunks, hb)) return st;
-  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)a.D);
   for (int32_t c = 0; c < chunks; ++c) {
     a.head_lo = hb[c];
     a.head_hi = hb[c + 1];
-    if (int st = run_attention(a, (hipStream_t)stream)) return st;
+    if (int st = run_attention(a, stream)) return st;
   }
   return ok();
+}
+
+int usp_attention_fwd_chunked(const void* q, const void* k, const void* v, void* o,
+                              usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
+                              int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
+                              void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, 0, h, scale, in_dt, out_dt, nullptr, 0, h};
+  if (int st = check_attention(a)) return st;
+  return run_chunked(a, chunks, (hipStream_t)stream);
+}
+
+int usp_attention_fwd_chunked_ws(const void* q, const void* k, const void* v, void* o,
+                                 usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S,
+                                 int32_t h, int32_t D, float scale, float* lse, int32_t chunks,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, 0, h, scale, in_dt, out_dt, ws, ws_bytes, h};
+  if (int st = check_attention(a)) return st;
+  if (in_dt == USP_BF16) {
+    if (!ws) return fail(USP_EINVAL, "workspace is null");
+    if (!aligned16(ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
+  } else {
+    a.ws = nullptr;  // the fp32 path needs none
+  }
+  return run_chunked(a, chunks, (hipStream_t)stream);
 }
 
 }  // extern "C"
