@@ -176,6 +176,28 @@ def test_rows_bitwise_independent_of_launch(D):
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
 
 
+EXACT_CASES = [  # B, S, h, D: lengths that are whole key tiles and whole 256-row tiles
+    (1, 256, 2, 128), (1, 512, 1, 64), (2, 4096, 1, 128), (1, 8192, 1, 64), (1, 320, 2, 128),
+    (1, 128, 3, 64),
+]
+
+
+@pytest.mark.parametrize("B,S,h,D", EXACT_CASES)
+def test_exact_tile_multiples(B, S, h, D):
+    """No partial key tile and no partial query tile (the masked last tile is
+    never taken; even and odd key-tile counts split into equal or unequal
+    halves): both kernels against the oracle, and bitwise against each other."""
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=61 + S + D)
+    ref, ref_lse = A.attention(*(widen(x, BF) for x in (q, k, v)), return_lse=True)
+    log(f"attention exact tiles B={B} S={S} h={h} D={D}")
+    out, lse = _run(q, k, v, BF, F, want_lse=True)
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lse - ref_lse)) <= BF16_LSE_ABS
+    out_ws, lse_ws = _run_ws(q, k, v, BF, F, want_lse=True)
+    assert out.tobytes() == out_ws.tobytes() and lse.tobytes() == lse_ws.tobytes()
+
+
 WS_CASES = [  # B, S, h, D: one key tile (empty first half), odd key-tile counts, both D
     (1, 1, 1, 64), (1, 64, 3, 128), (1, 257, 5, 128), (2, 513, 2, 64), (1, 1000, 2, 128),
     (1, 130, 4, 64), (3, 300, 2, 128),

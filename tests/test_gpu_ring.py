@@ -55,6 +55,7 @@ BLOCK_CASES = [  # B, Sq, Sk, h, hkv, D: ragged tails on both sides, one-tile an
     (1, 1, 1, 1, 1, 64), (1, 300, 65, 2, 1, 128), (2, 257, 1000, 2, 2, 64),
     (1, 100, 513, 4, 2, 128), (1, 513, 129, 1, 1, 64), (1, 700, 64, 2, 2, 128),
     (1, 64, 2, 1, 1, 128), (1, 1, 777, 3, 3, 64), (2, 600, 300, 4, 4, 128),
+    (1, 256, 512, 2, 2, 128), (1, 512, 256, 2, 1, 64),
 ]
 
 
