@@ -92,10 +92,11 @@ def cpu_baseline(q, k, v, h0, S, D, target_s):
                   for x in (q, k, v))
     cores = A.host_cores()
     rng = np.random.default_rng(123)
-    # calibrate on one core, then size the sample for about target_s of wall time
+    # calibrate on one core (512 rows, so that copying the head's K/V planes
+    # weighs little), then size the sample for about target_s of wall time
     t0 = time.perf_counter()
-    A.attention_rows(qf, kf, vf, 0, 0, np.arange(64))
-    per_row = (time.perf_counter() - t0) / 64
+    A.attention_rows(qf, kf, vf, 0, 0, np.arange(512))
+    per_row = (time.perf_counter() - t0) / 512
     n = int(max(64, min(S, target_s * cores / (per_row * h0))))
     rows = {(0, hd): (np.arange(S) if n >= S else np.sort(rng.choice(S, n, replace=False)))
             for hd in range(h0)}
