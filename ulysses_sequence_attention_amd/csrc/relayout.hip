@@ -43,7 +43,10 @@ struct RelayoutParams {
 };
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+// one 16-byte chunk per thread: 13-21 VGPRs, so that these waves also fit
+// beside the attention kernel's workgroups on a CU (measured faster alone
+// too than four chunks per thread at 64 VGPRs)
+constexpr int kUnroll = 1;
 
 template <bool kPack>
 __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutParams p, Ptrs blk) {

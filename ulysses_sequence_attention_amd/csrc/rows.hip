@@ -43,7 +43,10 @@ struct RowParams {
 };
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+// one 16-byte chunk per thread: 13-21 VGPRs, so that these waves also fit
+// beside the attention kernel's workgroups on a CU (measured faster alone
+// too than four chunks per thread at 64 VGPRs)
+constexpr int kUnroll = 1;
 
 // full-tensor row s (within a batch row) -> (rank r, index within its shard, shard length)
 __device__ __forceinline__ void rank_of(const RowParams& p, uint32_t s, uint32_t& r, uint32_t& i,
