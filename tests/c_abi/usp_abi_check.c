@@ -1,0 +1,185 @@
+/*
+ * A plain C consumer of libusp (include/usp.h) with the HIP runtime and no
+ * other framework in the process: it checks that the boundary is usable as a
+ * C ABI on its own. Numerical parity against the oracle is the Python tests'
+ * job; this program checks what needs no reference: the stated range splits,
+ * the pack -> unpack round trip bit for bit, the attention entry points that
+ * must agree bit for bit (default, workspace, head-chunked), finite outputs,
+ * and error codes with their messages. Exit status 0 when every check holds.
+ */
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "usp.h"
+
+static int failures = 0;
+
+#define CHECK(cond, ...)                        \
+  do {                                          \
+    if (!(cond)) {                              \
+      fprintf(stderr, "FAILED: " __VA_ARGS__);  \
+      fprintf(stderr, "\n");                    \
+      ++failures;                               \
+    }                                           \
+  } while (0)
+
+#define HIP_OK(call)                                                         \
+  do {                                                                       \
+    hipError_t e_ = (call);                                                  \
+    if (e_ != hipSuccess) {                                                  \
+      fprintf(stderr, "HIP error %s at %s\n", hipGetErrorString(e_), #call); \
+      exit(2);                                                               \
+    }                                                                        \
+  } while (0)
+
+/* deterministic bf16 bits of values in [-1, 1) (xorshift, truncating fp32) */
+static void fill_bf16(uint16_t* x, size_t n, uint32_t seed) {
+  uint32_t s = seed * 2654435761u + 1u;
+  for (size_t i = 0; i < n; ++i) {
+    s ^= s << 13;
+    s ^= s >> 17;
+    s ^= s << 5;
+    float f = (float)(s >> 8) / 8388608.0f - 1.0f;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    x[i] = (uint16_t)(u >> 16);
+  }
+}
+
+static void* dev_alloc(size_t bytes) {
+  void* p = NULL;
+  HIP_OK(hipMalloc(&p, bytes));
+  return p;
+}
+
+static void check_ranges(void) {
+  int64_t b[5];
+  CHECK(usp_balanced_ranges(257, 3, b) == USP_OK && b[0] == 0 && b[1] == 86 && b[2] == 172 &&
+            b[3] == 257, "257 tokens over 3 ranks");
+  CHECK(usp_balanced_ranges(577, 4, b) == USP_OK && b[1] == 145 && b[2] == 289 && b[3] == 433 &&
+            b[4] == 577, "577 tokens over 4 ranks");
+  CHECK(usp_balanced_ranges(65537, 4, b) == USP_OK && b[1] == 16385 && b[4] == 65537,
+        "65537 tokens over 4 ranks");
+  int32_t c[4];
+  CHECK(usp_head_chunk_ranges(8, 3, c) == USP_OK && c[1] == 3 && c[2] == 6 && c[3] == 8,
+        "8 heads in 3 chunks");
+  CHECK(usp_balanced_ranges(2, 3, b) == USP_EINVAL && strlen(usp_last_error()) > 0,
+        "fewer items than parts is rejected with a message");
+}
+
+static void check_relayout(void) {
+  const int64_t B = 2, S = 301;
+  const int32_t H = 6, D = 64, P = 4;
+  const size_t n = (size_t)B * S * H * D;
+  uint16_t* host = (uint16_t*)malloc(n * 2);
+  uint16_t* back = (uint16_t*)malloc(n * 2);
+  fill_bf16(host, n, 7);
+  int64_t hb[P + 1];
+  CHECK(usp_balanced_ranges(H, P, hb) == USP_OK, "head ranges");
+  void* seq = dev_alloc(n * 2);
+  void* out = dev_alloc(n * 2);
+  void* blk[P];
+  for (int j = 0; j < P; ++j) blk[j] = dev_alloc((size_t)B * S * (hb[j + 1] - hb[j]) * D * 2);
+  HIP_OK(hipMemcpy(seq, host, n * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemset(out, 0xff, n * 2));
+  CHECK(usp_pack_seq_to_heads(seq, blk, USP_BF16, B, S, H, D, P, -1, NULL) == USP_OK, "pack");
+  CHECK(usp_unpack_heads_to_seq((const void* const*)blk, out, USP_BF16, B, S, H, D, P, -1, NULL) ==
+            USP_OK, "unpack");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(back, out, n * 2, hipMemcpyDeviceToHost));
+  CHECK(memcmp(host, back, n * 2) == 0, "unpack(pack(x)) == x bit for bit");
+  /* block 1 holds heads [2, 4): spot-check one element against the closed form */
+  uint16_t e;
+  const int64_t bb = 1, s = 17, i = 1, d = 5;
+  HIP_OK(hipMemcpy(&e, (char*)blk[1] + ((((size_t)bb * S + s) * (hb[2] - hb[1]) + i) * D + d) * 2,
+                   2, hipMemcpyDeviceToHost));
+  CHECK(e == host[(((size_t)bb * S + s) * H + hb[1] + i) * D + d], "block element in place");
+  for (int j = 0; j < P; ++j) HIP_OK(hipFree(blk[j]));
+  HIP_OK(hipFree(seq));
+  HIP_OK(hipFree(out));
+  free(host);
+  free(back);
+}
+
+static void check_attention(void) {
+  const int64_t B = 1, S = 700;
+  const int32_t h = 3, D = 128;
+  const size_t n = (size_t)B * S * h * D;
+  uint16_t* host = (uint16_t*)malloc(n * 2);
+  void* qkv[3];
+  for (int t = 0; t < 3; ++t) {
+    fill_bf16(host, n, 11 + t);
+    qkv[t] = dev_alloc(n * 2);
+    HIP_OK(hipMemcpy(qkv[t], host, n * 2, hipMemcpyHostToDevice));
+  }
+  float* o[3];
+  float* lse[3];
+  for (int r = 0; r < 3; ++r) {
+    o[r] = (float*)dev_alloc(n * 4);
+    lse[r] = (float*)dev_alloc((size_t)B * h * S * 4);
+  }
+  size_t ws_bytes = 0;
+  CHECK(usp_attention_workspace_bytes(USP_BF16, B, S, h, D, &ws_bytes) == USP_OK && ws_bytes > 0,
+        "workspace size");
+  void* ws = dev_alloc(ws_bytes);
+  CHECK(usp_attention_fwd(qkv[0], qkv[1], qkv[2], o[0], USP_BF16, USP_F32, B, S, h, D, 0, h, 0.0f,
+                          lse[0], NULL) == USP_OK, "usp_attention_fwd");
+  CHECK(usp_attention_fwd_ws(qkv[0], qkv[1], qkv[2], o[1], USP_BF16, USP_F32, B, S, h, D, 0, h,
+                             0.0f, lse[1], ws, ws_bytes, NULL) == USP_OK, "usp_attention_fwd_ws");
+  CHECK(usp_attention_fwd_chunked(qkv[0], qkv[1], qkv[2], o[2], USP_BF16, USP_F32, B, S, h, D, 0.0f,
+                                  lse[2], 2, NULL) == USP_OK, "usp_attention_fwd_chunked");
+  HIP_OK(hipDeviceSynchronize());
+  float* a = (float*)malloc(n * 4);
+  float* b = (float*)malloc(n * 4);
+  HIP_OK(hipMemcpy(a, o[0], n * 4, hipMemcpyDeviceToHost));
+  int finite = 1;
+  for (size_t i = 0; i < n; ++i) finite &= isfinite(a[i]) && fabsf(a[i]) <= 1.0f;
+  CHECK(finite, "outputs finite and within the range of V");
+  for (int r = 1; r < 3; ++r) {
+    HIP_OK(hipMemcpy(b, o[r], n * 4, hipMemcpyDeviceToHost));
+    CHECK(memcmp(a, b, n * 4) == 0, "attention path %d equals the default bit for bit", r);
+  }
+  const size_t nl = (size_t)B * h * S;
+  HIP_OK(hipMemcpy(a, lse[0], nl * 4, hipMemcpyDeviceToHost));
+  for (int r = 1; r < 3; ++r) {
+    HIP_OK(hipMemcpy(b, lse[r], nl * 4, hipMemcpyDeviceToHost));
+    CHECK(memcmp(a, b, nl * 4) == 0, "lse of path %d equals the default bit for bit", r);
+  }
+  CHECK(usp_attention_fwd(qkv[0], qkv[1], qkv[2], o[0], USP_BF16, USP_F32, B, S, h, 96, 0, h, 0.0f,
+                          NULL, NULL) == USP_ENOSYS && strlen(usp_last_error()) > 0,
+        "unsupported head dim rejected with a message");
+  CHECK(usp_attention_fwd_ws(qkv[0], qkv[1], qkv[2], o[1], USP_BF16, USP_F32, B, S, h, D, 0, h,
+                             0.0f, NULL, ws, ws_bytes - 1, NULL) == USP_EINVAL,
+        "a workspace one byte short is rejected");
+  for (int t = 0; t < 3; ++t) HIP_OK(hipFree(qkv[t]));
+  for (int r = 0; r < 3; ++r) {
+    HIP_OK(hipFree(o[r]));
+    HIP_OK(hipFree(lse[r]));
+  }
+  HIP_OK(hipFree(ws));
+  free(host);
+  free(a);
+  free(b);
+}
+
+int main(void) {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    fprintf(stderr, "no HIP device\n");
+    return 2;
+  }
+  printf("%s\n", usp_version());
+  check_ranges();
+  check_relayout();
+  check_attention();
+  if (failures) {
+    fprintf(stderr, "%d check(s) failed\n", failures);
+    return 1;
+  }
+  printf("usp C ABI check: ok\n");
+  return 0;
+}

@@ -237,3 +237,16 @@ def test_chunked_ws_rejects():
     assert f(*args, 4, FAKE, need, None) == -1           # 5 heads in 4 chunks leaves one empty
     assert f(*args[:9], 80, *args[10:], 2, FAKE, need, None) == -5  # D = 80
     assert usp.usp_last_error()
+
+
+def test_c_consumer_links_against_this_library():
+    """The plain C consumer of the ABI resolves libusp to this package's build
+    and the HIP runtime, with no PyTorch library (linking only, no GPU)."""
+    import os
+    binp = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "usp_abi_check")
+    assert os.path.exists(binp), "run __graft_entry__.build() first"
+    out = subprocess.run(["ldd", binp], capture_output=True, text=True, check=True).stdout
+    libs = {line.split()[0]: line for line in out.splitlines() if "=>" in line}
+    assert os.path.realpath(usp._binding.LIB_PATH) in os.path.realpath(libs["libusp.so"].split("=>")[1].split()[0])
+    assert "libamdhip64.so.7" in libs and "not found" not in libs["libamdhip64.so.7"]
+    assert not any("torch" in line for line in libs.values())

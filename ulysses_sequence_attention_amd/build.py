@@ -60,6 +60,25 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "usp_abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "usp_abi_check")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile the plain C consumer of the ABI (tests/c_abi) with gcc against
+    include/usp.h, libusp.so and the HIP runtime; no PyTorch involved."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    tmp = C_CHECK_BIN + ".tmp"
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+          C_CHECK_SRC, "-o", tmp, "-L", PKG, "-lusp", "-L", os.path.join(rocm, "lib"),
+          "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../../ulysses_sequence_attention_amd",
+          "-Wl,-rpath," + os.path.join(rocm, "lib")], verbose)
+    os.replace(tmp, C_CHECK_BIN)
+    return C_CHECK_BIN
+
+
 if __name__ == "__main__":
     extra = [a for a in sys.argv[1:] if a != "--verbose"]
     print(build(verbose="--verbose" in sys.argv, extra_flags=extra))
+    print(build_c_check(verbose="--verbose" in sys.argv))
