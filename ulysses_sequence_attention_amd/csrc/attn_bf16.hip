@@ -121,16 +121,6 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ uint32_t word(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
-// bf16 element j of a and of b side by side in one dword (a low, b high)
-__device__ __forceinline__ uint32_t pair16(const uint4& a, const uint4& b, int j) {
-  // v_perm_b32 byte select over {b (bytes 4-7), a (bytes 0-3)}
-  return __builtin_amdgcn_perm(word(b, j >> 1), word(a, j >> 1), (j & 1) ? 0x07060302u : 0x05040100u);
-}
-
 // max / sum of a value with the same value in lane ^ 32 (v_permlane32_swap:
 // with both operands x it returns (x of lanes 0-31, x of lanes 32-63) in
 // both halves)
@@ -228,10 +218,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   }
 
   // ---- K/V tile staging (global -> LDS directly) ---------------------------
-  // global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i, so
-  // one load fills RPI whole rows and rows cannot be padded. Instead the
-  // 16-byte chunks of a row are stored at XOR-swizzled positions (lane i
-  // fetches the chunk whose swizzled position is i mod CPR):
+  // A direct load (buffer_load_dwordx4 ... lds) writes lane i's 16 bytes to
+  // LDS base + 16 i, so one load fills RPI whole rows and rows cannot be
+  // padded. Instead the 16-byte chunks of a row are stored at XOR-swizzled
+  // positions (lane i fetches the chunk whose swizzled position is i mod CPR):
   //   K: chunk c of row r at position c ^ ((r / RPL) mod CPR), so the 16 rows
   //      of a fragment read fall on 16 distinct bank quads;
   //   V: chunk c of row r at position c ^ 4((r / RPL) mod (CPR / 4)), so the
