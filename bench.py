@@ -27,7 +27,9 @@ video-DiT sequence over a 4 (Ulysses) x 2 (ring) grid: ring block 0, head
 group 0 (10 heads, 16380 query rows) attends to its own K/V block and then to
 ring block 1's (usp_attention_fwd_block, fp32 outputs and lse), and
 usp_attention_merge folds the two into the bf16 output; its flops are
-4 * Sq * S * D * h = 2.7474e12. "chunked" times usp_attention_fwd_chunked on
+4 * Sq * S * D * h = 2.7474e12. The second block's attention runs on a
+second stream (its own workspace), as a ring would launch it on arrival, and
+the fold waits for it; the one-stream pass is reported beside it. "chunked" times usp_attention_fwd_chunked on
 the long-sequence share (B=1, S=131072, h=8, D=128, 3 head-chunk passes of
 3/3/2 heads; 7.04e13 flop), and usp_attention_fwd_chunked_ws (workspace
 sized for the 3-head pass), next to the single-shot usp_attention_fwd on the
@@ -456,15 +458,64 @@ def main():
         torch.cuda.synchronize()
         r_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in revs]))
         m_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in revs]))
+        serial_out = o_out.clone()
+
+        # the same pass with the other blocks' attention on a second stream
+        # (each with its own workspace and output buffers): a ring delivers
+        # the next block long before the current one is done, so its launch
+        # can fill the CUs the current launch leaves idle at its tail; the
+        # folds stay in ring order on the first stream
+        side = torch.cuda.Stream()
+        rws2 = torch.empty_like(rws)
+        o_b2 = [o_blk, torch.empty_like(o_blk)]
+        l_b2 = [l_blk, torch.empty_like(l_blk)]
+        ev_blk = [torch.cuda.Event() for _ in range(2)]
+        ev_fold = [torch.cuda.Event() for _ in range(2)]
+        main_r = torch.cuda.current_stream()
+
+        def ring_pass_2s():
+            start = torch.cuda.Event()
+            start.record(main_r)
+            side.wait_event(start)
+            for e in ev_fold:
+                e.record(main_r)
+            usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws, stream=main_r)
+            for n, i in enumerate(order[1:]):
+                bset = n % 2
+                side.wait_event(ev_fold[bset])   # buffer set read by the fold two blocks back
+                usp.usp_attention_fwd_block(qr, *kvr[i], o_b2[bset], lse=l_b2[bset], ws=rws2,
+                                            stream=side)
+                ev_blk[bset].record(side)
+                main_r.wait_event(ev_blk[bset])
+                last = n == len(order) - 2
+                usp.usp_attention_merge(o_acc, l_acc, o_b2[bset], l_b2[bset],
+                                        o_out if last else o_acc, None if last else l_acc,
+                                        stream=main_r)
+                ev_fold[bset].record(main_r)
+
+        for _ in range(3):
+            ring_pass_2s()
+        torch.cuda.synchronize()
+        a2, b2 = ev(), ev()
+        a2.record()
+        for _ in range(reps):
+            ring_pass_2s()
+        b2.record()
+        torch.cuda.synchronize()
+        r2_ms = a2.elapsed_time(b2) / reps
+        if not torch.equal(serial_out, o_out):
+            raise RuntimeError("the two-stream ring pass changed the output")
         r_flops = 4.0 * rw.B * rh * Sq * rw.S * rw.D
         m_bytes = rw.B * Sq * rh * rw.D * (4 + 4 + 2) + 2 * rw.B * rh * Sq * 4
         ring = {"workload": "video_dit_ring", "grid": f"{rw.P} ulysses x {rw.ring} ring",
                 "rank": "ring block 0, head group 0", "h": rh, "Sq": Sq, "S": rw.S, "D": rw.D,
-                "ms": r_ms, "TFLOP/s": r_flops / (r_ms * 1e-3) / 1e12,
-                "frac_peak": r_flops / (r_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": r_flops,
+                "ms": r2_ms, "TFLOP/s": r_flops / (r2_ms * 1e-3) / 1e12,
+                "frac_peak": r_flops / (r2_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": r_flops,
+                "one_stream_ms": r_ms, "one_stream_TFLOP/s": r_flops / (r_ms * 1e-3) / 1e12,
                 "merge_us": m_ms * 1e3, "merge_GB/s": m_bytes / (m_ms * 1e-3) / 1e9,
-                "entry": "usp_attention_fwd_block (workspace) x 2 + usp_attention_merge"}
-        del qr, kvr, rws, o_acc, o_blk, l_acc, l_blk, o_out
+                "entry": "usp_attention_fwd_block (workspace) x 2 + usp_attention_merge; the "
+                         "second block on a second stream (one_stream: all on one stream)"}
+        del qr, kvr, rws, rws2, o_acc, o_blk, l_acc, l_blk, o_out, o_b2, l_b2, serial_out
 
     # head-chunked passes on the long-sequence share, against single shot
     chunked = None
