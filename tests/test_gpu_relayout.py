@@ -108,3 +108,36 @@ def test_p1_is_byte_identical():
     usp.usp_pack_seq_to_heads(to_dev(x, BF), [blk])
     torch.cuda.synchronize()
     assert to_host(blk).tobytes() == x.tobytes()
+
+
+def test_world_pack_unpack_beyond_one_launch():
+    """A 34.8 GB bf16 tensor (S = 17000003, H = 8, D = 128): 2^31 + 28M chunks,
+    more than one launch's 32-bit flat index, so the row walk is split in two
+    launches. Device-side full compare against the definition (block j holds
+    heads [c_j, c_{j+1})), the round trip, and the oracle on sampled rows
+    around the launch boundary (row 2^31 // 128 - 1 = 16777215)."""
+    import torch
+    B, S, H, D, P = 1, 17_000_003, 8, 128, 3
+    hb = R.balanced_ranges(H, P)
+    torch.manual_seed(5)
+    bits = torch.randint(-32768, 32768, (B, S, H, D), dtype=torch.int16, device=DEV)
+    blocks = [torch.empty((B, S, hb[j + 1] - hb[j], D), dtype=torch.bfloat16, device=DEV)
+              for j in range(P)]
+    log(f"pack world beyond one launch S={S} H={H} D={D} P={P} (34.8 GB)")
+    usp.usp_pack_seq_to_heads(bits.view(torch.bfloat16), blocks)
+    torch.cuda.synchronize()
+    for j in range(P):
+        assert torch.equal(blocks[j].view(torch.int16), bits[:, :, hb[j]:hb[j + 1]]), f"block {j}"
+    rows = np.array([0, 1, 16777213, 16777214, 16777215, 16777216, 16777217, S - 2, S - 1])
+    host = bits[:, rows].cpu().numpy().view(np.uint16)
+    ref = X.pack_seq_to_heads(host, P)
+    for j in range(P):
+        assert blocks[j][:, rows].view(torch.int16).cpu().numpy().view(np.uint16).tobytes() == \
+            ref[j].tobytes()
+    back = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=DEV)
+    log("unpack world beyond one launch")
+    usp.usp_unpack_heads_to_seq(blocks, back)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), bits)
+    del bits, blocks, back
+    torch.cuda.empty_cache()

@@ -145,3 +145,36 @@ def test_video_dit_boundary_full_size():
         ref = np.sum(wide, axis=0)
         got = widen(to_host(outs[r])[:, rows], BF)
         assert np.all(np.abs(got - ref) <= _rs_bound(wide, BF))
+
+
+def test_scatter_gather_beyond_one_launch():
+    """[1, 17000003, 1024] bf16 (34.8 GB): more 16-byte chunks than one
+    launch's 32-bit flat index, so the walk is split in two launches.
+    Device-side full compare (shard r is rows [t_r, t_{r+1})), the gather
+    round trip, and the oracle's scatter on sampled rows around the split."""
+    import torch
+    B, S, W, P = 1, 17_000_003, 1024, 3
+    tb = R.balanced_ranges(S, P)
+    torch.manual_seed(6)
+    full = torch.randint(-32768, 32768, (B, S, W), dtype=torch.int16, device=DEV)
+    shards = [torch.empty((B, tb[r + 1] - tb[r], W), dtype=torch.bfloat16, device=DEV)
+              for r in range(P)]
+    log(f"scatter beyond one launch S={S} W={W} P={P} (34.8 GB)")
+    usp.usp_scatter_rows(full.view(torch.bfloat16), shards)
+    torch.cuda.synchronize()
+    for r in range(P):
+        assert torch.equal(shards[r].view(torch.int16), full[:, tb[r]:tb[r + 1]]), f"shard {r}"
+    # rows around the launch split (row 16777214) and the shard boundaries
+    rows = np.array([0, 16777212, 16777213, 16777214, 16777215, tb[1] - 1, tb[1], tb[2], S - 1])
+    for s in rows:
+        r = int(np.searchsorted(tb, s, side="right") - 1)
+        ref = X.scatter_sequence(full[:, s:s + 1].cpu().numpy(), 1, 0)
+        got = shards[r][:, s - tb[r]:s - tb[r] + 1].view(torch.int16).cpu().numpy()
+        assert got.tobytes() == ref.tobytes(), s
+    back = torch.empty((B, S, W), dtype=torch.bfloat16, device=DEV)
+    log("gather beyond one launch")
+    usp.usp_gather_rows(shards, back)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), full)
+    del full, shards, back
+    torch.cuda.empty_cache()
