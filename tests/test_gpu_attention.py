@@ -474,3 +474,22 @@ def test_gqa_video_share_full_size():
     assert not np.any(np.isnan(out))
     rows = {(0, hd): _sample_rows(w.S, 200, 60 + hd) for hd in range(hq[1] - hq[0])}
     _check_sampled(out, qs, ks, vs, BF, w.B, w.S, rows, lse=lse)
+
+
+def test_very_long_sequence_sampled():
+    """S = 1048583 (16384 key tiles and a ragged tail, one head, D = 128):
+    the key-half and key-group kernels agree bit for bit, and sampled rows
+    (the ends and rows around 256-row tile and key-half boundaries) match the
+    oracle over all keys."""
+    B, S, h, D = 1, 1_048_583, 1, 128
+    q, k, v = synth.draw_qkv(B, S, h, D, seed=91)
+    log(f"attention very long sequence S={S} (key groups)")
+    out, lse = _run(q, k, v, BF, F, want_lse=True)
+    log(f"attention very long sequence S={S} (key halves, workspace)")
+    out_ws, lse_ws = _run_ws(q, k, v, BF, F, want_lse=True)
+    assert out.tobytes() == out_ws.tobytes() and lse.tobytes() == lse_ws.tobytes()
+    assert not np.any(np.isnan(out))
+    half = (S + 63) // 64 // 2 * 64     # first key of the second half
+    extra = np.array([255, 256, half - 1, half, half + 1, S - 257, S - 256])
+    rows = {(0, 0): np.unique(np.concatenate([_sample_rows(S, 40, 92), extra]))}
+    _check_sampled(out, q, k, v, BF, B, S, rows, lse=lse)

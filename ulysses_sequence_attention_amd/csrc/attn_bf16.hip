@@ -667,7 +667,8 @@ int launch(const AttnArgs& a, hipStream_t s) {
   p.n_tiles = 0;
   p.ws_o = p.ws_m = p.ws_l = nullptr;
   const int64_t tiles = int64_t(p.n_qtiles) * p.nheads * a.B;
-  if (tiles > 0x3fffffff) return fail(USP_ESHAPE, "attention grid too large");
+  if (tiles > 0x3fffffff || (a.ws && tiles * (a.D / 4) > 0x7fffffff))
+    return fail(USP_ESHAPE, "attention grid too large");
   if (a.ws && a.ws_bytes < halves_ws_bytes(tiles, a.D))
     return fail(USP_EINVAL, "workspace of %zu bytes is below the %zu this call needs", a.ws_bytes,
                 halves_ws_bytes(tiles, a.D));
