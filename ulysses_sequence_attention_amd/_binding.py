@@ -7,6 +7,12 @@ arguments, dtypes the usp_dtype enum, tensors their data pointers, and the
 stream defaults to PyTorch's current stream on the tensor's device. A
 negative status raises ``UspError`` with the library's message.
 
+The C ABI sees only pointers, so the binding checks what a pointer cannot
+carry before any call: every tensor's shape against the others (and, for
+block and shard lists, against the library's own balanced ranges), matching
+dtypes, and that all tensors live on the same GPU; a mismatch raises
+``ValueError`` instead of letting a kernel read or write past a buffer.
+
 The library must have been built (``python -m ulysses_sequence_attention_amd.build``);
 there is no fallback path.
 """
@@ -124,6 +130,57 @@ def _stream(t, stream):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _torch():
+    import torch
+    return torch
+
+
+def _need(t, name, shape, dtypes=None):
+    """Raise ValueError unless ``t`` has ``shape`` (and one of ``dtypes``)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+
+
+def _on_gpu(named):
+    """Raise ValueError unless every (name, tensor) in ``named`` that is not
+    None is a GPU tensor on the first one's device (checked after shapes)."""
+    ref = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if ref is None:
+            ref = t
+        elif t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {ref.device}")
+
+
+def _dims(t, name, n):
+    if t is None or t.dim() != n:
+        raise ValueError(f"{name} must be a {n}-dimensional tensor")
+    return tuple(t.shape)
+
+
+def _attn_io(q, k, v, o, lse, ws=None, kv_rows=None, kv_heads=None):
+    """Checks of q, o [B,S,h,D], k, v [B,kv_rows,kv_heads,D], lse [B,h,S]
+    and the workspace's device."""
+    torch = _torch()
+    B, S, h, D = _dims(q, "q", 4)
+    kr = S if kv_rows is None else kv_rows
+    kh = h if kv_heads is None else kv_heads
+    _need(k, "k", (B, kr, kh, D), (q.dtype,))
+    _need(v, "v", (B, kr, kh, D), (q.dtype,))
+    _need(o, "o", (B, S, h, D), (torch.float32, torch.bfloat16))
+    if lse is not None:
+        _need(lse, "lse", (B, h, S), (torch.float32,))
+    _on_gpu([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("ws", ws)])
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -150,6 +207,9 @@ def usp_balanced_ranges(total: int, parts: int) -> list[int]:
 
 def usp_balanced_ranges_device(total: int, parts: int, out, stream=None) -> None:
     """Boundaries into the device int64 tensor ``out`` (parts + 1 elements)."""
+    if parts >= 1:
+        _need(out, "out", (int(parts) + 1,), (_torch().int64,))
+        _on_gpu([("out", out)])
     _check(lib().usp_balanced_ranges_device(total, parts, _ptr(out), _stream(out, stream)),
            "usp_balanced_ranges_device")
 
@@ -162,8 +222,23 @@ def usp_head_chunk_ranges(heads: int, chunks: int) -> list[int]:
 
 
 def _relayout_dims(seq, blocks, rank):
-    B, L, H, D = seq.shape
-    S = blocks[0].shape[1] if rank >= 0 else L
+    B, L, H, D = _dims(seq, "seq", 4)
+    P = len(blocks)
+    if P < 1:
+        return B, L, H, D
+    S = _dims(blocks[0], "blocks[0]", 4)[1] if rank >= 0 else L
+    # shapes are checked where the library would accept the sizes; otherwise
+    # the call itself reports the error
+    if 1 <= P <= min(H, USP_MAX_PARTS) and S >= P and rank < P:
+        hb = usp_balanced_ranges(H, P)
+        for j in range(P):
+            _need(blocks[j], f"blocks[{j}]", (B, S, hb[j + 1] - hb[j], D), (seq.dtype,))
+        rows = S
+        if rank >= 0:
+            tb = usp_balanced_ranges(S, P)
+            rows = tb[rank + 1] - tb[rank]
+        _need(seq, "seq", (B, rows, H, D))
+        _on_gpu([("seq", seq)] + [(f"blocks[{j}]", blocks[j]) for j in range(P)])
     return B, S, H, D
 
 
@@ -187,11 +262,27 @@ def usp_unpack_heads_to_seq(blocks, seq, rank: int = -1, stream=None) -> None:
 
 
 def _row_dims(full_like):
+    if full_like is None or full_like.dim() < 2:
+        raise ValueError("row tensors must have at least 2 dimensions [B, S, ...]")
     B, S = full_like.shape[0], full_like.shape[1]
     W = 1
     for n in full_like.shape[2:]:
         W *= n
     return B, S, W
+
+
+def _check_shards(full_like, shards, which, name):
+    """shards[r] must be [B, len_r, ...] for the ranks in ``which``."""
+    B, S = full_like.shape[0], full_like.shape[1]
+    P = len(shards)
+    if not (1 <= P <= USP_MAX_PARTS and S >= P):
+        return
+    tb = usp_balanced_ranges(S, P)
+    which = [r for r in which if 0 <= r < P]
+    for r in which:
+        _need(shards[r], f"{name}[{r}]", (B, tb[r + 1] - tb[r]) + tuple(full_like.shape[2:]),
+              (full_like.dtype,))
+    _on_gpu([("full", full_like)] + [(f"{name}[{r}]", shards[r]) for r in which])
 
 
 def _ptr_array(tensors, P):
@@ -203,6 +294,7 @@ def usp_scatter_rows(full, shards, rank: int = -1, stream=None) -> None:
     for ``rank`` only (the other entries may be None)."""
     P = len(shards)
     B, S, W = _row_dims(full)
+    _check_shards(full, shards, range(P) if rank < 0 else [rank], "shards")
     _check(lib().usp_scatter_rows(_ptr(full), _ptr_array(shards, P), _dtype(full), B, S, W, P,
                                   rank, _stream(full, stream)), "usp_scatter_rows")
 
@@ -211,6 +303,7 @@ def usp_gather_rows(shards, full, stream=None) -> None:
     """shards[r] [B,len_r,...] -> full [B,S,...] in rank order."""
     P = len(shards)
     B, S, W = _row_dims(full)
+    _check_shards(full, shards, range(P), "shards")
     _check(lib().usp_gather_rows(_ptr_array(shards, P), _ptr(full), _dtype(full), B, S, W, P,
                                  _stream(full, stream)), "usp_gather_rows")
 
@@ -220,6 +313,10 @@ def usp_reduce_scatter_rows(partials, out, rank: int = -1, stream=None) -> None:
     every rank (rank < 0) or ``rank`` only."""
     P = len(partials)
     B, S, W = _row_dims(partials[0])
+    for j in range(P):
+        _need(partials[j], f"partials[{j}]", tuple(partials[0].shape), (partials[0].dtype,))
+    _check_shards(partials[0], out, range(P) if rank < 0 else [rank], "out")
+    _on_gpu([(f"partials[{j}]", partials[j]) for j in range(P)])
     _check(lib().usp_reduce_scatter_rows(_ptr_array(partials, P), _ptr_array(out, P),
                                          _dtype(partials[0]), B, S, W, P, rank,
                                          _stream(partials[0], stream)), "usp_reduce_scatter_rows")
@@ -228,6 +325,7 @@ def usp_reduce_scatter_rows(partials, out, rank: int = -1, stream=None) -> None:
 def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
                       lse=None, stream=None) -> None:
     """Attention over heads [head_lo, head_hi) of q, k, v, o [B,S,h,D]."""
+    _attn_io(q, k, v, o, lse)
     B, S, h, D = q.shape
     hi = h if head_hi is None else head_hi
     _check(lib().usp_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B, S,
@@ -247,6 +345,7 @@ def usp_attention_fwd_ws(q, k, v, o, ws, head_lo: int = 0, head_hi=None, scale: 
                          lse=None, stream=None) -> None:
     """usp_attention_fwd with the caller's workspace tensor ``ws`` (any dtype;
     its byte size is passed; None for fp32 inputs)."""
+    _attn_io(q, k, v, o, lse, ws)
     B, S, h, D = q.shape
     hi = h if head_hi is None else head_hi
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -260,6 +359,7 @@ def usp_attention_fwd_gqa(q, k, v, o, head_lo: int = 0, head_hi=None, scale: flo
     """Attention over query heads [head_lo, head_hi) of q, o [B,S,h,D] with
     k, v [B,S,h_kv,D] (query head n uses K/V head n // (h // h_kv));
     ``ws`` an optional workspace tensor as for usp_attention_fwd_ws."""
+    _attn_io(q, k, v, o, lse, ws, kv_heads=_dims(k, "k", 4)[2])
     B, S, h, D = q.shape
     hi = h if head_hi is None else head_hi
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -274,6 +374,8 @@ def usp_attention_fwd_block(q, k, v, o, head_lo: int = 0, head_hi=None, scale: f
     block k, v [B,Sk,h_kv,D] for query heads [head_lo, head_hi); ``lse``
     fp32 [B,h,Sq] or None; ``ws`` an optional workspace tensor sized for
     Sq query rows."""
+    kd = _dims(k, "k", 4)
+    _attn_io(q, k, v, o, lse, ws, kv_rows=kd[1], kv_heads=kd[2])
     B, Sq, h, D = q.shape
     hi = h if head_hi is None else head_hi
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -288,7 +390,17 @@ def usp_attention_merge(o_a, lse_a, o_b, lse_b, o, lse=None, head_lo: int = 0, h
     """Log-sum-exp merge of (o_a, lse_a) and (o_b, lse_b) — fp32 [B,S,h,D]
     and [B,h,S] — into o (fp32 or bf16; may be o_a itself when fp32) and
     lse (may be lse_a itself, or None)."""
-    B, S, h, D = o_a.shape
+    torch = _torch()
+    B, S, h, D = _dims(o_a, "o_a", 4)
+    _need(o_a, "o_a", (B, S, h, D), (torch.float32,))
+    _need(o_b, "o_b", (B, S, h, D), (torch.float32,))
+    _need(lse_a, "lse_a", (B, h, S), (torch.float32,))
+    _need(lse_b, "lse_b", (B, h, S), (torch.float32,))
+    _need(o, "o", (B, S, h, D), (torch.float32, torch.bfloat16))
+    if lse is not None:
+        _need(lse, "lse", (B, h, S), (torch.float32,))
+    _on_gpu([("o_a", o_a), ("lse_a", lse_a), ("o_b", o_b), ("lse_b", lse_b), ("o", o),
+             ("lse", lse)])
     hi = h if head_hi is None else head_hi
     _check(lib().usp_attention_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o),
                                      _ptr(lse), _dtype(o), B, S, h, D, head_lo, hi,
@@ -298,6 +410,7 @@ def usp_attention_merge(o_a, lse_a, o_b, lse_b, o, lse=None, head_lo: int = 0, h
 def usp_attention_fwd_chunked(q, k, v, o, chunks: int, scale: float = 0.0, lse=None,
                               stream=None) -> None:
     """Attention as ``chunks`` head-chunk passes (bitwise equal to single shot)."""
+    _attn_io(q, k, v, o, lse)
     B, S, h, D = q.shape
     _check(lib().usp_attention_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
                                            _dtype(o), B, S, h, D, scale, _ptr(lse), chunks,
@@ -308,6 +421,7 @@ def usp_attention_fwd_chunked_ws(q, k, v, o, chunks: int, ws, scale: float = 0.0
                                  stream=None) -> None:
     """usp_attention_fwd_chunked with the caller's workspace tensor ``ws``
     (sized for ceil(h / chunks) heads; None for fp32 inputs)."""
+    _attn_io(q, k, v, o, lse, ws)
     B, S, h, D = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().usp_attention_fwd_chunked_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
