@@ -8,7 +8,8 @@ Sources:
     take the longer length; fewer items than parts, or fewer than one part,
     is an error.
   * m-star ``sequence_parallel`` API page, ``sp_seq_split``: per-rank token
-    counts summing to the total, earlier ranks taking the remainder.
+    counts summing to the total, the first total mod P ranks holding one extra
+    item.
   * maxdiffusion PR #428 "two-phase (head-chunked) Ulysses all-to-all",
     description: head-group passes, the final chunk carries the remainder.
 """

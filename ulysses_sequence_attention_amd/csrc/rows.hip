@@ -6,8 +6,8 @@
 //   reduce-scatter  h3-blackwell-runtime reduce_scatter_rows: rank r's rows
 //            of the sum of P partials of the full sequence, added in rank
 //            order.
-// Rows split over P ranks by the balanced ranges (earlier ranks take the
-// remainder). W * esize is a multiple of 16, so a row is a whole number of
+// Rows split over P ranks by the balanced ranges (the first S mod P ranks
+// hold one extra row). W * esize is a multiple of 16, so a row is a whole number of
 // 16-byte chunks and no chunk straddles two rows.
 //
 // Both kernels walk one side linearly in 16-byte chunks (fully coalesced)
