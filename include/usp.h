@@ -65,8 +65,8 @@ const char* usp_version(void);
  * Balanced contiguous ranges (h3-blackwell-runtime distributed.py,
  * balanced_ranges; m-star sp_seq_split): split `total` ordered items into
  * `parts` contiguous non-empty ranges; with base = total / parts and
- * extra = total % parts, range r has base + (r < extra) items, so earlier
- * ranks carry the remainder.
+ * extra = total % parts, range r has base + (r < extra) items: the first
+ * `extra` ranges hold one item more than the others.
  *   bounds: caller-owned host array of parts + 1 int64; on success
  *           bounds[0] = 0, bounds[parts] = total, range r = [bounds[r],
  *           bounds[r+1]).

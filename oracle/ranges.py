@@ -11,7 +11,7 @@ Sources:
     counts summing to the total, the first total mod P ranks holding one extra
     item.
   * maxdiffusion PR #428 "two-phase (head-chunked) Ulysses all-to-all",
-    description: head-group passes, the final chunk carries the remainder.
+    description: head-group passes, the last one taking the heads left over.
 """
 from __future__ import annotations
 
@@ -49,7 +49,7 @@ def head_chunk_ranges(heads: int, chunks: int) -> list[int]:
     """Boundaries of ``chunks`` head-chunk passes over ``heads`` local heads.
 
     maxdiffusion PR #428 splits the all-to-all plus attention into head-group
-    passes and lets the final chunk carry the remainder. Reading taken here:
+    passes, the last pass taking whatever heads are left. Reading taken here:
     every chunk but the last holds ``ceil(heads / chunks)`` heads and the last
     holds what is left (8 heads in 3 chunks: 3/3/2). A plan that would leave a
     chunk empty is rejected.
