@@ -216,7 +216,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not "
-              "supported (the multi-GPU exchange is not part of this build)", file=sys.stderr)
+              "supported: it runs on one GPU (the multi-GPU exchange is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import ulysses_sequence_attention_amd as usp

@@ -46,7 +46,7 @@ enum {
   USP_ESHAPE = -2, /* sizes are inconsistent or overflow */
   USP_EDTYPE = -3, /* element type not supported for this call */
   USP_EALIGN = -4, /* a pointer or row is not 16-byte aligned */
-  USP_ENOSYS = -5, /* a valid request this build has no kernel for */
+  USP_ENOSYS = -5, /* a valid request the library has no kernel for */
   USP_EHIP = -6    /* the HIP runtime reported an error */
 };
 

@@ -3,7 +3,7 @@
 Usage: ``python -m ulysses_sequence_attention_amd.build [--verbose]``.
 Compiles every ``csrc/*.hip`` with hipcc for gfx950 into ``_build/`` at the
 repository root and links ``ulysses_sequence_attention_amd/libusp.so``.
-Always recompiles (the build check must compile every time it is asked to).
+Always recompiles, also when a built library is already present.
 """
 from __future__ import annotations
 
