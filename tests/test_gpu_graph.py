@@ -1,0 +1,67 @@
+"""The hot path under HIP graph capture. The library never allocates or
+synchronizes and takes a caller workspace, so a whole step — pack of Q, K,
+V, attention of every head group, unpack — can be captured once and
+replayed. Each replay follows new inputs copied into the captured buffers
+and eager work on the device, and is compared bit for bit with the same step
+run eagerly."""
+import pytest
+
+import ulysses_sequence_attention_amd as usp
+from ulysses_sequence_attention_amd import synth
+
+from gpu_util import DEV, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_step_replays_from_a_captured_graph():
+    import torch
+    w = synth.WORKLOADS["vit_l16"]            # B=32, S=577, H=16, D=64, P=4
+    B, S, H, D, P = w.B, w.S, w.H, w.D, w.P
+    hb = usp.usp_balanced_ranges(H, P)
+    bf = torch.bfloat16
+    qkv = [torch.empty((B, S, H, D), dtype=bf, device=DEV) for _ in range(3)]
+    blocks = [[torch.empty((B, S, hb[j + 1] - hb[j], D), dtype=bf, device=DEV) for j in range(P)]
+              for _ in range(3)]
+    oblocks = [torch.empty((B, S, hb[j + 1] - hb[j], D), dtype=bf, device=DEV) for j in range(P)]
+    out = torch.empty((B, S, H, D), dtype=bf, device=DEV)
+    hmax = max(hb[j + 1] - hb[j] for j in range(P))
+    ws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, B, S, hmax, D) // 4,
+                     dtype=torch.float32, device=DEV)
+
+    def step():
+        for x, bl in zip(qkv, blocks):
+            usp.usp_pack_seq_to_heads(x, bl)
+        for j in range(P):
+            usp.usp_attention_fwd_ws(blocks[0][j], blocks[1][j], blocks[2][j], oblocks[j], ws)
+        usp.usp_unpack_heads_to_seq(oblocks, out)
+
+    def load(seed):
+        for dst, src in zip(qkv, synth.draw_qkv(B, S, H, D, seed)):
+            dst.copy_(to_dev(src, synth.BF16))
+
+    load(100)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):             # warm-up outside the capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    log("capture pack -> attention x4 -> unpack (ViT-L/16 world)")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i, seed in enumerate((101, 102, 103)):
+        load(seed)
+        junk = torch.randn(1024, 1024, device=DEV) @ torch.randn(1024, 1024, device=DEV)
+        log(f"graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        del junk
+        log(f"eager step {i}")
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), f"replay {i} differs from the eager step"
+        assert not torch.isnan(got.float()).any()
