@@ -1,11 +1,15 @@
 /*
  * A plain C consumer of libusp (include/usp.h) with the HIP runtime and no
  * other framework in the process: it checks that the boundary is usable as a
- * C ABI on its own. Numerical parity against the oracle is the Python tests'
- * job; this program checks what needs no reference: the stated range splits,
- * the pack -> unpack round trip bit for bit, the attention entry points that
- * must agree bit for bit (default, workspace, head-chunked), finite outputs,
- * and error codes with their messages. Exit status 0 when every check holds.
+ * C ABI on its own; every entry point of usp.h is called. Numerical parity
+ * against the oracle is the Python tests' job; this program checks what needs
+ * no reference: the stated range splits (host and device), the pack -> unpack
+ * and scatter -> gather round trips bit for bit, an exact reduce-scatter of
+ * equal integer partials, the attention entry points that must agree bit for
+ * bit (default, workspace, head-chunked with and without a workspace, grouped
+ * heads against block attention with equal lengths), a result merged with
+ * itself, finite outputs, and error codes with their messages. Exit status 0
+ * when every check holds.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -133,6 +137,11 @@ static void check_attention(void) {
   CHECK(usp_attention_fwd_chunked(qkv[0], qkv[1], qkv[2], o[2], USP_BF16, USP_F32, B, S, h, D, 0.0f,
                                   lse[2], 2, NULL) == USP_OK, "usp_attention_fwd_chunked");
   HIP_OK(hipDeviceSynchronize());
+  float* chunked_ws_out = (float*)dev_alloc(n * 4);
+  CHECK(usp_attention_fwd_chunked_ws(qkv[0], qkv[1], qkv[2], chunked_ws_out, USP_BF16, USP_F32, B, S,
+                                     h, D, 0.0f, NULL, 2, ws, ws_bytes, NULL) == USP_OK,
+        "usp_attention_fwd_chunked_ws");
+  HIP_OK(hipDeviceSynchronize());
   float* a = (float*)malloc(n * 4);
   float* b = (float*)malloc(n * 4);
   HIP_OK(hipMemcpy(a, o[0], n * 4, hipMemcpyDeviceToHost));
@@ -143,6 +152,9 @@ static void check_attention(void) {
     HIP_OK(hipMemcpy(b, o[r], n * 4, hipMemcpyDeviceToHost));
     CHECK(memcmp(a, b, n * 4) == 0, "attention path %d equals the default bit for bit", r);
   }
+  HIP_OK(hipMemcpy(b, chunked_ws_out, n * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(a, b, n * 4) == 0, "chunked attention with a workspace equals the default bit for bit");
+  HIP_OK(hipFree(chunked_ws_out));
   const size_t nl = (size_t)B * h * S;
   HIP_OK(hipMemcpy(a, lse[0], nl * 4, hipMemcpyDeviceToHost));
   for (int r = 1; r < 3; ++r) {
@@ -166,6 +178,123 @@ static void check_attention(void) {
   free(b);
 }
 
+static void check_device_ranges(void) {
+  int64_t* d = (int64_t*)dev_alloc(5 * 8);
+  int64_t h[5];
+  CHECK(usp_balanced_ranges_device(577, 4, d, NULL) == USP_OK, "device ranges");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(h, d, 5 * 8, hipMemcpyDeviceToHost));
+  CHECK(h[0] == 0 && h[1] == 145 && h[2] == 289 && h[3] == 433 && h[4] == 577,
+        "device ranges equal the host ones");
+  HIP_OK(hipFree(d));
+}
+
+/* small integers as fp32: sums of a few of them are exact */
+static void fill_small_ints(float* x, size_t n, uint32_t seed) {
+  uint32_t s = seed * 2654435761u + 7u;
+  for (size_t i = 0; i < n; ++i) {
+    s = s * 1664525u + 1013904223u;
+    x[i] = (float)((int)(s >> 27) - 16);
+  }
+}
+
+static void check_rows(void) {
+  enum { P = 3 };
+  const int64_t B = 2, S = 101, W = 64;
+  const size_t n = (size_t)B * S * W;
+  int64_t tb[P + 1];
+  CHECK(usp_balanced_ranges(S, P, tb) == USP_OK, "row ranges");
+  float* host = (float*)malloc(n * 4);
+  float* back = (float*)malloc(n * 4);
+  fill_small_ints(host, n, 3);
+  float* full = (float*)dev_alloc(n * 4);
+  float* full2 = (float*)dev_alloc(n * 4);
+  void* sh[P];
+  void* red[P];
+  const void* parts[P];
+  for (int r = 0; r < P; ++r) {
+    sh[r] = dev_alloc((size_t)B * (tb[r + 1] - tb[r]) * W * 4);
+    red[r] = dev_alloc((size_t)B * (tb[r + 1] - tb[r]) * W * 4);
+    parts[r] = full;  /* P copies of the same partial */
+  }
+  HIP_OK(hipMemcpy(full, host, n * 4, hipMemcpyHostToDevice));
+  CHECK(usp_scatter_rows(full, sh, USP_F32, B, S, W, P, -1, NULL) == USP_OK, "scatter");
+  CHECK(usp_gather_rows((const void* const*)sh, full2, USP_F32, B, S, W, P, NULL) == USP_OK, "gather");
+  CHECK(usp_reduce_scatter_rows(parts, red, USP_F32, B, S, W, P, -1, NULL) == USP_OK,
+        "reduce-scatter");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(back, full2, n * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(host, back, n * 4) == 0, "gather(scatter(x)) == x bit for bit");
+  int rs_ok = 1;
+  for (int r = 0; r < P; ++r) {
+    const int64_t len = tb[r + 1] - tb[r];
+    float* got = (float*)malloc((size_t)B * len * W * 4);
+    HIP_OK(hipMemcpy(got, red[r], (size_t)B * len * W * 4, hipMemcpyDeviceToHost));
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t i = 0; i < len * W; ++i)
+        rs_ok &= got[b * len * W + i] == (float)P * host[(b * S + tb[r]) * W + i];
+    free(got);
+  }
+  CHECK(rs_ok, "reduce-scatter of P equal integer partials is P times the rows, exactly");
+  for (int r = 0; r < P; ++r) {
+    HIP_OK(hipFree(sh[r]));
+    HIP_OK(hipFree(red[r]));
+  }
+  HIP_OK(hipFree(full));
+  HIP_OK(hipFree(full2));
+  free(host);
+  free(back);
+}
+
+static void check_block_and_merge(void) {
+  const int64_t B = 1, S = 300;
+  const int32_t h = 4, hkv = 2, D = 64;
+  const size_t nq = (size_t)B * S * h * D, nk = (size_t)B * S * hkv * D, nl = (size_t)B * h * S;
+  uint16_t* host = (uint16_t*)malloc(nq * 2);
+  void *q = dev_alloc(nq * 2), *k = dev_alloc(nk * 2), *v = dev_alloc(nk * 2);
+  fill_bf16(host, nq, 21);
+  HIP_OK(hipMemcpy(q, host, nq * 2, hipMemcpyHostToDevice));
+  fill_bf16(host, nk, 22);
+  HIP_OK(hipMemcpy(k, host, nk * 2, hipMemcpyHostToDevice));
+  fill_bf16(host, nk, 23);
+  HIP_OK(hipMemcpy(v, host, nk * 2, hipMemcpyHostToDevice));
+  float *o1 = (float*)dev_alloc(nq * 4), *o2 = (float*)dev_alloc(nq * 4), *o3 = (float*)dev_alloc(nq * 4);
+  float *l1 = (float*)dev_alloc(nl * 4), *l2 = (float*)dev_alloc(nl * 4), *l3 = (float*)dev_alloc(nl * 4);
+  CHECK(usp_attention_fwd_gqa(q, k, v, o1, USP_BF16, USP_F32, B, S, h, hkv, D, 0, h, 0.0f, l1, NULL,
+                              0, NULL) == USP_OK, "usp_attention_fwd_gqa");
+  CHECK(usp_attention_fwd_block(q, k, v, o2, USP_BF16, USP_F32, B, S, S, h, hkv, D, 0, h, 0.0f, l2,
+                                NULL, 0, NULL) == USP_OK, "usp_attention_fwd_block");
+  /* a result merged with itself: weights 1/2 each, so O comes back exactly */
+  CHECK(usp_attention_merge(o2, l2, o2, l2, o3, l3, USP_F32, B, S, h, D, 0, h, NULL) == USP_OK,
+        "usp_attention_merge");
+  HIP_OK(hipDeviceSynchronize());
+  float* a = (float*)malloc(nq * 4);
+  float* b = (float*)malloc(nq * 4);
+  HIP_OK(hipMemcpy(a, o1, nq * 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(b, o2, nq * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(a, b, nq * 4) == 0, "block attention with Sq = Sk equals the grouped call bit for bit");
+  HIP_OK(hipMemcpy(a, o3, nq * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(a, b, nq * 4) == 0, "merging a result with itself returns it exactly");
+  HIP_OK(hipMemcpy(a, l2, nl * 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(b, l3, nl * 4, hipMemcpyDeviceToHost));
+  int lse_ok = 1;
+  for (size_t i = 0; i < nl; ++i) lse_ok &= fabsf(b[i] - (a[i] + 0.69314718f)) <= 2e-6f * (1.0f + fabsf(a[i]));
+  CHECK(lse_ok, "merging a result with itself adds log 2 to lse");
+  void* pq = q;
+  HIP_OK(hipFree(pq));
+  HIP_OK(hipFree(k));
+  HIP_OK(hipFree(v));
+  HIP_OK(hipFree(o1));
+  HIP_OK(hipFree(o2));
+  HIP_OK(hipFree(o3));
+  HIP_OK(hipFree(l1));
+  HIP_OK(hipFree(l2));
+  HIP_OK(hipFree(l3));
+  free(host);
+  free(a);
+  free(b);
+}
+
 int main(void) {
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
@@ -174,8 +303,11 @@ int main(void) {
   }
   printf("%s\n", usp_version());
   check_ranges();
+  check_device_ranges();
   check_relayout();
+  check_rows();
   check_attention();
+  check_block_and_merge();
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;
