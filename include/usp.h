@@ -63,8 +63,9 @@ const char* usp_version(void);
 
 /*
  * Balanced contiguous ranges (h3-blackwell-runtime distributed.py,
- * balanced_ranges; m-star sp_seq_split): split `total` ordered items into
- * `parts` contiguous non-empty ranges; with base = total / parts and
+ * balanced_ranges; m-star sp_seq_split): cut the item indices
+ * 0 .. total-1 into `parts` consecutive runs of at least one item; with
+ * base = total / parts and
  * extra = total % parts, range r has base + (r < extra) items: the first
  * `extra` ranges hold one item more than the others.
  *   bounds: caller-owned host array of parts + 1 int64; on success
@@ -148,9 +149,9 @@ int usp_scatter_rows(const void* full, void* const* shards, usp_dtype dtype, int
 
 /*
  * usp_gather_rows (m-star gather_sequence, h3-blackwell-runtime
- * SequenceParallelContext.all_gather_rows: the rank shards back into the
- * full tensor in rank order, padding never visible): full[b][t_r + i] =
- * shards[r][b][i] for every r.
+ * SequenceParallelContext.all_gather_rows: the P shards laid end to end in
+ * rank order rebuild the unsharded tensor, with no padding rows):
+ * full[b][t_r + i] = shards[r][b][i] for every r.
  */
 int usp_gather_rows(const void* const* shards, void* full, usp_dtype dtype, int64_t B, int64_t S,
                     int64_t W, int32_t P, void* stream);

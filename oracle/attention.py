@@ -1,11 +1,11 @@
 """Non-causal multi-head attention, float64 (oracle; test infrastructure).
 
 What the pages define: m-star ``sequence_parallel`` module description and
-``ulysses_attention`` — attention is the one operator that needs the whole
-sequence; under Ulysses each rank runs the unchanged attention kernel over the
-full sequence for its own group of heads, and heads are independent of one
-another (maxdiffusion PR #428 description: head-chunked passes are
-mathematically the single-shot result because heads are independent). The
+``ulysses_attention`` — of the model's steps only attention mixes
+information across all tokens; under Ulysses each rank runs the unchanged
+attention kernel over the full sequence for its own group of heads, and no
+head reads another head's data (maxdiffusion PR #428 description: for that
+reason head-chunked passes give exactly the single-shot result). The
 kernel itself is opaque on the pages; what it computes is taken as standard
 scaled dot-product attention, non-causal, per head:
 
@@ -15,7 +15,7 @@ with sigma = 1/sqrt(D) unless another scale is given (the pages never state
 the scale; 1/sqrt(D) is the standard choice).
 
 Grouped K/V heads (m-star ``ulysses_attention``: q has Hq heads, k and v Hkv,
-both divisible by the SP degree): query head n attends with key/value head
+the SP degree dividing both): query head n attends with key/value head
 floor(n / G), G = Hq / Hkv, i.e. each run of G consecutive query heads shares
 one K/V head. The pages do not spell out the mapping; this is the one under
 which contiguous head sharding keeps every rank's query heads with its own

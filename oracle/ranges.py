@@ -2,36 +2,37 @@
 
 Sources:
   * h3-blackwell-runtime ``distributed.py`` (blame view), function
-    ``balanced_ranges``: split ``total`` ordered items into ``parts``
-    contiguous, non-empty ranges whose lengths are ``base`` or ``base + 1``
-    with ``base, extra = divmod(total, parts)``; the first ``extra`` ranks
-    take the longer length; fewer items than parts, or fewer than one part,
-    is an error.
-  * m-star ``sequence_parallel`` API page, ``sp_seq_split``: per-rank token
-    counts summing to the total, the first total mod P ranks holding one extra
-    item.
+    ``balanced_ranges``: the items, in order, go to ``parts`` consecutive
+    runs, none of them empty; every run has ``q = total // parts`` items and
+    the lowest ``total % parts`` runs one more; asking for no runs at all,
+    or for more runs than items, raises an error.
+  * m-star ``sequence_parallel`` API page, ``sp_seq_split``: how many tokens
+    each rank gets; the counts add up to the sequence length and differ by
+    at most one, the first total mod P ranks holding the extra token.
   * maxdiffusion PR #428 "two-phase (head-chunked) Ulysses all-to-all",
-    description: head-group passes, the last one taking the heads left over.
+    description: one pass per group of heads, the last one taking the heads
+    left over.
 """
 from __future__ import annotations
+
+import itertools
 
 
 def balanced_ranges(total: int, parts: int) -> list[int]:
     """Boundaries ``[b_0 = 0, b_1, ..., b_parts = total]``; range r is
     ``[b_r, b_{r+1})``.
 
-    h3-blackwell-runtime ``distributed.py``, ``balanced_ranges``.
+    h3-blackwell-runtime ``distributed.py``, ``balanced_ranges``: the
+    lowest ``total % parts`` runs hold ``q + 1`` items, the others ``q``;
+    the boundaries are the running sums of those sizes.
     """
     if parts < 1:
-        raise ValueError("parts must be positive")
+        raise ValueError(f"need at least one range (got {parts})")
     if total < parts:
-        raise ValueError(f"cannot split {total} items into {parts} non-empty ranges")
-    base, extra = divmod(total, parts)
-    bounds = [0]
-    for rank in range(parts):
-        length = base + (1 if rank < extra else 0)
-        bounds.append(bounds[-1] + length)
-    return bounds
+        raise ValueError(f"{total} items are too few for {parts} ranges of one item or more")
+    q, longer = total // parts, total % parts
+    sizes = [q + 1] * longer + [q] * (parts - longer)
+    return [0] + list(itertools.accumulate(sizes))
 
 
 def range_lengths(bounds: list[int]) -> list[int]:
@@ -48,8 +49,9 @@ def seq_split(total: int, world_size: int) -> list[int]:
 def head_chunk_ranges(heads: int, chunks: int) -> list[int]:
     """Boundaries of ``chunks`` head-chunk passes over ``heads`` local heads.
 
-    maxdiffusion PR #428 splits the all-to-all plus attention into head-group
-    passes, the last pass taking whatever heads are left. Reading taken here:
+    maxdiffusion PR #428 runs the exchange and the attention once per group
+    of heads, in turn; an uneven count leaves the last group short. Reading
+    taken here:
     every chunk but the last holds ``ceil(heads / chunks)`` heads and the last
     holds what is left (8 heads in 3 chunks: 3/3/2). A plan that would leave a
     chunk empty is rejected.

@@ -1,10 +1,11 @@
 """Sequence-sharded <-> head-sharded relayouts (oracle; test infrastructure).
 
 What the pages define:
-  * m-star ``sequence_parallel`` module description: around attention, the
-    first all-to-all turns a sequence-sharded ``[seq/P, heads, dim]`` tensor
-    into a head-sharded ``[seq, heads/P, dim]`` one and the second turns it
-    back.
+  * m-star ``sequence_parallel`` module description: before attention an
+    all-to-all converts each rank's token shard, shape ``[seq/P, heads,
+    dim]``, into all tokens over the rank's own head group, shape ``[seq,
+    heads/P, dim]``; after attention a second all-to-all converts the output
+    the opposite way.
   * h3-blackwell-runtime ``distributed.py``, ``SequenceParallelContext.
     seq_to_heads``: rank r sends, to each rank j, its own token rows restricted
     to j's head range; rank j concatenates what it receives in source-rank

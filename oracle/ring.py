@@ -87,12 +87,12 @@ def ulysses_ring_world(q, k, v, U: int, R: int, scale=None):
     the sequence by balanced ranges; inside ring block r, pack (U parts) ->
     for each head group j, ring attention of block r's queries over all R
     blocks' keys of group j (order :func:`ring_order`) -> unpack. Returns
-    ``O [B, S, H, D]`` float64. With grouped K/V heads both head counts
-    must be divisible by U."""
+    ``O [B, S, H, D]`` float64. With grouped K/V heads U has to divide
+    H and Hkv."""
     B, S, H, D = q.shape
     Hkv = k.shape[2]
     if Hkv != H and (H % U or Hkv % U or H % Hkv):
-        raise ValueError(f"grouped heads need H ({H}) and Hkv ({Hkv}) divisible by U ({U})")
+        raise ValueError(f"grouped heads: U ({U}) has to divide H ({H}) and Hkv ({Hkv})")
     T = balanced_ranges(S, R)
     # ring group r's Ulysses blocks: qb[r][j] = [B, S_r, h_j, D]
     qb = [relayout.pack_seq_to_heads(q[:, T[r]:T[r + 1]], U) for r in range(R)]

@@ -5,8 +5,8 @@ first all-to-all makes each rank hold the full sequence over its head group,
 attention runs locally, the second all-to-all returns to the sequence shard;
 the result is the attention of the unsharded tensor. maxdiffusion PR #428
 description: the head-chunked two-phase variant runs the exchange plus
-attention over head sub-groups in turn, and is mathematically identical to
-the single-shot path because heads are independent.
+attention over head sub-groups in turn; since no head's attention reads
+another head's data, it gives exactly the single-shot result.
 """
 from __future__ import annotations
 
@@ -23,12 +23,12 @@ def ulysses_world(q, k, v, P: int, scale=None, attn=attention):
     ``attn`` maps ``(q_blk, k_blk, v_blk) -> o_blk`` for one block
     ``[B, S, h_j, D]``; it defaults to the oracle attention (a layout-only
     mock such as ``lambda q, k, v: v`` isolates the relayouts). With grouped
-    K/V heads (k, v ``[B, S, Hkv, D]``, Hkv < H) both head counts must be
-    divisible by P, so that block j's query heads share block j's K/V heads
+    K/V heads (k, v ``[B, S, Hkv, D]``, Hkv < H) P has to divide H and Hkv,
+    so that block j's query heads share block j's K/V heads
     (m-star ``ulysses_attention``)."""
     H, Hkv = q.shape[2], k.shape[2]
     if Hkv != H and (H % P or Hkv % P or H % Hkv):
-        raise ValueError(f"grouped heads need H ({H}) and Hkv ({Hkv}) divisible by P ({P})")
+        raise ValueError(f"grouped heads: P ({P}) has to divide H ({H}) and Hkv ({Hkv})")
     qb = relayout.pack_seq_to_heads(q, P)
     kb = relayout.pack_seq_to_heads(k, P)
     vb = relayout.pack_seq_to_heads(v, P)

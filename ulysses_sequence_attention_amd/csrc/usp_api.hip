@@ -37,9 +37,9 @@ int check_launch(const char* what) {
 // balanced_ranges): base = total / parts, the first total % parts ranges take
 // one extra item.
 static int check_ranges(int64_t total, int32_t parts) {
-  if (parts < 1) return fail(USP_EINVAL, "parts must be positive (got %d)", parts);
+  if (parts < 1) return fail(USP_EINVAL, "need at least one range (got %d)", parts);
   if (total < parts)
-    return fail(USP_EINVAL, "cannot split %lld items into %d non-empty ranges",
+    return fail(USP_EINVAL, "%lld items are too few for %d ranges of one item or more",
                 (long long)total, parts);
   return USP_OK;
 }
