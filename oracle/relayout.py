@@ -124,6 +124,62 @@ def pack_seq_to_heads_elementwise(seq: np.ndarray, P: int) -> list[np.ndarray]:
     return blocks
 
 
+def _chunk_plan(S: int, H: int, P: int, lo: int, hi: int):
+    """Token ranges and the per-group head count for a head-chunk relayout;
+    the chunk ``[lo, hi)`` indexes heads within each (equal) group."""
+    if H % P:
+        raise ValueError(f"head-chunk relayouts need equal head groups: P ({P}) has to divide H ({H})")
+    h = H // P
+    if not 0 <= lo < hi <= h:
+        raise ValueError(f"head chunk [{lo}, {hi}) is empty or outside a group of {h} heads")
+    return balanced_ranges(S, P), balanced_ranges(H, P)
+
+
+def pack_heads_chunk(src: np.ndarray, blocks: list[np.ndarray], S: int, lo: int, hi: int,
+                     rank: int | None = None) -> None:
+    """One phase of the head-chunked exchange, pack side (in place).
+
+    maxdiffusion PR #428 (description): the exchange and the attention run
+    once per chunk of every rank's heads, so only heads ``[lo, hi)`` of each
+    group move in a phase. With equal groups of h = H / P heads, block j
+    receives ``block_j[b, t, i, :] = seq[b, t, c_j + i, :]`` for ``lo <= i <
+    hi`` and every row t (world, ``src`` = ``seq[B, S, H, D]``) or only rows
+    ``[t_r, t_{r+1})`` (rank r's share, ``src`` = its shard ``[B, len_r, H,
+    D]``); nothing else in the blocks is written.
+    """
+    P = len(blocks)
+    B, L, H, D = src.shape
+    tb, hb = _chunk_plan(S, H, P, lo, hi)
+    t0 = 0 if rank is None else tb[rank]
+    if L != (S if rank is None else tb[rank + 1] - tb[rank]):
+        raise ValueError(f"source has {L} rows, expected {S if rank is None else tb[rank + 1] - tb[rank]}")
+    for j in range(P):
+        for b in range(B):
+            for s in range(L):
+                for i in range(lo, hi):
+                    blocks[j][b, t0 + s, i, :] = src[b, s, hb[j] + i, :]
+
+
+def unpack_heads_chunk(blocks: list[np.ndarray], dst: np.ndarray, S: int, lo: int, hi: int,
+                       rank: int | None = None) -> None:
+    """Unpack side of one head-chunk phase (in place): heads ``[lo, hi)`` of
+    every block go back to their place among all heads,
+    ``dst[b, s, c_j + i, :] = block_j[b, t0 + s, i, :]`` (world: ``dst`` =
+    ``[B, S, H, D]``, t0 = 0; rank r's share: ``dst`` = ``[B, len_r, H, D]``,
+    t0 = t_r); other heads of ``dst`` are not written."""
+    P = len(blocks)
+    B, L, H, D = dst.shape
+    tb, hb = _chunk_plan(S, H, P, lo, hi)
+    t0 = 0 if rank is None else tb[rank]
+    if L != (S if rank is None else tb[rank + 1] - tb[rank]):
+        raise ValueError(f"destination has {L} rows, expected {S if rank is None else tb[rank + 1] - tb[rank]}")
+    for j in range(P):
+        for b in range(B):
+            for s in range(L):
+                for i in range(lo, hi):
+                    dst[b, s, hb[j] + i, :] = blocks[j][b, t0 + s, i, :]
+
+
 def scatter_sequence(x_full: np.ndarray, P: int, rank: int) -> np.ndarray:
     """m-star ``scatter_sequence``: rank r's contiguous window of tokens
     (axis 1) of a replicated ``[B, S, ...]`` tensor."""

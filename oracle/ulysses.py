@@ -6,7 +6,9 @@ attention runs locally, the second all-to-all returns to the sequence shard;
 the result is the attention of the unsharded tensor. maxdiffusion PR #428
 description: the head-chunked two-phase variant runs the exchange plus
 attention over head sub-groups in turn; since no head's attention reads
-another head's data, it gives exactly the single-shot result.
+another head's data, it gives exactly the single-shot result. Both forms are
+here: ``attention_chunked`` (the passes over one block) and
+``ulysses_two_phase_world`` (the exchange itself in per-chunk phases).
 """
 from __future__ import annotations
 
@@ -37,6 +39,34 @@ def ulysses_world(q, k, v, P: int, scale=None, attn=attention):
     else:
         ob = [attn(qb[j], kb[j], vb[j]) for j in range(P)]
     return relayout.unpack_heads_to_seq(ob, H)
+
+
+def ulysses_two_phase_world(q, k, v, P: int, chunks: int, scale=None, attn=attention):
+    """The head-chunked two-phase exchange on world layouts (maxdiffusion PR
+    #428 description): for each chunk ``[k_c, k_{c+1})`` of the plan over a
+    group's h = H / P heads, in turn, pack those heads of q, k and v into the
+    head blocks, run ``attn`` on those heads of every block, and unpack them
+    from the output blocks. Returns ``O [B, S, H, D]``. Needs equal head
+    groups and plain multi-head attention (one K/V head per query head)."""
+    B, S, H, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("the two-phase composition takes q, k, v of one shape")
+    if H % P:
+        raise ValueError(f"head chunks need equal head groups: P ({P}) has to divide H ({H})")
+    h = H // P
+    kc = head_chunk_ranges(h, chunks)
+    qb, kb, vb, ob = ([np.zeros((B, S, h, D), dtype=np.float64) for _ in range(P)]
+                      for _ in range(4))
+    out = np.zeros((B, S, H, D), dtype=np.float64)
+    for c in range(chunks):
+        lo, hi = kc[c], kc[c + 1]
+        for x, xb in ((q, qb), (k, kb), (v, vb)):
+            relayout.pack_heads_chunk(np.asarray(x, dtype=np.float64), xb, S, lo, hi)
+        for j in range(P):
+            part = (qb[j][:, :, lo:hi], kb[j][:, :, lo:hi], vb[j][:, :, lo:hi])
+            ob[j][:, :, lo:hi] = attention(*part, scale=scale) if attn is attention else attn(*part)
+        relayout.unpack_heads_chunk(ob, out, S, lo, hi)
+    return out
 
 
 def attention_chunked(q, k, v, chunks: int, scale=None):

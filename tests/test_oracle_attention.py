@@ -161,6 +161,32 @@ def test_chunked_equals_single_shot(h):
         assert np.array_equal(out, ref)
 
 
+@pytest.mark.parametrize("B,S,H,D,P,chunks", [(1, 10, 6, 4, 3, 2), (2, 9, 15, 3, 3, 3),
+                                              (1, 13, 16, 2, 2, 3), (1, 8, 3, 4, 1, 2)])
+def test_two_phase_exchange_equals_single_shot(B, S, H, D, P, chunks):
+    # the head-chunked exchange (per-chunk pack -> attention -> unpack) gives
+    # the single-shot Ulysses result bit for bit and the single-device result
+    q, k, v = (_rand((B, S, H, D), i + 20) for i in range(3))
+    out = U.ulysses_two_phase_world(q, k, v, P, chunks)
+    assert np.array_equal(out, U.ulysses_world(q, k, v, P))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))).permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_two_phase_identity_mock_and_errors():
+    q, k, v = (_rand((2, 9, 12, 3), i) for i in range(3))
+    for chunks in (1, 2, 4):                   # groups of 4 heads: 4, 2/2, 1/1/1/1
+        out = U.ulysses_two_phase_world(q, k, v, 3, chunks, attn=lambda a, b, c: c)
+        assert np.array_equal(out, v)
+    out = U.ulysses_two_phase_world(q, k, v, 3, 2, attn=lambda a, b, c: a + 2 * c)
+    assert np.array_equal(out, q + 2 * v)      # elementwise mock: every head back in place
+    with pytest.raises(ValueError, match="equal head groups"):
+        U.ulysses_two_phase_world(*(_rand((1, 5, 7, 2), i) for i in range(3)), 3, 1)
+    with pytest.raises(ValueError, match="one shape"):
+        U.ulysses_two_phase_world(q, k[:, :, :3], v[:, :, :3], 3, 1)
+
+
 # ---- grouped K/V heads (Hkv < Hq): query head n uses K/V head n // (Hq / Hkv)
 
 @pytest.mark.parametrize("B,S,h,hkv,D,seed", [(1, 5, 4, 2, 3, 7), (2, 7, 6, 1, 2, 8),

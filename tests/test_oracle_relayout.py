@@ -145,3 +145,92 @@ def test_reduce_scatter_ranges_tile_the_sum():
 def test_reduce_scatter_rejects_mismatched_partials():
     with pytest.raises(ValueError):
         X.reduce_scatter_rows([np.zeros((1, 8, 2)), np.zeros((1, 7, 2))], 0)
+
+
+# ---- head-chunk phases of the two-phase exchange ----------------------------
+CHUNK_SHAPES = [  # B, S, H, D, P, chunks (equal head groups of h = H / P)
+    (1, 7, 6, 4, 3, 2),     # h = 2: chunks 1/1
+    (2, 9, 15, 2, 3, 3),    # h = 5: 2/2/1, ragged tokens 3/3/3 -> remainder chunk
+    (1, 9, 16, 3, 2, 3),    # h = 8: 3/3/2
+    (3, 5, 5, 2, 5, 1),     # one head per group, one chunk
+    (1, 6, 3, 2, 1, 2),     # P = 1, h = 3: 2/1
+]
+
+
+def _chunks(h, chunks):
+    # the plan, restated: ceil(h / chunks) heads per chunk, the last one short
+    size = -(-h // chunks)
+    return [(c * size, min((c + 1) * size, h)) for c in range(chunks)]
+
+
+@pytest.mark.parametrize("B,S,H,D,P,chunks", CHUNK_SHAPES)
+def test_chunk_packs_fill_the_blocks_chunk_by_chunk(B, S, H, D, P, chunks):
+    seq = synth.index_coded((B, S, H, D), "f32")
+    groups = _heads_groups(H, P)
+    h = H // P
+    blocks = [np.full((B, S, h, D), -1.0, np.float32) for _ in range(P)]
+    done = set()
+    for lo, hi in _chunks(h, chunks):
+        before = [b.copy() for b in blocks]
+        X.pack_heads_chunk(seq, blocks, S, lo, hi)
+        for j in range(P):
+            changed = set(np.nonzero(np.any(blocks[j] != before[j], axis=(0, 1, 3)))[0].tolist())
+            assert changed == set(range(lo, hi))          # its heads, all rows
+        done |= set(range(lo, hi))
+    assert done == set(range(h))
+    for j in range(P):                                     # closed form of every element
+        for b in range(B):
+            for s in range(S):
+                for i, head in enumerate(groups[j]):
+                    assert np.all(blocks[j][b, s, i] == ((b * S + s) * H + head) * D + np.arange(D))
+
+
+@pytest.mark.parametrize("B,S,H,D,P,chunks", CHUNK_SHAPES)
+def test_chunk_unpacks_rebuild_the_sequence_chunk_by_chunk(B, S, H, D, P, chunks):
+    seq = synth.index_coded((B, S, H, D), "bf16")
+    blocks = np.array_split(seq, P, axis=2)               # head blocks from a library split
+    out = np.zeros_like(seq)
+    h = H // P
+    for lo, hi in _chunks(h, chunks):
+        before = out.copy()
+        X.unpack_heads_chunk(blocks, out, S, lo, hi)
+        heads = set(np.nonzero(np.any(out != before, axis=(0, 1, 3)))[0].tolist())
+        assert heads <= {j * h + i for j in range(P) for i in range(lo, hi)}
+    assert out.tobytes() == seq.tobytes()
+
+
+@pytest.mark.parametrize("B,S,H,D,P,chunks", CHUNK_SHAPES)
+def test_chunk_rank_shares_tile_the_world(B, S, H, D, P, chunks):
+    seq = synth.index_coded((B, S, H, D), "f32")
+    world = np.array_split(seq, P, axis=2)
+    tok = np.array_split(np.arange(S), P)
+    h = H // P
+    blocks = [np.full((B, S, h, D), -1.0, np.float32) for _ in range(P)]
+    for lo, hi in _chunks(h, chunks):
+        for r in range(P):
+            before = [b.copy() for b in blocks]
+            X.pack_heads_chunk(seq[:, tok[r]], blocks, S, lo, hi, rank=r)
+            for j in range(P):
+                rows = set(np.nonzero(np.any(blocks[j] != before[j], axis=(0, 2, 3)))[0].tolist())
+                assert rows <= set(tok[r].tolist())
+    for j in range(P):
+        assert np.array_equal(blocks[j], world[j])
+    for r in range(P):
+        shard = np.zeros((B, len(tok[r]), H, D), np.float32)
+        for lo, hi in _chunks(h, chunks):
+            X.unpack_heads_chunk(world, shard, S, lo, hi, rank=r)
+        assert np.array_equal(shard, seq[:, tok[r]])
+
+
+def test_chunk_relayouts_reject_bad_plans():
+    seq = synth.index_coded((1, 6, 6, 2), "f32")
+    blocks = [np.zeros((1, 6, 2, 2), np.float32) for _ in range(3)]
+    with pytest.raises(ValueError, match="equal head groups"):
+        X.pack_heads_chunk(synth.index_coded((1, 6, 7, 2), "f32"), blocks, 6, 0, 1)
+    for lo, hi in [(0, 0), (1, 3), (-1, 1), (2, 1)]:
+        with pytest.raises(ValueError, match="head chunk"):
+            X.pack_heads_chunk(seq, blocks, 6, lo, hi)
+        with pytest.raises(ValueError, match="head chunk"):
+            X.unpack_heads_chunk(blocks, np.zeros_like(seq), 6, lo, hi)
+    with pytest.raises(ValueError, match="rows"):
+        X.pack_heads_chunk(seq[:, :3], blocks, 6, 0, 1, rank=0)   # rank 0 holds 2 rows
