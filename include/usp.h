@@ -129,6 +129,33 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
                             void* stream);
 
 /*
+ * One phase of the head-chunked (two-phase) exchange (maxdiffusion PR #428,
+ * "two-phase (head-chunked) Ulysses all-to-all", description: the exchange
+ * and the attention run once per chunk of every rank's heads, so that one
+ * chunk's exchange can overlap another chunk's attention). With P equal head
+ * groups of h = H / P heads (c_j = j * h), only heads [head_lo, head_hi) of
+ * every group move; the chunk plan over h comes from usp_head_chunk_ranges.
+ *   usp_pack_seq_to_heads_chunk, for head_lo <= i < head_hi:
+ *     rank < 0: blk[j][b][s][i][d] = seq[b][s][c_j + i][d] for all rows;
+ *     rank = r: blk[j][b][t_r + s][i][d] = seq[b][s][c_j + i][d] (seq = r's
+ *               shard [B][len_r][H][D]).
+ *   usp_unpack_heads_to_seq_chunk: the inverse for the same heads and rows.
+ * Nothing outside those heads (and, for rank >= 0, those rows) is read from
+ * the source or written to the destination, so a tensor's phases may run in
+ * any order or overlap each other's and other chunks' work; over a whole
+ * chunk plan they give exactly usp_pack_seq_to_heads / usp_unpack_heads_to_seq.
+ * Arguments, layouts and errors as usp_pack_seq_to_heads, plus: H not a
+ * multiple of P (ragged head groups), or [head_lo, head_hi) empty or outside
+ * [0, H / P) -> USP_EINVAL.
+ */
+int usp_pack_seq_to_heads_chunk(const void* seq, void* const* blk, usp_dtype dtype, int64_t B,
+                                int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                                int32_t head_lo, int32_t head_hi, void* stream);
+int usp_unpack_heads_to_seq_chunk(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
+                                  int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                                  int32_t head_lo, int32_t head_hi, void* stream);
+
+/*
  * Ragged token rows at the model boundary, without padding. A tensor
  * [B][S][W] (W = elements per token row, e.g. H * D) is split along S into
  * P contiguous balanced ranges [t_r, t_{r+1}) (usp_balanced_ranges(S, P));

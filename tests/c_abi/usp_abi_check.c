@@ -109,6 +109,59 @@ static void check_relayout(void) {
   free(back);
 }
 
+/* The two-phase exchange: pack and unpack one head chunk at a time (equal
+ * head groups of 3 heads, plan 2/1) rebuild the tensor bit for bit, and each
+ * pack phase leaves the other heads of a block as they were. */
+static void check_relayout_chunks(void) {
+  const int64_t B = 2, S = 203;
+  const int32_t H = 12, D = 64, P = 4, h = H / P;
+  const size_t n = (size_t)B * S * H * D, nb = (size_t)B * S * h * D;
+  uint16_t* host = (uint16_t*)malloc(n * 2);
+  uint16_t* back = (uint16_t*)malloc(n * 2);
+  uint16_t* hblk = (uint16_t*)malloc(nb * 2);
+  fill_bf16(host, n, 11);
+  int32_t kc[3];
+  CHECK(usp_head_chunk_ranges(h, 2, kc) == USP_OK && kc[1] == 2 && kc[2] == 3, "chunk plan 2/1");
+  void* seq = dev_alloc(n * 2);
+  void* out = dev_alloc(n * 2);
+  void* blk[P];
+  for (int j = 0; j < P; ++j) {
+    blk[j] = dev_alloc(nb * 2);
+    HIP_OK(hipMemset(blk[j], 0xff, nb * 2));
+  }
+  HIP_OK(hipMemcpy(seq, host, n * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemset(out, 0xff, n * 2));
+  CHECK(usp_pack_seq_to_heads_chunk(seq, blk, USP_BF16, B, S, H, D, P, -1, kc[0], kc[1], NULL) ==
+            USP_OK, "pack chunk 0");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(hblk, blk[3], nb * 2, hipMemcpyDeviceToHost));
+  int ok_first = 1;
+  for (size_t row = 0; row < (size_t)B * S; ++row)
+    for (int i = 0; i < h; ++i)
+      for (int d = 0; d < D; ++d) {
+        const uint16_t got = hblk[(row * h + i) * D + d];
+        const uint16_t want = i < kc[1] ? host[(row * H + 3 * h + i) * D + d] : 0xffff;
+        ok_first &= got == want;
+      }
+  CHECK(ok_first, "first phase: its heads moved, the others untouched");
+  CHECK(usp_pack_seq_to_heads_chunk(seq, blk, USP_BF16, B, S, H, D, P, -1, kc[1], kc[2], NULL) ==
+            USP_OK, "pack chunk 1");
+  for (int c = 0; c < 2; ++c)
+    CHECK(usp_unpack_heads_to_seq_chunk((const void* const*)blk, out, USP_BF16, B, S, H, D, P, -1,
+                                        kc[c], kc[c + 1], NULL) == USP_OK, "unpack chunk");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(back, out, n * 2, hipMemcpyDeviceToHost));
+  CHECK(memcmp(host, back, n * 2) == 0, "chunk phases: unpack(pack(x)) == x bit for bit");
+  CHECK(usp_pack_seq_to_heads_chunk(seq, blk, USP_BF16, B, S, 10, D, P, -1, 0, 1, NULL) ==
+            USP_EINVAL && strlen(usp_last_error()) > 0, "ragged head groups rejected");
+  for (int j = 0; j < P; ++j) HIP_OK(hipFree(blk[j]));
+  HIP_OK(hipFree(seq));
+  HIP_OK(hipFree(out));
+  free(host);
+  free(back);
+  free(hblk);
+}
+
 static void check_attention(void) {
   const int64_t B = 1, S = 700;
   const int32_t h = 3, D = 128;
@@ -305,6 +358,7 @@ int main(void) {
   check_ranges();
   check_device_ranges();
   check_relayout();
+  check_relayout_chunks();
   check_rows();
   check_attention();
   check_block_and_merge();

@@ -82,6 +82,30 @@ def test_relayout_rejects(fn, kw, status):
     assert usp.usp_last_error()
 
 
+def _pack_chunk(seq=FAKE, blk=(FAKE, FAKE), dt=1, B=1, S=8, H=4, D=64, P=2, rank=-1, lo=0, hi=1):
+    arr = (ctypes.c_void_p * max(len(blk), 1))(*blk)
+    return L.usp_pack_seq_to_heads_chunk(seq, arr, dt, B, S, H, D, P, rank, lo, hi, None)
+
+
+def _unpack_chunk(seq=FAKE, blk=(FAKE, FAKE), dt=1, B=1, S=8, H=4, D=64, P=2, rank=-1, lo=0, hi=1):
+    arr = (ctypes.c_void_p * max(len(blk), 1))(*blk)
+    return L.usp_unpack_heads_to_seq_chunk(arr, seq, dt, B, S, H, D, P, rank, lo, hi, None)
+
+
+@pytest.mark.parametrize("fn", [_pack_chunk, _unpack_chunk])
+@pytest.mark.parametrize("kw,status", [
+    # the whole-group checks
+    (dict(P=0), -1), (dict(S=1), -1), (dict(rank=2), -1), (dict(B=0), -2), (dict(dt=7), -3),
+    (dict(D=4), -4), (dict(seq=FAKE + 8), -4), (dict(blk=(FAKE, None)), -1),
+    # the chunk: equal groups, non-empty, inside a group of H / P heads
+    (dict(H=5), -1), (dict(lo=1, hi=1), -1), (dict(lo=0, hi=3), -1), (dict(lo=-1), -1),
+    (dict(lo=2, hi=1), -1),
+])
+def test_chunk_relayout_rejects(fn, kw, status):
+    assert fn(**kw) == status
+    assert usp.usp_last_error()
+
+
 def _attn(q=FAKE, k=FAKE, v=FAKE, o=FAKE, i=1, out=0, B=1, S=16, h=2, D=64, lo=0, hi=2,
           scale=0.0, lse=None):
     return L.usp_attention_fwd(q, k, v, o, i, out, B, S, h, D, lo, hi, scale, lse, None)

@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
         rel = [_vp, _vp, ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
         L.usp_pack_seq_to_heads.argtypes = rel
         L.usp_unpack_heads_to_seq.argtypes = rel
+        rel_chunk = rel[:-1] + [_i32, _i32, _vp]
+        L.usp_pack_seq_to_heads_chunk.argtypes = rel_chunk
+        L.usp_unpack_heads_to_seq_chunk.argtypes = rel_chunk
         L.usp_attention_fwd.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
                                         _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
         L.usp_attention_fwd_chunked.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
@@ -259,6 +262,31 @@ def usp_unpack_heads_to_seq(blocks, seq, rank: int = -1, stream=None) -> None:
     B, S, H, D = _relayout_dims(seq, blocks, rank)
     _check(lib().usp_unpack_heads_to_seq(arr, _ptr(seq), _dtype(seq), B, S, H, D, P, rank,
                                          _stream(seq, stream)), "usp_unpack_heads_to_seq")
+
+
+def usp_pack_seq_to_heads_chunk(seq, blocks, head_lo: int, head_hi: int, rank: int = -1,
+                                stream=None) -> None:
+    """One head-chunk phase of the pack: heads [head_lo, head_hi) of every
+    (equal) group of seq [B,S,H,D] (world) or of rank's shard -> the same
+    heads of blocks[j] [B,S,H/P,D]; nothing else is written."""
+    P = len(blocks)
+    arr = (_vp * max(P, 1))(*[_ptr(b) for b in blocks])
+    B, S, H, D = _relayout_dims(seq, blocks, rank)
+    _check(lib().usp_pack_seq_to_heads_chunk(_ptr(seq), arr, _dtype(seq), B, S, H, D, P, rank,
+                                             head_lo, head_hi, _stream(seq, stream)),
+           "usp_pack_seq_to_heads_chunk")
+
+
+def usp_unpack_heads_to_seq_chunk(blocks, seq, head_lo: int, head_hi: int, rank: int = -1,
+                                  stream=None) -> None:
+    """One head-chunk phase of the unpack: heads [head_lo, head_hi) of every
+    blocks[j] -> their place in seq (world) or in rank's shard."""
+    P = len(blocks)
+    arr = (_vp * max(P, 1))(*[_ptr(b) for b in blocks])
+    B, S, H, D = _relayout_dims(seq, blocks, rank)
+    _check(lib().usp_unpack_heads_to_seq_chunk(arr, _ptr(seq), _dtype(seq), B, S, H, D, P, rank,
+                                               head_lo, head_hi, _stream(seq, stream)),
+           "usp_unpack_heads_to_seq_chunk")
 
 
 def _row_dims(full_like):

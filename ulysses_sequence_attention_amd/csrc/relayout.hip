@@ -98,6 +98,46 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutParams p, Pt
     if (dst[u]) __builtin_nontemporal_store(val[u], dst[u]);
 }
 
+// One phase of the head-chunked exchange (maxdiffusion PR #428, two-phase
+// all-to-all): only heads [lo, lo + hc) of each of the P equal groups of h
+// heads move. Per seq row these are P runs of hc * cph chunks, at head
+// offset j * h + lo on the seq side and at head lo of row (b, t0 + s) in
+// block j; within a run the chunk index r is the same on both sides, so a
+// chunk's two addresses are the run bases plus r and no head division is
+// needed. Both sides are read and written in runs of hc * D * esize bytes.
+struct ChunkParams {
+  u32x4* seq;
+  uint32_t n_chunks;  // chunks moved by this launch (< 2^31)
+  uint32_t row0;      // first seq row of this launch
+  uint32_t cpr;       // chunks per seq row = H * cph
+  uint32_t cph;       // chunks per head
+  uint32_t h, lo;     // heads per group; first head of the phase in a group
+  uint32_t crow;      // chunks moved per seq row = P * cgrp
+  uint32_t cgrp;      // chunks moved per group and row = hc * cph
+  uint32_t len, S, t0;
+  FastDiv fd_crow, fd_cgrp, fd_len;
+};
+
+template <bool kPack>
+__global__ __launch_bounds__(kThreads) void relayout_chunk_kernel(ChunkParams p, Ptrs blk) {
+  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= p.n_chunks) return;
+  const uint32_t lrow = p.fd_crow.div(idx);
+  const uint32_t c = idx - lrow * p.crow;
+  const uint32_t j = p.fd_cgrp.div(c);
+  const uint32_t r = c - j * p.cgrp;
+  const uint32_t row = p.row0 + lrow;
+  const uint32_t b = p.fd_len.div(row);
+  const uint32_t s = row - b * p.len;
+  const uint64_t hrow = uint64_t(b) * p.S + p.t0 + s;
+  const uint64_t hoff = (hrow * p.h + p.lo) * p.cph + r;
+  const uint64_t soff = uint64_t(row) * p.cpr + (uint64_t(j) * p.h + p.lo) * p.cph + r;
+  if (kPack)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(p.seq + soff), blk.p[j] + hoff);
+  else
+    __builtin_nontemporal_store(__builtin_nontemporal_load(blk.p[j] + hoff), p.seq + soff);
+}
+
 __global__ void ranges_kernel(int64_t total, int32_t parts, int64_t* bounds) {
   const int32_t r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r > parts) return;
@@ -128,6 +168,44 @@ int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s) {
   if (cpr >= (1u << 30) || a.S >= (int64_t(1) << 31) || rows >= (1ull << 31))
     return fail(USP_ESHAPE, "relayout sizes exceed the 32-bit index range of one row walk");
 
+  Ptrs blk{};
+  for (int j = 0; j < a.P; ++j)
+    blk.p[j] = pack ? static_cast<u32x4*>(a.blk_out[j])
+                    : const_cast<u32x4*>(static_cast<const u32x4*>(a.blk_in[j]));
+  u32x4* const seq = pack ? const_cast<u32x4*>(static_cast<const u32x4*>(a.seq_in))
+                          : static_cast<u32x4*>(a.seq_out);
+
+  if (a.head_hi > 0) {  // one head-chunk phase (equal groups, checked by the caller)
+    ChunkParams p;
+    p.seq = seq;
+    p.cpr = uint32_t(cpr);
+    p.cph = cph;
+    p.h = uint32_t(a.H / a.P);
+    p.lo = uint32_t(a.head_lo);
+    p.cgrp = uint32_t(a.head_hi - a.head_lo) * cph;
+    p.crow = p.cgrp * uint32_t(a.P);  // <= cpr < 2^30
+    p.len = uint32_t(len);
+    p.S = uint32_t(a.S);
+    p.t0 = uint32_t(t0);
+    p.fd_crow = FastDiv(p.crow);
+    p.fd_cgrp = FastDiv(p.cgrp);
+    p.fd_len = FastDiv(p.len);
+    const uint64_t max_rows = ((1ull << 31) - 1) / p.crow;
+    for (uint64_t r0 = 0; r0 < rows; r0 += max_rows) {
+      const uint64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
+      p.row0 = uint32_t(r0);
+      p.n_chunks = uint32_t(nr * p.crow);
+      const uint32_t grid = (p.n_chunks + kThreads - 1) / kThreads;
+      if (pack)
+        relayout_chunk_kernel<true><<<grid, kThreads, 0, s>>>(p, blk);
+      else
+        relayout_chunk_kernel<false><<<grid, kThreads, 0, s>>>(p, blk);
+      if (int st = check_launch(pack ? "head-chunk pack kernel" : "head-chunk unpack kernel"))
+        return st;
+    }
+    return USP_OK;
+  }
+
   RelayoutParams p;
   p.cpr = uint32_t(cpr);
   p.cph = cph;
@@ -142,13 +220,7 @@ int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s) {
   p.fd_base = FastDiv(p.base);
   p.fd_base1 = FastDiv(p.base + 1);
   p.fd_len = FastDiv(p.len);
-
-  Ptrs blk{};
-  for (int j = 0; j < a.P; ++j)
-    blk.p[j] = pack ? static_cast<u32x4*>(a.blk_out[j])
-                    : const_cast<u32x4*>(static_cast<const u32x4*>(a.blk_in[j]));
-  p.seq = pack ? const_cast<u32x4*>(static_cast<const u32x4*>(a.seq_in))
-               : static_cast<u32x4*>(a.seq_out);
+  p.seq = seq;
 
   // Keep every flat chunk index of a launch below 2^31: split the row walk.
   const uint64_t max_rows = ((1ull << 31) - 1) / cpr;

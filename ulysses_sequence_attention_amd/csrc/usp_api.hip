@@ -218,6 +218,40 @@ int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, 
   return ok();
 }
 
+// One phase of the head-chunked exchange: the relayout checks, plus equal
+// head groups and a non-empty chunk inside a group.
+static int check_chunk(int32_t H, int32_t P, int32_t head_lo, int32_t head_hi) {
+  if (H % P)
+    return fail(USP_EINVAL, "head-chunk relayouts need equal head groups (%d heads over %d ranks)", H, P);
+  if (head_lo < 0 || head_hi > H / P || head_lo >= head_hi)
+    return fail(USP_EINVAL, "head chunk [%d, %d) is empty or outside a group of %d heads", head_lo,
+                head_hi, H / P);
+  return USP_OK;
+}
+
+int usp_pack_seq_to_heads_chunk(const void* seq, void* const* blk, usp_dtype dtype, int64_t B,
+                                int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                                int32_t head_lo, int32_t head_hi, void* stream) {
+  if (int st = check_relayout(seq, (const void* const*)blk, dtype, B, S, H, D, P, rank))
+    return st;
+  if (int st = check_chunk(H, P, head_lo, head_hi)) return st;
+  RelayoutArgs a{seq, nullptr, nullptr, blk, B, S, H, D, P, rank < 0 ? -1 : rank,
+                 esize_of(dtype), head_lo, head_hi};
+  if (int st = launch_relayout(a, true, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_unpack_heads_to_seq_chunk(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
+                                  int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
+                                  int32_t head_lo, int32_t head_hi, void* stream) {
+  if (int st = check_relayout(seq, blk, dtype, B, S, H, D, P, rank)) return st;
+  if (int st = check_chunk(H, P, head_lo, head_hi)) return st;
+  RelayoutArgs a{nullptr, seq, blk, nullptr, B, S, H, D, P, rank < 0 ? -1 : rank,
+                 esize_of(dtype), head_lo, head_hi};
+  if (int st = launch_relayout(a, false, (hipStream_t)stream)) return st;
+  return ok();
+}
+
 int usp_scatter_rows(const void* full, void* const* shards, usp_dtype dtype, int64_t B, int64_t S,
                      int64_t W, int32_t P, int32_t rank, void* stream) {
   if (!shards) return fail(USP_EINVAL, "null shard array");

@@ -45,6 +45,9 @@ struct RelayoutArgs {
   void* const* blk_out;        // pack: P destination blocks
   int64_t B, S;
   int32_t H, D, P, rank, esize;
+  // one phase of the head-chunked exchange: heads [head_lo, head_hi) of each
+  // of the P equal groups (head_hi = 0: whole groups, ragged allowed)
+  int32_t head_lo, head_hi;
 };
 int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s);
 
