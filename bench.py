@@ -33,7 +33,13 @@ the fold waits for it; the one-stream pass is reported beside it. "chunked" time
 the long-sequence share (B=1, S=131072, h=8, D=128, 3 head-chunk passes of
 3/3/2 heads; 7.04e13 flop), and usp_attention_fwd_chunked_ws (workspace
 sized for the 3-head pass), next to the single-shot usp_attention_fwd on the
-same inputs (all the same bits).
+same inputs (all the same bits). "two_phase" runs the same step as the
+head-chunked two-phase exchange: for each chunk of the 5 heads (2/2/1), pack
+rank 0's rows of those heads of Q, K and V (usp_pack_seq_to_heads_chunk),
+attention on those heads of block 0, unpack them
+(usp_unpack_heads_to_seq_chunk); overlapped, the next chunk's pack and this
+chunk's unpack run on the second stream under the attention; the output is
+checked bitwise against the single-shot step.
 
 Steps run pipelined: step i + 1's pack and step i's unpack are issued on a
 second stream (default priority) so that they run under the attention of the
@@ -207,6 +213,8 @@ def main():
     ap.add_argument("--skip-rows", action="store_true", help="skip the row-movement timings")
     ap.add_argument("--skip-ring", action="store_true", help="skip the Ulysses+Ring pass timing")
     ap.add_argument("--skip-chunked", action="store_true", help="skip the head-chunked timing")
+    ap.add_argument("--skip-two-phase", action="store_true",
+                    help="skip the two-phase (per head chunk) step timing")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     args = ap.parse_args()
@@ -360,6 +368,80 @@ def main():
     if not torch.equal(pipe_out, oshard):
         raise RuntimeError("pipelined steps produced a different output than a serial step")
     del bsets[1], osets[1], pipe_out
+
+    # the two-phase exchange on the same share: per head chunk (2/2/1 of the
+    # 5 heads), pack rank 0's rows of the chunk's heads, attention on them,
+    # unpack them. Overlapped: the next chunk's pack and this chunk's unpack
+    # run on the second stream under the attention (they touch other heads).
+    two_phase = None
+    if not args.skip_two_phase:
+        print("[bench] two-phase steps", file=sys.stderr, flush=True)
+        kc = usp.usp_head_chunk_ranges(h0, 3)
+        ch = [(kc[c], kc[c + 1]) for c in range(len(kc) - 1)]
+        ws_c = torch.empty(usp.usp_attention_workspace_bytes(
+            usp.USP_BF16, B, S, max(hi - lo for lo, hi in ch), D) // 4, dtype=torch.float32, device=dev)
+        e_cp = [torch.cuda.Event() for _ in ch]
+        e_ca = [torch.cuda.Event() for _ in ch]
+
+        def tp_pack(c, stream):
+            for x, bl in zip(shard, blocks):
+                usp.usp_pack_seq_to_heads_chunk(x, bl, ch[c][0], ch[c][1], rank=0, stream=stream)
+
+        def tp_attn(c):
+            usp.usp_attention_fwd_ws(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0], ws_c,
+                                     head_lo=ch[c][0], head_hi=ch[c][1], stream=main_s)
+
+        def tp_unpack(c, stream):
+            usp.usp_unpack_heads_to_seq_chunk(oblocks, oshard, ch[c][0], ch[c][1], rank=0,
+                                              stream=stream)
+
+        def tp_serial():
+            for c in range(len(ch)):
+                tp_pack(c, main_s)
+                tp_attn(c)
+                tp_unpack(c, main_s)
+
+        def tp_overlapped():
+            io_s.wait_stream(main_s)
+            tp_pack(0, io_s)
+            e_cp[0].record(io_s)
+            for c in range(len(ch)):
+                main_s.wait_event(e_cp[c])
+                tp_attn(c)
+                e_ca[c].record(main_s)
+                if c + 1 < len(ch):
+                    tp_pack(c + 1, io_s)
+                    e_cp[c + 1].record(io_s)
+                io_s.wait_event(e_ca[c])
+                tp_unpack(c, io_s)
+            main_s.wait_stream(io_s)
+
+        tp = {}
+        for name, fn in (("serial", tp_serial), ("overlapped", tp_overlapped)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            a, b_ = ev(), ev()
+            a.record(main_s)
+            for _ in range(args.steps):
+                fn()
+            b_.record(main_s)
+            torch.cuda.synchronize()
+            tp[name] = a.elapsed_time(b_) / args.steps
+            got = oshard.clone()
+            step()
+            torch.cuda.synchronize()
+            if not torch.equal(got, oshard):
+                raise RuntimeError(f"two-phase ({name}) steps differ from a single-shot step")
+        two_phase = {"chunks": kc, "ms_per_step": tp["overlapped"],
+                     "TFLOP/s": attn_flops / (tp["overlapped"] * 1e-3) / 1e12,
+                     "serial_ms_per_step": tp["serial"],
+                     "serial_TFLOP/s": attn_flops / (tp["serial"] * 1e-3) / 1e12,
+                     "how": "per head chunk: pack rank-0 rows of its heads (q, k, v) -> "
+                            "attention on its heads of block 0 -> unpack; overlapped: the next "
+                            "chunk's pack and this chunk's unpack on a second stream",
+                     "bitwise_equal_single_shot": True}
+        del ws_c
 
     # usp_attention_fwd (no workspace) on the same block, for comparison
     print("[bench] attention without workspace", file=sys.stderr, flush=True)
@@ -654,6 +736,7 @@ def main():
         "attention_gqa": gqa,
         "ring": ring,
         "chunked": chunked,
+        "two_phase": two_phase,
         "step_serial": {"ms_per_step": ms_step,
                         "TFLOP/s": attn_flops / (ms_step * 1e-3) / 1e12,
                         "how": "the same steps on one stream: pack, attention, unpack"},
