@@ -37,7 +37,8 @@ same inputs (all the same bits). "two_phase" runs the same step as the
 head-chunked two-phase exchange: for each chunk of the 5 heads (2/2/1), pack
 rank 0's rows of those heads of Q, K and V (usp_pack_seq_to_heads_chunk),
 attention on those heads of block 0, unpack them
-(usp_unpack_heads_to_seq_chunk); overlapped, the next chunk's pack and this
+(usp_unpack_heads_to_seq_chunk; "relayout_world" also times one such chunk
+of the world tensor alone, heads [0, 2) of every group); overlapped, the next chunk's pack and this
 chunk's unpack run on the second stream under the attention; the output is
 checked bitwise against the single-shot step.
 
@@ -708,6 +709,26 @@ def main():
             gbs = 2.0 * nbytes / (ms * 1e-3) / 1e9
             rel[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
                          "frac_of_copy": gbs / copy_gbs, "bytes_rw": 2 * nbytes}
+        # one two-phase chunk of the same tensor: heads [0, 2) of each group of 5
+        cb = nbytes * 2 // h0
+        for name, fn in (("pack_chunk", lambda i: usp.usp_pack_seq_to_heads_chunk(
+                              srcs[i % 3], dsts[i % 3], 0, 2)),
+                         ("unpack_chunk", lambda i: usp.usp_unpack_heads_to_seq_chunk(
+                              dsts[i % 3], srcs[i % 3], 0, 2))):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            a, b_ = ev(), ev()
+            a.record()
+            for i in range(args.relayout_reps):
+                fn(i)
+            b_.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b_) / args.relayout_reps
+            gbs = 2.0 * cb / (ms * 1e-3) / 1e9
+            rel[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
+                         "frac_of_copy": gbs / copy_gbs, "bytes_rw": 2 * cb,
+                         "heads": "[0, 2) of each group of 5"}
 
     out = {
         "metric": METRIC,
