@@ -38,9 +38,11 @@ head-chunked two-phase exchange: for each chunk of the 5 heads (2/2/1), pack
 rank 0's rows of those heads of Q, K and V (usp_pack_seq_to_heads_chunk),
 attention on those heads of block 0, unpack them
 (usp_unpack_heads_to_seq_chunk; "relayout_world" also times one such chunk
-of the world tensor alone, heads [0, 2) of every group); overlapped, the next chunk's pack and this
-chunk's unpack run on the second stream under the attention; the output is
-checked bitwise against the single-shot step.
+of the world tensor alone, heads [0, 2) of every group). Pipelined, a
+chunk's pack for the next step and its unpack for this step run on the
+second stream as soon as this step's attention of that chunk is done, under
+the attention of the following chunks; "serial_*" runs the same phases on
+one stream. The output is checked bitwise against the single-shot step.
 
 Steps run pipelined: step i + 1's pack and step i's unpack are issued on a
 second stream (default priority) so that they run under the attention of the
@@ -402,30 +404,47 @@ def main():
                 tp_attn(c)
                 tp_unpack(c, main_s)
 
-        def tp_overlapped():
+        e_cu = [torch.cuda.Event() for _ in ch]
+        for e in e_ca + e_cu:
+            e.record(main_s)
+
+        def tp_pipelined(n):
+            # chunk c of step i + 1 is packed, and chunk c of step i unpacked,
+            # as soon as step i's attention of chunk c is done (it has read
+            # those heads and written its output), i.e. under the attention
+            # of the following chunks; an attention of chunk c waits for the
+            # pack of its own step and the unpack of the previous one
             io_s.wait_stream(main_s)
-            tp_pack(0, io_s)
-            e_cp[0].record(io_s)
             for c in range(len(ch)):
-                main_s.wait_event(e_cp[c])
-                tp_attn(c)
-                e_ca[c].record(main_s)
-                if c + 1 < len(ch):
-                    tp_pack(c + 1, io_s)
-                    e_cp[c + 1].record(io_s)
                 io_s.wait_event(e_ca[c])
-                tp_unpack(c, io_s)
+                tp_pack(c, io_s)
+                e_cp[c].record(io_s)
+            for i in range(n):
+                for c in range(len(ch)):
+                    main_s.wait_event(e_cp[c])
+                    main_s.wait_event(e_cu[c])
+                    tp_attn(c)
+                    e_ca[c].record(main_s)
+                for c in range(len(ch)):
+                    io_s.wait_event(e_ca[c])
+                    if i + 1 < n:
+                        tp_pack(c, io_s)
+                        e_cp[c].record(io_s)
+                    tp_unpack(c, io_s)
+                    e_cu[c].record(io_s)
             main_s.wait_stream(io_s)
 
+        def tp_serial_n(n):
+            for _ in range(n):
+                tp_serial()
+
         tp = {}
-        for name, fn in (("serial", tp_serial), ("overlapped", tp_overlapped)):
-            for _ in range(args.warmup):
-                fn()
+        for name, fn in (("serial", tp_serial_n), ("pipelined", tp_pipelined)):
+            fn(args.warmup)
             torch.cuda.synchronize()
             a, b_ = ev(), ev()
             a.record(main_s)
-            for _ in range(args.steps):
-                fn()
+            fn(args.steps)
             b_.record(main_s)
             torch.cuda.synchronize()
             tp[name] = a.elapsed_time(b_) / args.steps
@@ -434,13 +453,14 @@ def main():
             torch.cuda.synchronize()
             if not torch.equal(got, oshard):
                 raise RuntimeError(f"two-phase ({name}) steps differ from a single-shot step")
-        two_phase = {"chunks": kc, "ms_per_step": tp["overlapped"],
-                     "TFLOP/s": attn_flops / (tp["overlapped"] * 1e-3) / 1e12,
+        two_phase = {"chunks": kc, "ms_per_step": tp["pipelined"],
+                     "TFLOP/s": attn_flops / (tp["pipelined"] * 1e-3) / 1e12,
                      "serial_ms_per_step": tp["serial"],
                      "serial_TFLOP/s": attn_flops / (tp["serial"] * 1e-3) / 1e12,
                      "how": "per head chunk: pack rank-0 rows of its heads (q, k, v) -> "
-                            "attention on its heads of block 0 -> unpack; overlapped: the next "
-                            "chunk's pack and this chunk's unpack on a second stream",
+                            "attention on its heads of block 0 -> unpack; pipelined: a chunk's "
+                            "pack for the next step and unpack for this step on a second stream "
+                            "as soon as this step's attention of that chunk is done",
                      "bitwise_equal_single_shot": True}
         del ws_c
 
