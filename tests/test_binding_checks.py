@@ -66,6 +66,19 @@ def test_relayout_block_shapes_follow_the_balanced_ranges():
         usp.usp_pack_seq_to_heads(t(2, 4, 7, 64), good, rank=1)
 
 
+def test_chunk_relayout_block_shapes():
+    seq = t(2, 10, 6, 64)                       # 6 heads over 3 ranks: groups of 2
+    good = [t(2, 10, 2, 64) for _ in range(3)]
+    with pytest.raises(ValueError, match=r"blocks\[2\] has shape"):
+        usp.usp_pack_seq_to_heads_chunk(seq, good[:2] + [t(2, 10, 3, 64)], 0, 1)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        usp.usp_pack_seq_to_heads_chunk(seq, good, 0, 1)
+    with pytest.raises(ValueError, match=r"blocks\[0\] has dtype"):
+        usp.usp_unpack_heads_to_seq_chunk([t(2, 10, 2, 64, dtype=F)] + good[1:], seq, 1, 2)
+    with pytest.raises(ValueError, match="seq has shape"):           # rank 0 holds 4 rows
+        usp.usp_unpack_heads_to_seq_chunk(good, t(2, 3, 6, 64), 0, 2, rank=0)
+
+
 def test_row_shard_shapes_follow_the_balanced_ranges():
     full = t(1, 10, 16)                         # 10 rows over 3 ranks: 4 / 3 / 3
     with pytest.raises(ValueError, match=r"shards\[0\] has shape"):
