@@ -44,28 +44,38 @@ def ulysses_world(q, k, v, P: int, scale=None, attn=attention):
 def ulysses_two_phase_world(q, k, v, P: int, chunks: int, scale=None, attn=attention):
     """The head-chunked two-phase exchange on world layouts (maxdiffusion PR
     #428 description): for each chunk ``[k_c, k_{c+1})`` of the plan over a
-    group's h = H / P heads, in turn, pack those heads of q, k and v into the
-    head blocks, run ``attn`` on those heads of every block, and unpack them
-    from the output blocks. Returns ``O [B, S, H, D]``. Needs equal head
-    groups and plain multi-head attention (one K/V head per query head)."""
+    group's K/V heads, in turn, pack those heads of k and v and their query
+    heads of q into the head blocks, run ``attn`` on those heads of every
+    block, and unpack them from the output blocks. Returns ``O [B, S, H, D]``.
+
+    Needs equal head groups (P divides H and Hkv). With grouped K/V heads (G =
+    H / Hkv query heads per K/V head) the plan runs over the hkv = Hkv / P K/V
+    heads of a group and chunk ``[lo, hi)`` carries query heads ``[lo G, hi
+    G)``, so no chunk splits the query heads of one K/V head; with G = 1 it is
+    the plan over the group's H / P heads."""
     B, S, H, D = q.shape
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("the two-phase composition takes q, k, v of one shape")
-    if H % P:
-        raise ValueError(f"head chunks need equal head groups: P ({P}) has to divide H ({H})")
-    h = H // P
-    kc = head_chunk_ranges(h, chunks)
-    qb, kb, vb, ob = ([np.zeros((B, S, h, D), dtype=np.float64) for _ in range(P)]
-                      for _ in range(4))
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or Hkv < 1 or H % Hkv:
+        raise ValueError("the two-phase composition takes q [B,S,H,D] and k, v [B,S,Hkv,D] "
+                         "with Hkv dividing H")
+    if H % P or Hkv % P:
+        raise ValueError(f"head chunks need equal head groups: P ({P}) has to divide H ({H}) "
+                         f"and Hkv ({Hkv})")
+    G, h, hkv = H // Hkv, H // P, Hkv // P
+    kc = head_chunk_ranges(hkv, chunks)
+    qb, ob = ([np.zeros((B, S, h, D), dtype=np.float64) for _ in range(P)] for _ in range(2))
+    kb, vb = ([np.zeros((B, S, hkv, D), dtype=np.float64) for _ in range(P)] for _ in range(2))
     out = np.zeros((B, S, H, D), dtype=np.float64)
     for c in range(chunks):
         lo, hi = kc[c], kc[c + 1]
-        for x, xb in ((q, qb), (k, kb), (v, vb)):
+        relayout.pack_heads_chunk(np.asarray(q, dtype=np.float64), qb, S, lo * G, hi * G)
+        for x, xb in ((k, kb), (v, vb)):
             relayout.pack_heads_chunk(np.asarray(x, dtype=np.float64), xb, S, lo, hi)
         for j in range(P):
-            part = (qb[j][:, :, lo:hi], kb[j][:, :, lo:hi], vb[j][:, :, lo:hi])
-            ob[j][:, :, lo:hi] = attention(*part, scale=scale) if attn is attention else attn(*part)
-        relayout.unpack_heads_chunk(ob, out, S, lo, hi)
+            part = (qb[j][:, :, lo * G:hi * G], kb[j][:, :, lo:hi], vb[j][:, :, lo:hi])
+            ob[j][:, :, lo * G:hi * G] = (attention(*part, scale=scale) if attn is attention
+                                          else attn(*part))
+        relayout.unpack_heads_chunk(ob, out, S, lo * G, hi * G)
     return out
 
 

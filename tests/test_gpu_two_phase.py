@@ -207,3 +207,48 @@ def test_two_phase_video_dit_world():
     log("two-phase video-DiT world, chunks 2/2/1")
     one, two = _steps(*(to_dev(x, BF) for x in (q, k, v)), w.P, 3, w.S)
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,S,H,Hkv,D,P,chunks", [(2, 300, 20, 10, 64, 2, 3), (1, 4096, 32, 8, 128, 4, 2)])
+def test_two_phase_grouped_heads_equals_single_shot(B, S, H, Hkv, D, P, chunks):
+    """Grouped K/V heads: the plan runs over each group's K/V heads and a
+    chunk [lo, hi) carries query heads [lo G, hi G); per chunk, pack those
+    query heads of q and K/V heads of k and v, usp_attention_fwd_gqa on the
+    chunk's query heads, unpack them. Bitwise equal to the single-shot
+    grouped step, and the oracle's two-phase result within tolerance."""
+    import torch
+    G, h, hkv = H // Hkv, H // P, Hkv // P
+    q, k, v = synth.draw_qkv(B, S, H, D, 50 + P, hkv=Hkv)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+
+    def blocks(heads):
+        return [torch.empty((B, S, heads, D), dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+
+    def attend(qb, kb, vb, ob, lo, hi):
+        nb = usp.usp_attention_workspace_bytes(usp.USP_BF16, B, S, hi - lo, D)
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        for j in range(P):
+            usp.usp_attention_fwd_gqa(qb[j], kb[j], vb[j], ob[j], head_lo=lo, head_hi=hi, ws=ws)
+
+    log(f"two-phase grouped B={B} S={S} H={H} Hkv={Hkv} D={D} P={P} chunks={chunks}")
+    qb, kb, vb, ob = blocks(h), blocks(hkv), blocks(hkv), blocks(h)
+    usp.usp_pack_seq_to_heads(dq, qb)
+    usp.usp_pack_seq_to_heads(dk, kb)
+    usp.usp_pack_seq_to_heads(dv, vb)
+    attend(qb, kb, vb, ob, 0, h)
+    one = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=DEV)
+    usp.usp_unpack_heads_to_seq(ob, one)
+    qb, kb, vb, ob = blocks(h), blocks(hkv), blocks(hkv), blocks(h)
+    two = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=DEV)
+    for lo, hi in _plan(hkv, chunks):
+        usp.usp_pack_seq_to_heads_chunk(dq, qb, lo * G, hi * G)
+        usp.usp_pack_seq_to_heads_chunk(dk, kb, lo, hi)
+        usp.usp_pack_seq_to_heads_chunk(dv, vb, lo, hi)
+        attend(qb, kb, vb, ob, lo * G, hi * G)
+        usp.usp_unpack_heads_to_seq_chunk(ob, two, lo * G, hi * G)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    if S <= 512:
+        ref = U.ulysses_two_phase_world(*(widen(x, BF) for x in (q, k, v)), P, chunks)
+        max_abs, rel = err(widen(to_host(two), BF), ref)
+        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_FROB, (max_abs, rel)

@@ -183,8 +183,25 @@ def test_two_phase_identity_mock_and_errors():
     assert np.array_equal(out, q + 2 * v)      # elementwise mock: every head back in place
     with pytest.raises(ValueError, match="equal head groups"):
         U.ulysses_two_phase_world(*(_rand((1, 5, 7, 2), i) for i in range(3)), 3, 1)
-    with pytest.raises(ValueError, match="one shape"):
-        U.ulysses_two_phase_world(q, k[:, :, :3], v[:, :, :3], 3, 1)
+    with pytest.raises(ValueError, match="Hkv dividing H"):
+        U.ulysses_two_phase_world(q, k[:, :, :5], v[:, :, :5], 3, 1)
+    with pytest.raises(ValueError, match="equal head groups"):          # Hkv = 4 over P = 3
+        U.ulysses_two_phase_world(q, k[:, :, :4], v[:, :, :4], 3, 1)
+
+
+@pytest.mark.parametrize("B,S,H,Hkv,D,P,chunks", [(1, 11, 12, 6, 4, 3, 2), (2, 9, 20, 10, 3, 2, 3),
+                                                  (1, 7, 8, 2, 2, 2, 1), (1, 10, 6, 3, 4, 1, 2)])
+def test_two_phase_grouped_heads(B, S, H, Hkv, D, P, chunks):
+    # chunks over each group's K/V heads, each with its G query heads: the
+    # grouped single-shot result exactly, and SDPA with enable_gqa
+    q = _rand((B, S, H, D), 30)
+    k, v = (_rand((B, S, Hkv, D), 31 + i) for i in range(2))
+    out = U.ulysses_two_phase_world(q, k, v, P, chunks)
+    assert np.array_equal(out, U.ulysses_world(q, k, v, P))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v)),
+        enable_gqa=True).permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12
 
 
 # ---- grouped K/V heads (Hkv < Hq): query head n uses K/V head n // (Hq / Hkv)
