@@ -30,7 +30,7 @@ import numpy as np
 
 from . import relayout
 from .attention import attention
-from .ranges import balanced_ranges
+from .ranges import balanced_ranges, head_chunk_ranges
 
 
 def merge(o_a, lse_a, o_b, lse_b):
@@ -106,4 +106,44 @@ def ulysses_ring_world(q, k, v, U: int, R: int, scale=None):
             o, _ = ring_attention(qb[r][j], blocks, scale=scale, order=ring_order(r, R))
             ob.append(o)
         out[:, T[r]:T[r + 1]] = relayout.unpack_heads_to_seq(ob, H)
+    return out
+
+
+def ulysses_ring_two_phase_world(q, k, v, U: int, R: int, chunks: int, scale=None):
+    """:func:`ulysses_ring_world` with the Ulysses exchange in head-chunk
+    phases (maxdiffusion PR #428 applies its chunking to Ulysses+Ring too):
+    for each chunk ``[lo, hi)`` of the plan over a Ulysses group's K/V heads
+    (hkv = Hkv / U; query heads ``[lo G, hi G)``, G = H / Hkv), in turn: pack
+    those heads of every ring block, run every rank's ring pass on them,
+    unpack them. Needs U to divide H and Hkv. Returns ``O [B, S, H, D]``."""
+    B, S, H, D = q.shape
+    Hkv = k.shape[2]
+    if H % Hkv or H % U or Hkv % U:
+        raise ValueError(f"head chunks need equal head groups: U ({U}) has to divide H ({H}) "
+                         f"and Hkv ({Hkv}), and Hkv has to divide H")
+    G, h, hkv = H // Hkv, H // U, Hkv // U
+    T = balanced_ranges(S, R)
+    L = [T[r + 1] - T[r] for r in range(R)]
+    x64 = [np.asarray(x, dtype=np.float64) for x in (q, k, v)]
+    qb = [[np.zeros((B, L[r], h, D)) for _ in range(U)] for r in range(R)]
+    kb = [[np.zeros((B, L[r], hkv, D)) for _ in range(U)] for r in range(R)]
+    vb = [[np.zeros((B, L[r], hkv, D)) for _ in range(U)] for r in range(R)]
+    ob = [[np.zeros((B, L[r], h, D)) for _ in range(U)] for r in range(R)]
+    out = np.zeros((B, S, H, D), dtype=np.float64)
+    kc = head_chunk_ranges(hkv, chunks)
+    for c in range(chunks):
+        lo, hi = kc[c], kc[c + 1]
+        for r in range(R):
+            rows = slice(T[r], T[r + 1])
+            relayout.pack_heads_chunk(x64[0][:, rows], qb[r], L[r], lo * G, hi * G)
+            relayout.pack_heads_chunk(x64[1][:, rows], kb[r], L[r], lo, hi)
+            relayout.pack_heads_chunk(x64[2][:, rows], vb[r], L[r], lo, hi)
+        for r in range(R):
+            for j in range(U):
+                blocks = [(kb[i][j][:, :, lo:hi], vb[i][j][:, :, lo:hi]) for i in range(R)]
+                o, _ = ring_attention(qb[r][j][:, :, lo * G:hi * G], blocks, scale=scale,
+                                      order=ring_order(r, R))
+                ob[r][j][:, :, lo * G:hi * G] = o
+        for r in range(R):
+            relayout.unpack_heads_chunk(ob[r], out[:, T[r]:T[r + 1]], L[r], lo * G, hi * G)
     return out

@@ -179,26 +179,28 @@ def test_merge_parity(B, S, h, D, lo, hi):
     assert np.array_equal(il.cpu().numpy()[:, sel], lout[:, sel])
 
 
-def _ring_pass(dq, kv_blocks, order, out_dtype, use_ws=True):
-    """One rank's ring pass on the GPU: block attention over each K/V block
-    in ``order`` folded by usp_attention_merge; the last fold writes
-    ``out_dtype``. Returns (o, lse)."""
+def _ring_pass(dq, kv_blocks, order, out_dtype, use_ws=True, lo=0, hi=None):
+    """One rank's ring pass on the GPU over query heads [lo, hi): block
+    attention over each K/V block in ``order`` folded by usp_attention_merge;
+    the last fold writes ``out_dtype``. Returns (o, lse) (other heads
+    poisoned)."""
     import torch
     B, Sq, h, D = dq.shape
-    o_acc, l_acc = _block(dq, *kv_blocks[order[0]], F, use_ws)
+    hi = h if hi is None else hi
+    o_acc, l_acc = _block(dq, *kv_blocks[order[0]], F, use_ws, lo, hi)
     if len(order) == 1:
         if out_dtype == F:
             return o_acc, l_acc
-        return _block(dq, *kv_blocks[order[0]], BF, use_ws)
+        return _block(dq, *kv_blocks[order[0]], BF, use_ws, lo, hi)
     for n, i in enumerate(order[1:]):
-        o_i, l_i = _block(dq, *kv_blocks[i], F, use_ws)
+        o_i, l_i = _block(dq, *kv_blocks[i], F, use_ws, lo, hi)
         last = n == len(order) - 2
         if last and out_dtype == BF:
             o = poisoned((B, Sq, h, D), BF)
-            usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o, l_acc)
+            usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o, l_acc, head_lo=lo, head_hi=hi)
             o_acc = o
         else:
-            usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o_acc, l_acc)
+            usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o_acc, l_acc, head_lo=lo, head_hi=hi)
     return o_acc, l_acc
 
 
@@ -238,6 +240,59 @@ def _ring_world(w, q, k, v, out_dtype):
         out[:, T[r]:T[r + 1]] = seq
     torch.cuda.synchronize()
     return to_host(out)
+
+
+def _ring_world_two_phase(w, q, k, v, out_dtype, chunks):
+    """The same U x R composition with the Ulysses exchange in head-chunk
+    phases: for each chunk of the plan over a group's K/V heads (query heads
+    [lo G, hi G)), pack those heads of every ring block
+    (usp_pack_seq_to_heads_chunk), run every rank's ring pass on them, unpack
+    them (usp_unpack_heads_to_seq_chunk)."""
+    import torch
+    B, S, H, D, U, Rr = w.B, w.S, w.H, w.D, w.P, w.ring
+    Hkv = w.kv_heads
+    G, h, hkv = H // Hkv, H // U, Hkv // U
+    T = R.balanced_ranges(S, Rr)
+    L = [T[r + 1] - T[r] for r in range(Rr)]
+    dq, dk, dv = (to_dev(x, w.dtype) for x in (q, k, v))
+    seqs = [[x[:, T[r]:T[r + 1]].contiguous() for r in range(Rr)] for x in (dq, dk, dv)]
+    odt = torch.float32 if out_dtype == F else torch.bfloat16
+
+    def blocks(heads, dt=torch.bfloat16):
+        return [[torch.empty((B, L[r], heads, D), dtype=dt, device=DEV) for _ in range(U)]
+                for r in range(Rr)]
+
+    qb, kb, vb, ob = blocks(h), blocks(hkv), blocks(hkv), blocks(h, odt)
+    outs = [torch.empty((B, L[r], H, D), dtype=odt, device=DEV) for r in range(Rr)]
+    kc = R.head_chunk_ranges(hkv, chunks)
+    for c in range(chunks):
+        lo, hi = kc[c], kc[c + 1]
+        for r in range(Rr):
+            usp.usp_pack_seq_to_heads_chunk(seqs[0][r], qb[r], lo * G, hi * G)
+            usp.usp_pack_seq_to_heads_chunk(seqs[1][r], kb[r], lo, hi)
+            usp.usp_pack_seq_to_heads_chunk(seqs[2][r], vb[r], lo, hi)
+        for r in range(Rr):
+            for j in range(U):
+                log(f"ring pass in chunks {w.name} chunk [{lo},{hi}) ring block {r} head group {j}")
+                o, _ = _ring_pass(qb[r][j], [(kb[i][j], vb[i][j]) for i in range(Rr)],
+                                  RG.ring_order(r, Rr), out_dtype, lo=lo * G, hi=hi * G)
+                ob[r][j][:, :, lo * G:hi * G] = o[:, :, lo * G:hi * G]
+        for r in range(Rr):
+            usp.usp_unpack_heads_to_seq_chunk(ob[r], outs[r], lo * G, hi * G)
+    torch.cuda.synchronize()
+    return to_host(torch.cat(outs, dim=1))
+
+
+def test_ring_small_in_head_chunks_equals_unchunked():
+    """ring_small (U = 2, R = 3, 12 query heads over 4 K/V heads: groups of
+    2 K/V heads, chunks 1/1, G = 3) in head-chunk phases gives the unchunked
+    composition bit for bit, fp32 and bf16 outputs."""
+    w = synth.WORKLOADS["ring_small"]
+    q, k, v = synth.draw_workload(w)
+    for dt in (F, BF):
+        one = _ring_world(w, q, k, v, dt)
+        two = _ring_world_two_phase(w, q, k, v, dt, 2)
+        assert two.tobytes() == one.tobytes(), dt
 
 
 def test_ring_small_world_full_compare():

@@ -220,3 +220,22 @@ def test_ring_small_workload_composition():
     assert balanced_ranges(w.S, w.ring) == [0, 501, 1001, 1501]
     out = RG.ulysses_ring_world(q, k, v, w.P, w.ring)
     assert np.max(np.abs(out - A.attention(q, k, v))) <= 1e-12
+
+
+@pytest.mark.parametrize("B,S,H,Hkv,D,Uu,R,chunks", [(1, 23, 4, 4, 8, 2, 3, 2), (2, 40, 12, 6, 4, 2, 2, 3),
+                                                      (1, 17, 8, 4, 4, 2, 4, 1), (1, 13, 6, 6, 4, 1, 3, 2)])
+def test_ulysses_ring_in_head_chunks(B, S, H, Hkv, D, Uu, R, chunks):
+    # the chunked exchange around the ring passes: the unchunked composition
+    # exactly, SDPA within rounding
+    q = _rand((B, S, H, D), 60)
+    k = _rand((B, S, Hkv, D), 61)
+    v = _rand((B, S, Hkv, D), 62)
+    out = RG.ulysses_ring_two_phase_world(q, k, v, Uu, R, chunks)
+    assert np.array_equal(out, RG.ulysses_ring_world(q, k, v, Uu, R))
+    assert np.max(np.abs(out - _sdpa(q, k, v))) <= 1e-12
+
+
+def test_ulysses_ring_in_head_chunks_rejects_ragged_groups():
+    q = _rand((1, 8, 6, 4), 1)
+    with pytest.raises(ValueError, match="equal head groups"):
+        RG.ulysses_ring_two_phase_world(q, q, q, 4, 2, 1)
