@@ -3,6 +3,7 @@
 Every call here returns before any device work: host-only range functions,
 and invalid arguments that the library must reject without launching."""
 import ctypes
+import os
 import subprocess
 
 import pytest
@@ -274,3 +275,22 @@ def test_c_consumer_links_against_this_library():
     assert os.path.realpath(usp._binding.LIB_PATH) in os.path.realpath(libs["libusp.so"].split("=>")[1].split()[0])
     assert "libamdhip64.so.7" in libs and "not found" not in libs["libamdhip64.so.7"]
     assert not any("torch" in line for line in libs.values())
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No fallback path: with libusp.so absent the binding raises instead of
+    computing anything (checked in a fresh process)."""
+    import subprocess
+    import sys
+    code = ("import ulysses_sequence_attention_amd._binding as b\n"
+            "b._LIB = None\n"
+            "b.LIB_PATH = '/nonexistent/libusp.so'\n"
+            "try:\n"
+            "    b.usp_balanced_ranges(10, 3)\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.stdout.startswith("raised") and "is missing" in r.stdout, r.stdout + r.stderr
