@@ -14,7 +14,11 @@ from gpu_util import DEV, log, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def test_step_replays_from_a_captured_graph():
+@pytest.mark.parametrize("phases", [False, True])
+def test_step_replays_from_a_captured_graph(phases):
+    """phases: the two-phase form of the same step (per head chunk 2/2 of the
+    4 heads of a group: pack, attention, unpack), whose replays must also
+    equal the eager single-shot step."""
     import torch
     w = synth.WORKLOADS["vit_l16"]            # B=32, S=577, H=16, D=64, P=4
     B, S, H, D, P = w.B, w.S, w.H, w.D, w.P
@@ -36,6 +40,18 @@ def test_step_replays_from_a_captured_graph():
             usp.usp_attention_fwd_ws(blocks[0][j], blocks[1][j], blocks[2][j], oblocks[j], ws)
         usp.usp_unpack_heads_to_seq(oblocks, out)
 
+    def step_phases():
+        for lo, hi in ((0, 2), (2, 4)):
+            for x, bl in zip(qkv, blocks):
+                usp.usp_pack_seq_to_heads_chunk(x, bl, lo, hi)
+            for j in range(P):
+                usp.usp_attention_fwd_ws(blocks[0][j], blocks[1][j], blocks[2][j], oblocks[j], ws,
+                                         head_lo=lo, head_hi=hi)
+            usp.usp_unpack_heads_to_seq_chunk(oblocks, out, lo, hi)
+
+    captured = step_phases if phases else step
+    assert usp.usp_head_chunk_ranges(hb[1] - hb[0], 2) == [0, 2, 4]
+
     def load(seed):
         for dst, src in zip(qkv, synth.draw_qkv(B, S, H, D, seed)):
             dst.copy_(to_dev(src, synth.BF16))
@@ -44,13 +60,13 @@ def test_step_replays_from_a_captured_graph():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):             # warm-up outside the capture
-        step()
+        captured()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    log("capture pack -> attention x4 -> unpack (ViT-L/16 world)")
+    log(f"capture pack -> attention x4 -> unpack (ViT-L/16 world){' in head-chunk phases' if phases else ''}")
     with torch.cuda.graph(graph):
-        step()
+        captured()
     torch.cuda.synchronize()
     for i, seed in enumerate((101, 102, 103)):
         load(seed)
