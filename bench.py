@@ -145,28 +145,109 @@ def stored_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def pmc_summary(dirs, out_json):
-    """Parse rocprofv3 --pmc counter CSVs (FETCH_SIZE and WRITE_SIZE runs of
-    this benchmark) into per-kernel KiB per dispatch, calibrate both counters
-    on the plain copy kernel (COPY_BYTES read and written per dispatch), and
-    write the attention kernel's HBM traffic per launch to ``out_json``."""
+def kernel_kind(name):
+    """Short name of a kernel of this benchmark from its rocprofv3 name."""
+    return ("attention" if "attn_bf16_kernel<128, 8, 1, 2," in name else
+            "attention_groups" if "attn_bf16_kernel<128, 8, 2, 1," in name else
+            "merge" if "attn_merge_halves" in name else
+            "copy" if "copyBuffer" in name else
+            "pack" if "relayout_kernel<true>" in name else
+            "unpack" if "relayout_kernel<false>" in name else None)
+
+
+def read_pmc(dirs):
+    """rocprofv3 --pmc CSVs under ``dirs`` -> {(kind, counter): {dispatch: value}},
+    each value summed over the counter's instances (SEs, SIMDs, channels)."""
     per = {}
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for r in csv.DictReader(f):
-                    name = r["Kernel_Name"]
-                    kind = ("attention" if "attn_bf16_kernel<128, 8, 1, 2," in name else
-                            "attention_groups" if "attn_bf16_kernel<128, 8, 2, 1," in name else
-                            "merge" if "attn_merge_halves" in name else
-                            "copy" if "copyBuffer" in name else
-                            "pack" if "relayout_kernel<true>" in name else
-                            "unpack" if "relayout_kernel<false>" in name else None)
+                    kind = kernel_kind(r["Kernel_Name"])
                     if kind is None:
                         continue
                     key = (kind, r["Counter_Name"])
                     per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
                     per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+                    if "End_Timestamp" in r:
+                        per.setdefault((kind, "_duration_ns"), {})[r["Dispatch_Id"]] = (
+                            float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+                    for col in ("VGPR_Count", "Accum_VGPR_Count", "LDS_Block_Size", "Workgroup_Size"):
+                        if col in r:
+                            per.setdefault((kind, "_" + col), {})[r["Dispatch_Id"]] = float(r[col])
+    return per
+
+
+# per-dispatch algorithmic flops of the video-DiT share's attention (all of it
+# runs in the key-half kernel; the merge does no matrix work)
+ATTN_FLOPS = 4.0 * 5 * 32760 * 32760 * 128
+
+
+def sq_summary(dirs, out_txt):
+    """Summarise rocprofv3 --pmc runs of SQ/GRBM counters of this benchmark:
+    per-kernel mean per dispatch of every counter, and for the attention
+    kernel the matrix flops the counters imply against the algorithmic
+    flops, the matrix-core busy fraction and the LDS figures."""
+    per = read_pmc(dirs)
+    avg = {k: float(np.mean(list(v.values()))) for k, v in per.items()}
+    lines = [f"# kernel source: attn_bf16.hip sha256 {source_digest()}", "",
+             "kernel           counter                          mean/dispatch  dispatches"]
+    for (kind, ctr), val in sorted(avg.items()):
+        if kind == "copy":
+            continue
+        lines.append(f"{kind:16s} {ctr:32s} {val:14.6g}  {len(per[(kind, ctr)])}")
+    a = {c: v for (k, c), v in avg.items() if k == "attention"}
+    if a:
+        lines.append("")
+        lines.append("attention kernel (usp_attention_fwd_ws key-half walk), derived:")
+        dur = a.get("_duration_ns")
+        if dur:
+            lines.append(f"  duration {dur / 1e3:.1f} us per dispatch under the profiler "
+                         f"(counters serialise dispatches)")
+        mops = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        if mops is not None:
+            lines.append(f"  matrix flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = {mops * 512:.4e} "
+                         f"against {ATTN_FLOPS:.4e} algorithmic ({mops * 512 / ATTN_FLOPS:.4f}x)")
+        n_mfma = a.get("SQ_INSTS_MFMA")
+        if n_mfma is not None:
+            lines.append(f"  MFMA instructions {n_mfma:.4e} x 32768 flop (32x32x16) = "
+                         f"{n_mfma * 32768:.4e} ({n_mfma * 32768 / ATTN_FLOPS:.4f}x algorithmic)")
+        busy, gui = a.get("SQ_VALU_MFMA_BUSY_CYCLES"), a.get("GRBM_GUI_ACTIVE")
+        if busy is not None and gui:
+            # GRBM_GUI_ACTIVE counts each XCD's active cycles (8 instances):
+            # the kernel's cycles are gui / 8; 1024 SIMDs
+            cyc = gui / 8
+            lines.append(f"  GRBM_GUI_ACTIVE / 8 XCDs = {cyc:.4e} cycles"
+                         + (f" (= {cyc / (dur * 1e-9) / 1e9:.3f} GHz over the dispatch)" if dur else ""))
+            lines.append(f"  matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = "
+                         f"{busy / (1024 * cyc):.3f}")
+        coex = a.get("SQ_VALU_MFMA_COEXEC_CYCLES")
+        if coex is not None and busy:
+            lines.append(f"  VALU issued while the matrix core is busy: {coex / busy:.3f} of busy cycles")
+        if a.get("SQ_INSTS_LDS") and a.get("SQ_INSTS_MFMA"):
+            lines.append(f"  LDS instructions per MFMA: {a['SQ_INSTS_LDS'] / a['SQ_INSTS_MFMA']:.3f}")
+        if a.get("SQ_INSTS_LDS_LOAD_BANDWIDTH") is not None and n_mfma:
+            lb = a["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64
+            lines.append(f"  LDS bytes loaded {lb:.4e} = {lb / n_mfma:.0f} B per MFMA")
+        bc, act = a.get("SQ_LDS_BANK_CONFLICT"), a.get("SQ_LDS_IDX_ACTIVE")
+        if bc is not None and act:
+            lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {bc / act:.4f}")
+        if a.get("SQ_INSTS_VALU_TRANS_F32") is not None:
+            lines.append(f"  transcendental VALU instructions {a['SQ_INSTS_VALU_TRANS_F32']:.4e} "
+                         f"(one exp2 per score: {5 * 32760 * 32760 / 64:.4e} wave instructions)")
+    text = "\n".join(lines)
+    print(text)
+    if out_txt:
+        with open(out_txt, "w") as f:
+            f.write(text + "\n")
+
+
+def pmc_summary(dirs, out_json):
+    """Parse rocprofv3 --pmc counter CSVs (FETCH_SIZE and WRITE_SIZE runs of
+    this benchmark) into per-kernel KiB per dispatch, calibrate both counters
+    on the plain copy kernel (COPY_BYTES read and written per dispatch), and
+    write the attention kernel's HBM traffic per launch to ``out_json``."""
+    per = read_pmc(dirs)
     # the runtime's copy kernel also serves small copies (a clone, a compare):
     # calibrate on the 1 GiB copies only, the dispatches of at least half the
     # largest count
@@ -220,10 +301,16 @@ def main():
                     help="skip the two-phase (per head chunk) step timing")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
+    ap.add_argument("--pmc-sq", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 SQ/GRBM counter runs of this benchmark and exit")
+    ap.add_argument("--pmc-out", metavar="FILE", help="text file for --pmc-sq's summary")
     args = ap.parse_args()
 
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, TRAFFIC_JSON)
+        return
+    if args.pmc_sq:
+        sq_summary(args.pmc_sq, args.pmc_out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not "

@@ -136,18 +136,34 @@ __device__ __forceinline__ float sum_halves(float x) {
 // 16 bytes per lane from global memory straight into LDS
 // (buffer_load_dwordx4 ... lds): lane i reads base + voff (a 32-bit byte
 // offset; base wave-uniform, the buffer descriptor built from it in scalar
-// registers) and its bytes land at lds_base + 16 i, lds_base uniform over
-// the wave. Per-lane addressing is a fixed 32-bit offset, so a load costs no
-// per-lane address arithmetic. The builtins exist for the device target
-// only; the host pass sees an empty body.
+// registers: raw buffer, stride 0, no range clamp in practice since offsets
+// stay inside the tensor) and its bytes land at lds_base + 16 i, lds_base
+// uniform over the wave (M0). Per-lane addressing is a fixed 32-bit offset,
+// so a load costs no per-lane address arithmetic.
+//
+// Written as inline assembly on purpose: issued through the compiler's
+// builtin, the load counts as an LDS write of unknown address, and the
+// compiler then makes the next LDS read of any buffer wait for every such
+// load to land (s_waitcnt vmcnt(0) in front of the step's first fragment
+// read), which serialises each tile load with the step that issues it
+// (measured: 4-5% of the kernel's time). The kernel waits for its own loads
+// (loads_done) before the barrier that publishes them. The instruction has
+// no register result. The host pass sees an empty body.
 __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // raw buffer: stride 0, no range clamp in practice (offsets stay inside the
-  // tensor), 32-bit data format in the descriptor's last word
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, 0, 0, 0);
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
+  r[2] = 0x7fffffff;
+  r[3] = 0x00020000;
+  const int m0 = __builtin_amdgcn_readfirstlane(
+      int(uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds_base))));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
 #endif
 }
 
@@ -230,25 +246,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   // (rows [q RPI, q RPI + RPI)).
   auto swz_k = [](int r) { return (r / RPL) % CPR; };
   auto swz_v = [](int r) { return 4 * ((r / RPL) % (CPR / 4)); };
-  uint32_t kgo[NI], vgo[NI];  // per-lane byte offsets from the tile's first row
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
-    kgo[i] = uint32_t((r * rsk + (pos ^ swz_k(r)) * 8) * 2);
-    vgo[i] = uint32_t((r * rsk + (pos ^ swz_v(r)) * 8) * 2);
-  }
+  // Load i of wave w covers rows (w + GW i) RPI .. + RPI. Both swizzles
+  // repeat every 16 rows (K: RPL * CPR, V: RPL * CPR / 4 divides it) and
+  // GW * RPI is a multiple of 16, so a lane's swizzled chunk is the same in
+  // every load: one per-lane offset serves all of them, and load i adds the
+  // wave-uniform GW * RPI * i rows to the tile's base address.
+  static_assert((GW * RPI) % (RPL * CPR) == 0, "loads must start on a swizzle period");
+  const int lr0 = w * RPI + lane / CPR, lpos = lane % CPR;  // row and chunk of load 0
+  const uint32_t kgo = uint32_t((lr0 * rsk + (lpos ^ swz_k(lr0)) * 8) * 2);
+  const uint32_t vgo = uint32_t((lr0 * rsk + (lpos ^ swz_v(lr0)) * 8) * 2);
   // A tile that runs past Sk loads key row Sk - 1 in place of the missing rows:
   // finite data whose scores the mask sets to -inf (weight 0).
-  auto issue = [&](const uint16_t* src, const uint32_t (&go)[NI], int lbase, int t0, bool guard,
-                   bool is_v) {
-    const uint16_t* base = src + hbk + size_t(t0) * rsk;
+  auto issue = [&](const uint16_t* src, uint32_t go, int lbase, int t0, bool guard, bool is_v) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      uint32_t off = go[i];
-      if (guard) {
-        const int r = (w + GW * i) * RPI + lane / CPR, pos = lane % CPR;
-        const int rc = min(r, Sk - 1 - t0);
-        off = uint32_t((rc * rsk + (pos ^ (is_v ? swz_v(r) : swz_k(r))) * 8) * 2);
+      const uint16_t* base = src + hbk + size_t(t0) * rsk;
+      uint32_t off;
+      if (guard) {  // rows are clamped relative to the tile's first row (< Sk)
+        const int r = GW * RPI * i + lr0, rc = min(r, Sk - 1 - t0);
+        off = uint32_t((rc * rsk + (lpos ^ (is_v ? swz_v(r) : swz_k(r))) * 8) * 2);
+      } else {
+        base += size_t(GW * RPI * i) * rsk;
+        off = go;
       }
       load_lds16(base, off, glds + lbase + (w + GW * i) * 1024);
     }
