@@ -261,6 +261,33 @@ int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, u
                          size_t ws_bytes, void* stream);
 
 /*
+ * usp_attention_fwd_noalloc: usp_attention_fwd_ws with its workspace taken
+ * from device memory the library reserves statically, for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It calls no allocating routine; the
+ * caller still owns q, k, v, o and lse. The same kernels and the same bits
+ * as usp_attention_fwd_ws (and usp_attention_fwd).
+ *   Limit: the bf16 path needs usp_attention_workspace_bytes(in_dt, B, S,
+ *          head_hi - head_lo, D) bytes of scratch, at most
+ *          USP_NOALLOC_SCRATCH_BYTES (192 MiB: the video-DiT share of
+ *          B = 1, S = 32760, 5 heads, D = 128 needs 171.7 MB); larger calls
+ *          fail with USP_EINVAL before any launch (split them into head
+ *          ranges). fp32 inputs need no scratch.
+ *   The scratch is one array per GPU, held from the library's first use on
+ *   that GPU until the process ends, and shared by every call on it: calls
+ *   that may overlap on one GPU (other streams, other threads) race and
+ *   must be serialised by the caller. Its contents do not need clearing.
+ * Arguments, layouts and other errors as usp_attention_fwd, plus: the
+ *   device of `stream` cannot be determined or its scratch address looked
+ *   up -> USP_EHIP.
+ */
+#define USP_NOALLOC_SCRATCH_BYTES (192u << 20)
+int usp_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                              usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S, int32_t h,
+                              int32_t D, int32_t head_lo, int32_t head_hi, float scale, float* lse,
+                              void* stream);
+
+/*
  * Attention with grouped key/value heads (m-star ulysses_attention: q holds
  * Hq heads, k and v Hkv, both divisible by the SP degree, so each rank's head
  * group is [seq, Hq/P, D] against [seq, Hkv/P, D]): as usp_attention_fwd over

@@ -207,6 +207,16 @@ static void check_attention(void) {
   }
   HIP_OK(hipMemcpy(b, chunked_ws_out, n * 4, hipMemcpyDeviceToHost));
   CHECK(memcmp(a, b, n * 4) == 0, "chunked attention with a workspace equals the default bit for bit");
+  /* the no-allocation form reuses chunked_ws_out: its scratch is the library's */
+  CHECK(usp_attention_fwd_noalloc(qkv[0], qkv[1], qkv[2], chunked_ws_out, USP_BF16, USP_F32, B, S, h,
+                                  D, 0, h, 0.0f, NULL, NULL) == USP_OK, "usp_attention_fwd_noalloc");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(b, chunked_ws_out, n * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(a, b, n * 4) == 0, "attention without allocation equals the default bit for bit");
+  CHECK(usp_attention_fwd_noalloc(qkv[0], qkv[1], qkv[2], chunked_ws_out, USP_BF16, USP_F32, 2, 16384,
+                                  8, D, 0, 8, 0.0f, NULL, NULL) == USP_EINVAL &&
+            strstr(usp_last_error(), "scratch") != NULL,
+        "a call beyond the static scratch is rejected");
   HIP_OK(hipFree(chunked_ws_out));
   const size_t nl = (size_t)B * h * S;
   HIP_OK(hipMemcpy(a, lse[0], nl * 4, hipMemcpyDeviceToHost));

@@ -157,6 +157,32 @@ def test_attention_ws_rejects(kw, status):
     assert usp.usp_last_error()
 
 
+def _attn_na(q=FAKE, i=1, out=0, B=1, S=16, h=2, D=64, lo=0, hi=2):
+    return L.usp_attention_fwd_noalloc(q, FAKE, FAKE, FAKE, i, out, B, S, h, D, lo, hi, 0.0, None,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # beyond the static scratch: 2 x 16384 rows x 8 heads at D = 128 (268 MB > 192 MiB),
+    # rejected from the sizes alone, before any device call
+    (dict(B=2, S=16384, h=8, D=128, hi=8), -1),
+    (dict(q=None), -1), (dict(D=96), -5), (dict(lo=1, hi=1), -1), (dict(i=7), -3),
+])
+def test_noalloc_rejects(kw, status):
+    assert _attn_na(**kw) == status
+    msg = usp.usp_last_error()
+    assert msg
+    if kw.get("B") == 2:
+        assert "scratch" in msg and str(192 << 20) in msg
+
+
+def test_noalloc_scratch_limit_in_header():
+    text = open(usp._binding.HEADER).read()
+    assert "#define USP_NOALLOC_SCRATCH_BYTES (192u << 20)" in text
+    # the video-DiT share (B = 1, S = 32760, 5 heads, D = 128) fits
+    assert _ws_bytes(1, 1, 32760, 5, 128)[1] <= 192 << 20
+
+
 def test_chunked_rejects():
     f = L.usp_attention_fwd_chunked
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 16, 5, 64, 0.0, None, 4, None) == -1  # empty chunk

@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.usp_unpack_heads_to_seq_chunk.argtypes = rel_chunk
         L.usp_attention_fwd.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
                                         _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
+        L.usp_attention_fwd_noalloc.argtypes = L.usp_attention_fwd.argtypes
         L.usp_attention_fwd_chunked.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
                                                 _i64, _i64, _i32, _i32, _f32, _vp, _i32, _vp]
         L.usp_attention_fwd_chunked_ws.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
@@ -359,6 +360,18 @@ def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float =
     _check(lib().usp_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o), B, S,
                                    h, D, head_lo, hi, scale, _ptr(lse), _stream(q, stream)),
            "usp_attention_fwd")
+
+
+def usp_attention_fwd_noalloc(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
+                              lse=None, stream=None) -> None:
+    """usp_attention_fwd_ws with the library's static scratch as workspace
+    (no allocation; calls that overlap on one GPU race)."""
+    _attn_io(q, k, v, o, lse)
+    B, S, h, D = q.shape
+    hi = h if head_hi is None else head_hi
+    _check(lib().usp_attention_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q), _dtype(o),
+                                           B, S, h, D, head_lo, hi, scale, _ptr(lse),
+                                           _stream(q, stream)), "usp_attention_fwd_noalloc")
 
 
 def usp_attention_workspace_bytes(in_dtype: int, B: int, S: int, heads: int, D: int) -> int:

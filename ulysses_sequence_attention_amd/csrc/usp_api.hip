@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "usp_internal.h"
@@ -318,6 +319,67 @@ int usp_attention_fwd_ws(const void* q, const void* k, const void* v, void* o, u
     if (!aligned16(ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
   } else {
     a.ws = nullptr;  // the fp32 path needs none
+  }
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+// ---- usp_attention_fwd_noalloc: the key-half workspace in a static array ----
+namespace usp {
+namespace {
+
+// Device memory the library reserves on every GPU it runs on, for callers
+// that cannot allocate (graph capture, tight serving loops). In host code
+// the array's name is a host-side stand-in, not a device address: host code
+// only ever uses the per-device address from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = size_t(USP_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The scratch address on the device that runs `stream`, looked up once per
+// device with that device current.
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(USP_EHIP, "hipGetDevice failed");
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess)
+    return fail(USP_EHIP, "hipStreamGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(USP_EINVAL, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return fail(USP_EHIP, "hipSetDevice(%d) failed", dev);
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(USP_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return USP_OK;
+}
+
+}  // namespace
+}  // namespace usp
+
+int usp_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                              usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t S, int32_t h,
+                              int32_t D, int32_t head_lo, int32_t head_hi, float scale, float* lse,
+                              void* stream) {
+  using namespace usp;
+  AttnArgs a{q, k, v, o, lse, B, S, S, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0, h};
+  if (int st = check_attention(a)) return st;
+  if (in_dt == USP_BF16) {
+    const size_t need = attention_bf16_ws_bytes(B, S, head_hi - head_lo, D);
+    if (need > kScratchBytes)
+      return fail(USP_EINVAL, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                  need, kScratchBytes);
+    if (int st = scratch_address((hipStream_t)stream, &a.ws)) return st;
+    a.ws_bytes = kScratchBytes;
   }
   if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
   if (int st = run_attention(a, (hipStream_t)stream)) return st;
