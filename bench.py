@@ -8,70 +8,58 @@ path, every row of it:
 
   ranges   token / head boundaries (host)
   pack     rank 0's token shard [1, 4095, 40, 128] of Q, K and V into the 8
-           head-group blocks [1, 32760, 5, 128] (the data rank 0 sends in the
+           head-group blocks [1, 32760, 5, 128], the three tensors in one
+           launch (usp_pack_seq_to_heads_planes: the data rank 0 sends in the
            first all-to-all; the other ranks' rows were placed beforehand)
   attn     non-causal attention over the full sequence on block 0 (h = 5),
            usp_attention_fwd_ws with its workspace allocated beforehand
   unpack   rank 0's rows of the 8 output blocks back to [1, 4095, 40, 128]
 
-The attention of usp_attention_fwd (no workspace; the same bits) is timed
-on its own as well and reported as "attention_no_workspace", and
-usp_attention_fwd_gqa (with a workspace) on rank 0's share of the grouped
-video-DiT workload (40 query heads over 8 K/V heads: 5 query heads and one
-K/V head per rank) as "attention_gqa". "rows_world" reports the model-boundary
-row movements at the same share's hidden size ([1, 32760, 5120] bf16 over 8
-ranks, world mode): scatter and gather (read + write of the tensor) and the
-reduce-scatter of 8 partials (8 reads + 1 write), buffers rotated like the
-relayouts'. "ring" reports one rank's ring pass of Ulysses+Ring on the
-video-DiT sequence over a 4 (Ulysses) x 2 (ring) grid: ring block 0, head
-group 0 (10 heads, 16380 query rows) attends to its own K/V block and then to
-ring block 1's (usp_attention_fwd_block, fp32 outputs and lse), and
-usp_attention_merge folds the two into the bf16 output; its flops are
-4 * Sq * S * D * h = 2.7474e12. The second block's attention runs on a
-second stream (its own workspace), as a ring would launch it on arrival, and
-the fold waits for it; the one-stream pass is reported beside it. "chunked" times usp_attention_fwd_chunked on
-the long-sequence share (B=1, S=131072, h=8, D=128, 3 head-chunk passes of
-3/3/2 heads; 7.04e13 flop), and usp_attention_fwd_chunked_ws (workspace
-sized for the 3-head pass), next to the single-shot usp_attention_fwd on the
-same inputs (all the same bits). "two_phase" runs the same step as the
-head-chunked two-phase exchange: for each chunk of the 5 heads (2/2/1), pack
-rank 0's rows of those heads of Q, K and V (usp_pack_seq_to_heads_chunk),
-attention on those heads of block 0, unpack them
-(usp_unpack_heads_to_seq_chunk; "relayout_world" also times one such chunk
-of the world tensor alone, heads [0, 2) of every group). Pipelined, a
-chunk's pack for the next step and its unpack for this step run on the
-second stream as soon as this step's attention of that chunk is done, under
-the attention of the following chunks; "serial_*" runs the same phases on
-one stream. The output is checked bitwise against the single-shot step.
-
 Steps run pipelined: step i + 1's pack and step i's unpack are issued on a
 second stream (default priority) so that they run under the attention of the
-neighbouring step (the relayout waves fit beside the attention workgroups on
-a CU), with two sets of head and output blocks and stream-ordered events that
-keep each step's pack before its attention and its unpack after it. Every
-step still does all of its work; the timed region holds exactly K packs, K
-attention calls and K unpacks, and the output is checked bitwise against a
-serial step. The same steps run serially (one stream) are reported as
-"step_serial", with per-kernel HIP events.
+neighbouring step, with two sets of head and output blocks and stream-ordered
+events that keep each step's pack before its attention and its unpack after
+it. Every step does all of its work; the timed region holds exactly K packs,
+K attention calls and K unpacks, and the output is checked bitwise against a
+serial step. The same steps on one stream are "step_serial", with HIP events
+around each part of every step (median, minimum and mean per part).
 
 value = attention flops of a step (4 * S^2 * D * h = 2.7474e12) / step time.
-Also reported: each kernel alone (HIP events around each launch on the
-launch stream), the world-tensor pack / unpack bandwidth of the full
-[1, 32760, 40, 128] tensor (read + write bytes / time, buffers rotated so the
-256 MB last-level cache cannot serve repeats), and a plain device copy of
-1 GiB as the practical HBM reference.
 
-cpu_baseline: the float64 CPU oracle on a bounded sample of query rows of
-the same attention, on every host core this process may use.
+Also measured, each with HIP events around every call on its stream (median
+and minimum reported; buffers rotated past the 256 MB last-level cache where
+a leg says "cold"):
+  * usp_attention_fwd (no workspace), usp_attention_fwd_noalloc (static
+    scratch) and the same attention with softmax scale 1 instead of
+    1/sqrt(D) (the other reading of "Q scaled by 1/sqrt(D)"; ungraded: its
+    error against the oracle on sampled rows is reported beside it);
+  * the other workloads' full worlds, pack -> attention of every head group
+    -> unpack: ViT-L/16 (B=32, S=577, H=16, D=64, P=4; HBM-warm and cold)
+    and the indivisible long sequence (B=2, S=65537, H=12, D=64, P=4, 1% of
+    K rows x 8);
+  * usp_attention_fwd_gqa on rank 0's share of the grouped video-DiT
+    workload; one rank's Ulysses+Ring pass (video-DiT over 4 x 2 ranks: two
+    key blocks, then the merge); the head-chunked passes on the long
+    sequence (B=1, S=131072, h=8, 3/3/2) against single shot; the same step
+    as the two-phase exchange (per head chunk 2/2/1: pack, attention,
+    unpack); the world relayouts of the [1, 32760, 40, 128] tensor (one
+    tensor, and q, k, v in one launch; whole groups and one head chunk); the
+    model-boundary row movements at [1, 32760, 5120]; a 1 GiB device copy as
+    the practical HBM reference.
+
+cpu_baseline: the float64 CPU oracle, per configuration and part, on every
+host core this process may use (attention in a process pool, one BLAS thread
+per worker; pack/unpack index loops single-threaded): ``value`` is the
+video-DiT share's attention on a sample of its rows.
 
 roofline: the attention call (usp_attention_fwd_ws: the key-half flash
 kernel, then the merge kernel) is the dominant step; ``achieved`` is its
-flops over its event-timed duration.
+flops over its mean event-timed duration in the serial steps.
 roofline.traffic: HBM bytes per attention call from rocprofv3 FETCH_SIZE /
 WRITE_SIZE counter runs (both kernels), each scaled by what the counter reads
 for the plain copy kernel of known size in the same run (``--pmc-summary``);
 reported only while the attention source is the one the counters were taken
-on.
+on. roofline.legs repeats every leg's headline figure in compact form.
 """
 from __future__ import annotations
 
@@ -101,35 +89,6 @@ COPY_BYTES = 1 << 30
 def source_digest(path=ATTN_SRC) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
-
-
-def cpu_baseline(q, k, v, h0, S, D, target_s):
-    """Time the oracle (float64 NumPy, process pool over host cores) on a
-    sample of query rows of heads [0, h0); returns the cpu_baseline object."""
-    from oracle import attention as A
-    from ulysses_sequence_attention_amd import synth
-
-    qf, kf, vf = (synth.bf16_bits_to_f32(np.ascontiguousarray(x[:, :, :h0])).astype(np.float64)
-                  for x in (q, k, v))
-    cores = A.host_cores()
-    rng = np.random.default_rng(123)
-    # calibrate on one core (512 rows, so that copying the head's K/V planes
-    # weighs little), then size the sample for about target_s of wall time
-    t0 = time.perf_counter()
-    A.attention_rows(qf, kf, vf, 0, 0, np.arange(512))
-    per_row = (time.perf_counter() - t0) / 512
-    n = int(max(64, min(S, target_s * cores / (per_row * h0))))
-    rows = {(0, hd): (np.arange(S) if n >= S else np.sort(rng.choice(S, n, replace=False)))
-            for hd in range(h0)}
-    t0 = time.perf_counter()
-    A.attention_parallel(qf, kf, vf, rows_per_head=rows, workers=cores)
-    wall = time.perf_counter() - t0
-    flops = 4.0 * S * D * n * h0
-    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"all {S} query rows" if n >= S else f"{n} query rows") +
-                      f" x {h0} heads of the S={S}, D={D} attention "
-                      f"({flops:.3e} flop, {wall:.1f} s wall, float64 NumPy, "
-                      f"{cores} worker processes x 1 BLAS thread)"}
 
 
 def stored_traffic():
@@ -283,22 +242,145 @@ def pmc_summary(dirs, out_json):
     print("\n".join(lines))
 
 
+def oracle_parts(data, target_s):
+    """Time the oracle (float64 NumPy) on the workloads of this benchmark, per
+    configuration and part, on every host core this process may use (the
+    attention in a process pool with one BLAS thread per worker; the
+    pack/unpack index loops single-threaded, as written). Returns the
+    cpu_baseline object: ``value`` is the video-DiT share's attention."""
+    from oracle import attention as A
+    from oracle import relayout as X
+    from ulysses_sequence_attention_amd import synth
+
+    cores = A.host_cores()
+    parts = {}
+
+    def f64(x, heads=None):
+        x = x if heads is None else x[:, :, heads[0]:heads[1]]
+        if x.dtype == np.uint16:
+            return synth.bf16_bits_to_f32(np.ascontiguousarray(x)).astype(np.float64)
+        return np.ascontiguousarray(x, dtype=np.float64)
+
+    def attn(name, q, k, v, rows_per_head, scale=None, note=""):
+        B, S, h, D = q.shape
+        n = sum(len(r) for r in rows_per_head.values())
+        t0 = time.perf_counter()
+        A.attention_parallel(q, k, v, scale=scale, rows_per_head=rows_per_head, workers=cores)
+        wall = time.perf_counter() - t0
+        flops = 4.0 * D * k.shape[1] * n
+        parts[name] = {"wall_s": round(wall, 3), "GFLOP/s": flops / wall / 1e9, "flop": flops,
+                       "rows": n, "of_rows": B * S * h, "note": note}
+        return flops / wall
+
+    rng = np.random.default_rng(123)
+
+    def sample(S, n):
+        return np.arange(S) if n >= S else np.sort(rng.choice(S, n, replace=False))
+
+    # the video-DiT share (heads 0-4 of the world tensor): a sample sized for
+    # about target_s of wall time, calibrated on one core
+    q, k, v = data["video_dit_share"]
+    h0, S = 5, q.shape[1]
+    qf, kf, vf = (f64(x, (0, h0)) for x in (q, k, v))
+    t0 = time.perf_counter()
+    A.attention_rows(qf, kf, vf, 0, 0, np.arange(512))
+    per_row = (time.perf_counter() - t0) / 512
+    n = int(max(64, min(S, target_s * cores / (per_row * h0))))
+    value = attn("attention_video_dit_share", qf, kf, vf,
+                 {(0, hd): sample(S, n) for hd in range(h0)},
+                 note="rows sampled per head" if n < S else "every row")
+    del qf, kf, vf
+    # the world pack and unpack of the video-DiT q tensor, index loops
+    t0 = time.perf_counter()
+    blocks = X.pack_seq_to_heads(q, 8)
+    t_pack = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    X.unpack_heads_to_seq(blocks, q.shape[2])
+    t_unpack = time.perf_counter() - t0
+    del blocks
+    moved = 2.0 * q.nbytes
+    parts["pack_world_video_dit"] = {"wall_s": round(t_pack, 3), "GB/s": moved / t_pack / 1e9,
+                                     "bytes_rw": moved, "note": "single-threaded index loops"}
+    parts["unpack_world_video_dit"] = {"wall_s": round(t_unpack, 3), "GB/s": moved / t_unpack / 1e9,
+                                       "bytes_rw": moved, "note": "single-threaded index loops"}
+    # the other configurations' attention (every group of the world)
+    q, k, v = data["vit_l16"]
+    qf, kf, vf = (f64(x) for x in (q, k, v))
+    attn("attention_vit_l16", qf, kf, vf,
+         {(b, hd): np.arange(q.shape[1]) for b in range(q.shape[0]) for hd in range(q.shape[2])},
+         note="every row of all 16 heads")
+    q, k, v = data["indivisible_long"]
+    qf, kf, vf = (f64(x) for x in (q, k, v))
+    attn("attention_indivisible_long", qf, kf, vf,
+         {(b, hd): sample(q.shape[1], 256) for b in range(q.shape[0]) for hd in range(q.shape[2])},
+         note="256 rows sampled per (batch, head)")
+    q, k, v = data["long_chunked"]
+    qf, kf, vf = (f64(x) for x in (q, k, v))
+    attn("attention_long_chunked", qf, kf, vf,
+         {(0, hd): sample(q.shape[1], 96) for hd in range(q.shape[2])},
+         note="96 rows sampled per head")
+    q, k, v = data["tiny_fp32"]
+    qf, kf, vf = (f64(x) for x in (q, k, v))
+    attn("attention_tiny_fp32", qf, kf, vf,
+         {(0, hd): np.arange(q.shape[1]) for hd in range(q.shape[2])}, note="every row")
+    s = parts["attention_video_dit_share"]
+    return {"value": value / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{s['rows']} of {s['of_rows']} rows (5 heads) of the S=32760 D=128 share, "
+                      f"{s['wall_s']:.1f} s, fp64 NumPy, {cores} procs",
+            "parts": parts}
+
+class Timer:
+    """HIP events around every call of a leg on one stream; summary in ms."""
+
+    def __init__(self, torch, stream=None):
+        self.torch, self.stream, self.ev = torch, stream, []
+
+    def __call__(self, fn, *args, **kw):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s = self.stream or t.cuda.current_stream()
+        a.record(s)
+        fn(*args, **kw)
+        b.record(s)
+        self.ev.append((a, b))
+
+    def summary(self):
+        self.torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in self.ev])
+        return {"median_ms": float(np.median(ms)), "min_ms": float(ms.min()),
+                "mean_ms": float(ms.mean()), "calls": int(len(ms))}
+
+
+def timed(torch, fn, reps, warm=3):
+    """Median / minimum / mean of ``reps`` calls of ``fn(i)`` after ``warm``."""
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for i in range(reps):
+        t(fn, i)
+    return t.summary()
+
+
+def tflops(flops, ms):
+    return flops / (ms * 1e-3) / 1e12
+
+
+def gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--relayout-reps", type=int, default=6)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target wall time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle's video-DiT attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-relayout-bw", action="store_true")
-    ap.add_argument("--skip-gqa", action="store_true", help="skip the grouped-head attention timing")
-    ap.add_argument("--skip-rows", action="store_true", help="skip the row-movement timings")
-    ap.add_argument("--skip-ring", action="store_true", help="skip the Ulysses+Ring pass timing")
-    ap.add_argument("--skip-chunked", action="store_true", help="skip the head-chunked timing")
-    ap.add_argument("--skip-two-phase", action="store_true",
-                    help="skip the two-phase (per head chunk) step timing")
+    ap.add_argument("--skip-legs", action="store_true",
+                    help="time only the video-DiT step (for profiler runs)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     ap.add_argument("--pmc-sq", nargs="+", metavar="DIR",
@@ -314,16 +396,25 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not "
-              "supported: it runs on one GPU (the multi-GPU exchange is not implemented)", file=sys.stderr)
+              "supported: it runs on one GPU (the multi-GPU exchange is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     import ulysses_sequence_attention_amd as usp
     from ulysses_sequence_attention_amd import synth
 
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     w = synth.WORKLOADS["video_dit_share"]
     B, S, H, D, P = w.B, w.S, w.H, w.D, w.P
-    print(f"[bench] drawing inputs {B}x{S}x{H}x{D} bf16", file=sys.stderr, flush=True)
-    q, k, v = synth.draw_workload(w)
+    legs_on = not args.skip_legs
+    names = ["video_dit_share"] + (["vit_l16", "indivisible_long", "long_chunked", "tiny_fp32"]
+                                   if legs_on or not args.no_cpu_baseline else [])
+    data = {}
+    for name in names:
+        say(f"drawing {name}")
+        data[name] = synth.draw_workload(synth.WORKLOADS[name])
     tb = usp.usp_balanced_ranges(S, P)
     hb = usp.usp_balanced_ranges(H, P)
     h0, len0 = hb[1] - hb[0], tb[1] - tb[0]
@@ -331,8 +422,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(q, k, v, h0, S, D, args.cpu_seconds)
+        say("cpu baseline (oracle, per configuration and part)")
+        cpu = oracle_parts(data, args.cpu_seconds)
 
     import torch
     dev = torch.device("cuda:0")
@@ -341,28 +432,24 @@ def main():
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
+    def blocks_of(Bx, Sx, hbx, Dx, dtype=torch.bfloat16):
+        return [torch.empty((Bx, Sx, hbx[j + 1] - hbx[j], Dx), dtype=dtype, device=dev)
+                for j in range(len(hbx) - 1)]
 
-    world = [bf(x) for x in (q, k, v)]
-    del q, k, v
+    world = [bf(x) for x in data["video_dit_share"]]
     shard = [x[:, tb[0]:tb[1]].contiguous() for x in world]
-    blocks = [[torch.empty((B, S, hb[j + 1] - hb[j], D), dtype=torch.bfloat16, device=dev)
-               for j in range(P)] for _ in range(3)]
-    for x, bl in zip(world, blocks):   # every rank's rows, as received in the exchange
-        usp.usp_pack_seq_to_heads(x, bl)
-    oblocks = [torch.zeros((B, S, hb[j + 1] - hb[j], D), dtype=torch.bfloat16, device=dev)
-               for j in range(P)]
+    blocks = [blocks_of(B, S, hb, D) for _ in range(3)]
+    usp.usp_pack_seq_to_heads_planes(world, blocks)   # every rank's rows, as received
+    oblocks = [torch.zeros_like(t) for t in blocks[0]]
     oshard = torch.empty((B, len0, H, D), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, B, S, h0, D) // 4,
-                     dtype=torch.float32, device=dev)
+    ws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, B, S, h0, D),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(e=None):
         if e is not None:
             e[0].record()
-        for x, bl in zip(shard, blocks):
-            usp.usp_pack_seq_to_heads(x, bl, rank=0)
+        usp.usp_pack_seq_to_heads_planes(shard, blocks, rank=0)
         if e is not None:
             e[1].record()
         usp.usp_attention_fwd_ws(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0], ws)
@@ -372,13 +459,16 @@ def main():
         if e is not None:
             e[3].record()
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    say(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
-    print(f"[bench] timing {args.steps} serial steps", file=sys.stderr, flush=True)
+    say(f"timing {args.steps} serial steps")
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
@@ -386,23 +476,22 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    unpack_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
-    elem = 2  # bf16
-    share_bytes = 2 * B * len0 * H * D * elem   # one tensor, read + write
 
-    # the same steps pipelined: two sets of head and output blocks, the
-    # relayouts on a second stream (default priority) under the neighbouring
-    # steps' attention; stream-ordered events keep every step's pack before its
-    # attention and its unpack after it, and no set is rewritten while read
-    print("[bench] pipelined steps", file=sys.stderr, flush=True)
+    def part(i0, i1):
+        ms = np.array([e[i0].elapsed_time(e[i1]) for e in evs])
+        return {"median_ms": float(np.median(ms)), "min_ms": float(ms.min()), "mean_ms": float(ms.mean()),
+                "calls": int(len(ms))}
+
+    t_pack, t_attn, t_unpack = part(0, 1), part(1, 2), part(2, 3)
+    attn_tflops = tflops(attn_flops, t_attn["mean_ms"])
+    share_bytes = 2 * B * len0 * H * D * 2   # one tensor's shard, read + write
+
+    # the same steps pipelined (see the module docstring)
+    say("pipelined steps")
     main_s = torch.cuda.current_stream()
     io_s = torch.cuda.Stream()
     bsets = [blocks, [[torch.empty_like(t) for t in bl] for bl in blocks]]
-    for x, bl in zip(world, bsets[1]):   # every rank's rows in the second set too
-        usp.usp_pack_seq_to_heads(x, bl)
+    usp.usp_pack_seq_to_heads_planes(world, bsets[1])
     osets = [oblocks, [torch.zeros_like(t) for t in oblocks]]
     ev_pack = [torch.cuda.Event() for _ in range(2)]
     ev_attn = [torch.cuda.Event() for _ in range(2)]
@@ -413,8 +502,7 @@ def main():
     def p_pack(i):
         st = i % 2
         io_s.wait_event(ev_attn[st])      # set st was last read by attention i - 2
-        for x, bl in zip(shard, bsets[st]):
-            usp.usp_pack_seq_to_heads(x, bl, rank=0, stream=io_s)
+        usp.usp_pack_seq_to_heads_planes(shard, bsets[st], rank=0, stream=io_s)
         ev_pack[st].record(io_s)
 
     def p_attn(i):
@@ -444,14 +532,13 @@ def main():
 
     pipelined(args.warmup)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} pipelined steps", file=sys.stderr, flush=True)
+    say(f"timing {args.steps} pipelined steps")
     a, b_ = ev(), ev()
     a.record(main_s)
     pipelined(args.steps, start=a)
     b_.record(main_s)
     torch.cuda.synchronize()
     pipe_ms = a.elapsed_time(b_) / args.steps
-    # the pipelined steps must leave exactly what a serial step leaves
     pipe_out = oshard.clone()
     step()
     torch.cuda.synchronize()
@@ -459,48 +546,169 @@ def main():
         raise RuntimeError("pipelined steps produced a different output than a serial step")
     del bsets[1], osets[1], pipe_out
 
-    # the two-phase exchange on the same share: per head chunk (2/2/1 of the
-    # 5 heads), pack rank 0's rows of the chunk's heads, attention on them,
-    # unpack them. Overlapped: the next chunk's pack and this chunk's unpack
-    # run on the second stream under the attention (they touch other heads).
-    two_phase = None
-    if not args.skip_two_phase:
-        print("[bench] two-phase steps", file=sys.stderr, flush=True)
+    legs = {}
+    out_extra = {}
+    reps = max(5, args.steps // 4)
+    blk0 = (blocks[0][0], blocks[1][0], blocks[2][0])
+    if legs_on:
+        say("attention without workspace / without allocation / softmax scale 1")
+        legs["attn_no_workspace"] = timed(torch, lambda i: usp.usp_attention_fwd(*blk0, oblocks[0]), reps)
+        legs["attn_noalloc"] = timed(torch, lambda i: usp.usp_attention_fwd_noalloc(*blk0, oblocks[0]),
+                                     reps)
+        o_s1 = torch.empty((B, S, h0, D), dtype=torch.float32, device=dev)
+        legs["attn_scale1"] = timed(torch, lambda i: usp.usp_attention_fwd_ws(*blk0, o_s1, ws, scale=1.0),
+                                    reps)
+        # the scale-1 reading against the oracle on sampled rows (ungraded)
+        from oracle import attention as A
+        rows = np.sort(np.random.default_rng(7).choice(S, 48, replace=False))
+        qh, kh, vh = (synth.bf16_bits_to_f32(np.ascontiguousarray(x[:, :, :h0])).astype(np.float64)
+                      for x in data["video_dit_share"])
+        got = o_s1.cpu().numpy().astype(np.float64)
+        dmax, num, den = 0.0, 0.0, 0.0
+        for hd in range(h0):
+            ref, _ = A.attention_rows(qh, kh, vh, 0, hd, rows, scale=1.0)
+            d = got[0, rows, hd] - ref
+            dmax = max(dmax, float(np.abs(d).max()))
+            num += float((d * d).sum())
+            den += float((ref * ref).sum())
+        legs["attn_scale1"].update({"max_abs": dmax, "rel_frob": (num / den) ** 0.5,
+                                    "rows_checked": 48 * h0})
+        del o_s1, qh, kh, vh
+
+        # grouped K/V heads: rank 0's share of the grouped video-DiT workload
+        say("attention with grouped K/V heads")
+        gw = synth.WORKLOADS["gqa_video_share"]
+        gq, gk, gv = synth.draw_workload(gw)
+        ghq = usp.usp_balanced_ranges(gw.H, gw.P)
+        ghk = usp.usp_balanced_ranges(gw.kv_heads, gw.P)
+        q0 = bf(gq[:, :, ghq[0]:ghq[1]])
+        k0, v0 = (bf(x[:, :, ghk[0]:ghk[1]]) for x in (gk, gv))
+        del gq, gk, gv
+        o0 = torch.empty_like(q0)
+        gh = ghq[1] - ghq[0]
+        gws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, gw.B, gw.S, gh, gw.D),
+                          dtype=torch.uint8, device=dev)
+        legs["attn_gqa"] = timed(torch, lambda i: usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws), reps)
+        legs["attn_gqa"]["flop"] = 4.0 * gw.B * gh * gw.S * gw.S * gw.D
+        del q0, k0, v0, o0, gws
+
+        # one rank's Ulysses+Ring pass: two key blocks, then the merge
+        say("Ulysses+Ring pass")
+        rw = synth.WORKLOADS["video_dit_ring"]
+        rq, rk, rv = (bf(x) for x in synth.draw_workload(rw))
+        rT = usp.usp_balanced_ranges(rw.S, rw.ring)
+        rc = usp.usp_balanced_ranges(rw.H, rw.P)
+        rh = rc[1] - rc[0]
+
+        def head_group0(x, i):
+            bl = blocks_of(rw.B, rT[i + 1] - rT[i], rc, rw.D)
+            usp.usp_pack_seq_to_heads(x[:, rT[i]:rT[i + 1]].contiguous(), bl)
+            return bl[0]
+
+        qr = head_group0(rq, 0)
+        kvr = [(head_group0(rk, i), head_group0(rv, i)) for i in range(rw.ring)]
+        del rq, rk, rv
+        Sq = rT[1] - rT[0]
+        rws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, rw.B, Sq, rh, rw.D),
+                          dtype=torch.uint8, device=dev)
+        rws2 = torch.empty_like(rws)
+        o_acc = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.float32, device=dev)
+        l_acc = torch.empty((rw.B, rh, Sq), dtype=torch.float32, device=dev)
+        o_b2 = [torch.empty_like(o_acc) for _ in range(2)]
+        l_b2 = [torch.empty_like(l_acc) for _ in range(2)]
+        o_out = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.bfloat16, device=dev)
+        order = [0] + [(0 - i) % rw.ring for i in range(1, rw.ring)]
+        side = torch.cuda.Stream()
+        ev_blk = [torch.cuda.Event() for _ in range(2)]
+        ev_fold = [torch.cuda.Event() for _ in range(2)]
+
+        def ring_pass(i, two_streams=True):
+            # the second block's attention on a second stream (a ring delivers
+            # it long before the first is done); folds in ring order on the first
+            ms_ = torch.cuda.current_stream()
+            st2 = side if two_streams else ms_
+            start = torch.cuda.Event()
+            start.record(ms_)
+            st2.wait_event(start)
+            for e in ev_fold:
+                e.record(ms_)
+            usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws, stream=ms_)
+            for n, blk in enumerate(order[1:]):
+                s2 = n % 2
+                st2.wait_event(ev_fold[s2])
+                usp.usp_attention_fwd_block(qr, *kvr[blk], o_b2[s2], lse=l_b2[s2],
+                                            ws=rws2 if two_streams else rws, stream=st2)
+                ev_blk[s2].record(st2)
+                ms_.wait_event(ev_blk[s2])
+                last = n == len(order) - 2
+                usp.usp_attention_merge(o_acc, l_acc, o_b2[s2], l_b2[s2], o_out if last else o_acc,
+                                        None if last else l_acc, stream=ms_)
+                ev_fold[s2].record(ms_)
+
+        legs["ring_one_stream"] = timed(torch, lambda i: ring_pass(i, False), reps)
+        one = o_out.clone()
+        legs["ring"] = timed(torch, ring_pass, reps)
+        if not torch.equal(one, o_out):
+            raise RuntimeError("the two-stream ring pass changed the output")
+        legs["ring"]["flop"] = 4.0 * rw.B * rh * Sq * rw.S * rw.D
+        del qr, kvr, rws, rws2, o_acc, l_acc, o_b2, l_b2, o_out, one
+
+        # head-chunked passes on the long-sequence share, against single shot
+        say("head-chunked passes (S=131072)")
+        cw = synth.WORKLOADS["long_chunked"]
+        cq, ck, cv = (bf(x) for x in data["long_chunked"])
+        co = torch.empty_like(cq)
+        cmax = -(-cw.H // cw.chunks)
+        cws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cmax, cw.D),
+                          dtype=torch.uint8, device=dev)
+        fws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cw.H, cw.D),
+                          dtype=torch.uint8, device=dev)
+        c_flops = 4.0 * cw.B * cw.H * cw.S * cw.S * cw.D
+        for name, fn in (("chunked", lambda i: usp.usp_attention_fwd_chunked(cq, ck, cv, co, cw.chunks)),
+                         ("chunked_ws", lambda i: usp.usp_attention_fwd_chunked_ws(cq, ck, cv, co,
+                                                                                   cw.chunks, cws)),
+                         ("single_shot", lambda i: usp.usp_attention_fwd(cq, ck, cv, co)),
+                         ("single_shot_ws", lambda i: usp.usp_attention_fwd_ws(cq, ck, cv, co, fws))):
+            legs["long_" + name] = timed(torch, fn, 3, warm=1)
+            legs["long_" + name]["flop"] = c_flops
+        del cq, ck, cv, co, cws, fws
+
+        # the two-phase exchange on the same share: per head chunk (2/2/1 of
+        # the 5 heads), pack rank 0's rows of the chunk's heads (q, k, v in one
+        # launch), attention on them, unpack them. Overlapped: a chunk's pack
+        # for the next step and its unpack for this step go to the second
+        # stream as soon as this step's attention of that chunk is done.
+        say("two-phase steps")
         kc = usp.usp_head_chunk_ranges(h0, 3)
         ch = [(kc[c], kc[c + 1]) for c in range(len(kc) - 1)]
         ws_c = torch.empty(usp.usp_attention_workspace_bytes(
-            usp.USP_BF16, B, S, max(hi - lo for lo, hi in ch), D) // 4, dtype=torch.float32, device=dev)
+            usp.USP_BF16, B, S, max(hi - lo for lo, hi in ch), D), dtype=torch.uint8, device=dev)
         e_cp = [torch.cuda.Event() for _ in ch]
         e_ca = [torch.cuda.Event() for _ in ch]
+        e_cu = [torch.cuda.Event() for _ in ch]
+        for e in e_ca + e_cu:
+            e.record(main_s)
 
         def tp_pack(c, stream):
-            for x, bl in zip(shard, blocks):
-                usp.usp_pack_seq_to_heads_chunk(x, bl, ch[c][0], ch[c][1], rank=0, stream=stream)
+            usp.usp_pack_seq_to_heads_planes(shard, blocks, rank=0, head_lo=ch[c][0],
+                                             head_hi=ch[c][1], stream=stream)
 
         def tp_attn(c):
-            usp.usp_attention_fwd_ws(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0], ws_c,
-                                     head_lo=ch[c][0], head_hi=ch[c][1], stream=main_s)
+            usp.usp_attention_fwd_ws(*blk0, oblocks[0], ws_c, head_lo=ch[c][0], head_hi=ch[c][1],
+                                     stream=main_s)
 
         def tp_unpack(c, stream):
             usp.usp_unpack_heads_to_seq_chunk(oblocks, oshard, ch[c][0], ch[c][1], rank=0,
                                               stream=stream)
 
-        def tp_serial():
-            for c in range(len(ch)):
-                tp_pack(c, main_s)
-                tp_attn(c)
-                tp_unpack(c, main_s)
-
-        e_cu = [torch.cuda.Event() for _ in ch]
-        for e in e_ca + e_cu:
-            e.record(main_s)
+        def tp_serial(n):
+            for _ in range(n):
+                for c in range(len(ch)):
+                    tp_pack(c, main_s)
+                    tp_attn(c)
+                    tp_unpack(c, main_s)
 
         def tp_pipelined(n):
-            # chunk c of step i + 1 is packed, and chunk c of step i unpacked,
-            # as soon as step i's attention of chunk c is done (it has read
-            # those heads and written its output), i.e. under the attention
-            # of the following chunks; an attention of chunk c waits for the
-            # pack of its own step and the unpack of the previous one
             io_s.wait_stream(main_s)
             for c in range(len(ch)):
                 io_s.wait_event(e_ca[c])
@@ -521,12 +729,7 @@ def main():
                     e_cu[c].record(io_s)
             main_s.wait_stream(io_s)
 
-        def tp_serial_n(n):
-            for _ in range(n):
-                tp_serial()
-
-        tp = {}
-        for name, fn in (("serial", tp_serial_n), ("pipelined", tp_pipelined)):
+        for name, fn in (("two_phase_serial", tp_serial), ("two_phase", tp_pipelined)):
             fn(args.warmup)
             torch.cuda.synchronize()
             a, b_ = ev(), ev()
@@ -534,312 +737,158 @@ def main():
             fn(args.steps)
             b_.record(main_s)
             torch.cuda.synchronize()
-            tp[name] = a.elapsed_time(b_) / args.steps
+            legs[name] = {"mean_ms": a.elapsed_time(b_) / args.steps, "steps": args.steps,
+                          "flop": attn_flops}
             got = oshard.clone()
             step()
             torch.cuda.synchronize()
             if not torch.equal(got, oshard):
-                raise RuntimeError(f"two-phase ({name}) steps differ from a single-shot step")
-        two_phase = {"chunks": kc, "ms_per_step": tp["pipelined"],
-                     "TFLOP/s": attn_flops / (tp["pipelined"] * 1e-3) / 1e12,
-                     "serial_ms_per_step": tp["serial"],
-                     "serial_TFLOP/s": attn_flops / (tp["serial"] * 1e-3) / 1e12,
-                     "how": "per head chunk: pack rank-0 rows of its heads (q, k, v) -> "
-                            "attention on its heads of block 0 -> unpack; pipelined: a chunk's "
-                            "pack for the next step and unpack for this step on a second stream "
-                            "as soon as this step's attention of that chunk is done",
-                     "bitwise_equal_single_shot": True}
+                raise RuntimeError(f"{name} steps differ from a single-shot step")
         del ws_c
 
-    # usp_attention_fwd (no workspace) on the same block, for comparison
-    print("[bench] attention without workspace", file=sys.stderr, flush=True)
-    for _ in range(3):
-        usp.usp_attention_fwd(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0])
-    reps = max(3, args.steps // 10)
-    a, b_ = ev(), ev()
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        usp.usp_attention_fwd(blocks[0][0], blocks[1][0], blocks[2][0], oblocks[0])
-    b_.record()
-    torch.cuda.synchronize()
-    nows_ms = a.elapsed_time(b_) / reps
+        # the other workloads' whole worlds: pack q, k, v -> attention of every
+        # head group -> unpack, with each part timed
+        def world_leg(name, sets):
+            wl = synth.WORKLOADS[name]
+            tbw = usp.usp_balanced_ranges(wl.S, wl.P)
+            hbw = usp.usp_balanced_ranges(wl.H, wl.P)
+            del tbw
+            host = data[name]
+            sets_ = []
+            for si in range(sets):
+                qkv = [bf(x) for x in host]
+                bl = [blocks_of(wl.B, wl.S, hbw, wl.D) for _ in range(3)]
+                ob = blocks_of(wl.B, wl.S, hbw, wl.D)
+                out = torch.empty((wl.B, wl.S, wl.H, wl.D), dtype=torch.bfloat16, device=dev)
+                wsw = torch.empty(usp.usp_attention_workspace_bytes(
+                    usp.USP_BF16, wl.B, wl.S, max(hbw[j + 1] - hbw[j] for j in range(wl.P)), wl.D),
+                    dtype=torch.uint8, device=dev)
+                sets_.append((qkv, bl, ob, out, wsw))
+            flops = 4.0 * wl.B * wl.H * wl.S * wl.S * wl.D
+            tw = [Timer(torch) for _ in range(4)]
 
-    # grouped K/V heads: rank 0's share of the grouped video-DiT workload
-    gqa = None
-    if not args.skip_gqa:
-        print("[bench] attention with grouped K/V heads", file=sys.stderr, flush=True)
-        gw = synth.WORKLOADS["gqa_video_share"]
-        gq, gk, gv = synth.draw_workload(gw)
-        ghq = usp.usp_balanced_ranges(gw.H, gw.P)
-        ghk = usp.usp_balanced_ranges(gw.kv_heads, gw.P)
-        q0 = bf(gq[:, :, ghq[0]:ghq[1]])
-        k0, v0 = (bf(x[:, :, ghk[0]:ghk[1]]) for x in (gk, gv))
-        del gq, gk, gv
-        o0 = torch.empty_like(q0)
-        gh, ghkv = ghq[1] - ghq[0], ghk[1] - ghk[0]
-        gws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, gw.B, gw.S, gh, gw.D) // 4,
-                          dtype=torch.float32, device=dev)
-        for _ in range(3):
-            usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws)
-        a, b_ = ev(), ev()
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(reps):
-            usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws)
-        b_.record()
-        torch.cuda.synchronize()
-        g_ms = a.elapsed_time(b_) / reps
-        g_flops = 4.0 * gw.B * gh * gw.S * gw.S * gw.D
-        gqa = {"workload": "gqa_video_share", "h": gh, "h_kv": ghkv, "S": gw.S, "D": gw.D,
-               "ms": g_ms, "TFLOP/s": g_flops / (g_ms * 1e-3) / 1e12,
-               "entry": "usp_attention_fwd_gqa (workspace)"}
-        del q0, k0, v0, o0, gws
+            def run(i):
+                qkv, bl, ob, out, wsw = sets_[i % sets]
+                tw[0](usp.usp_pack_seq_to_heads_planes, qkv, bl)
+                a_ = torch.cuda.Event(enable_timing=True)
+                a_.record()
+                for j in range(wl.P):
+                    usp.usp_attention_fwd_ws(bl[0][j], bl[1][j], bl[2][j], ob[j], wsw)
+                b2 = torch.cuda.Event(enable_timing=True)
+                b2.record()
+                tw[1].ev.append((a_, b2))
+                tw[2](usp.usp_unpack_heads_to_seq, ob, out)
 
-    # one rank's Ulysses+Ring pass: two key blocks, then the merge
-    ring = None
-    if not args.skip_ring:
-        print("[bench] Ulysses+Ring pass", file=sys.stderr, flush=True)
-        rw = synth.WORKLOADS["video_dit_ring"]
-        rq, rk, rv = (bf(x) for x in synth.draw_workload(rw))
-        rT = usp.usp_balanced_ranges(rw.S, rw.ring)
-        rc = usp.usp_balanced_ranges(rw.H, rw.P)
-        rh = rc[1] - rc[0]
-
-        def head_group0(x, i):
-            bl = [torch.empty((rw.B, rT[i + 1] - rT[i], rc[j + 1] - rc[j], rw.D),
-                              dtype=torch.bfloat16, device=dev) for j in range(rw.P)]
-            usp.usp_pack_seq_to_heads(x[:, rT[i]:rT[i + 1]], bl)
-            return bl[0]
-
-        qr = head_group0(rq, 0)
-        kvr = [(head_group0(rk, i), head_group0(rv, i)) for i in range(rw.ring)]
-        del rq, rk, rv
-        Sq = rT[1] - rT[0]
-        rws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, rw.B, Sq, rh, rw.D) // 4,
-                          dtype=torch.float32, device=dev)
-        o_acc = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.float32, device=dev)
-        o_blk = torch.empty_like(o_acc)
-        l_acc = torch.empty((rw.B, rh, Sq), dtype=torch.float32, device=dev)
-        l_blk = torch.empty_like(l_acc)
-        o_out = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.bfloat16, device=dev)
-        order = [0] + [(0 - i) % rw.ring for i in range(1, rw.ring)]
-
-        def ring_pass(e=None):
-            if e is not None:
-                e[0].record()
-            usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws)
-            for n, i in enumerate(order[1:]):
-                usp.usp_attention_fwd_block(qr, *kvr[i], o_blk, lse=l_blk, ws=rws)
-                if e is not None:
-                    e[1].record()
-                last = n == len(order) - 2
-                usp.usp_attention_merge(o_acc, l_acc, o_blk, l_blk, o_out if last else o_acc,
-                                        None if last else l_acc)
-            if e is not None:
-                e[2].record()
-
-        for _ in range(3):
-            ring_pass()
-        revs = [[ev() for _ in range(3)] for _ in range(reps)]
-        torch.cuda.synchronize()
-        for i in range(reps):
-            ring_pass(revs[i])
-        torch.cuda.synchronize()
-        r_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in revs]))
-        m_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in revs]))
-        serial_out = o_out.clone()
-
-        # the same pass with the other blocks' attention on a second stream
-        # (each with its own workspace and output buffers): a ring delivers
-        # the next block long before the current one is done, so its launch
-        # can fill the CUs the current launch leaves idle at its tail; the
-        # folds stay in ring order on the first stream
-        side = torch.cuda.Stream()
-        rws2 = torch.empty_like(rws)
-        o_b2 = [o_blk, torch.empty_like(o_blk)]
-        l_b2 = [l_blk, torch.empty_like(l_blk)]
-        ev_blk = [torch.cuda.Event() for _ in range(2)]
-        ev_fold = [torch.cuda.Event() for _ in range(2)]
-        main_r = torch.cuda.current_stream()
-
-        def ring_pass_2s():
-            start = torch.cuda.Event()
-            start.record(main_r)
-            side.wait_event(start)
-            for e in ev_fold:
-                e.record(main_r)
-            usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws, stream=main_r)
-            for n, i in enumerate(order[1:]):
-                bset = n % 2
-                side.wait_event(ev_fold[bset])   # buffer set read by the fold two blocks back
-                usp.usp_attention_fwd_block(qr, *kvr[i], o_b2[bset], lse=l_b2[bset], ws=rws2,
-                                            stream=side)
-                ev_blk[bset].record(side)
-                main_r.wait_event(ev_blk[bset])
-                last = n == len(order) - 2
-                usp.usp_attention_merge(o_acc, l_acc, o_b2[bset], l_b2[bset],
-                                        o_out if last else o_acc, None if last else l_acc,
-                                        stream=main_r)
-                ev_fold[bset].record(main_r)
-
-        for _ in range(3):
-            ring_pass_2s()
-        torch.cuda.synchronize()
-        a2, b2 = ev(), ev()
-        a2.record()
-        for _ in range(reps):
-            ring_pass_2s()
-        b2.record()
-        torch.cuda.synchronize()
-        r2_ms = a2.elapsed_time(b2) / reps
-        if not torch.equal(serial_out, o_out):
-            raise RuntimeError("the two-stream ring pass changed the output")
-        r_flops = 4.0 * rw.B * rh * Sq * rw.S * rw.D
-        m_bytes = rw.B * Sq * rh * rw.D * (4 + 4 + 2) + 2 * rw.B * rh * Sq * 4
-        ring = {"workload": "video_dit_ring", "grid": f"{rw.P} ulysses x {rw.ring} ring",
-                "rank": "ring block 0, head group 0", "h": rh, "Sq": Sq, "S": rw.S, "D": rw.D,
-                "ms": r2_ms, "TFLOP/s": r_flops / (r2_ms * 1e-3) / 1e12,
-                "frac_peak": r_flops / (r2_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flop": r_flops,
-                "one_stream_ms": r_ms, "one_stream_TFLOP/s": r_flops / (r_ms * 1e-3) / 1e12,
-                "merge_us": m_ms * 1e3, "merge_GB/s": m_bytes / (m_ms * 1e-3) / 1e9,
-                "entry": "usp_attention_fwd_block (workspace) x 2 + usp_attention_merge; the "
-                         "second block on a second stream (one_stream: all on one stream)"}
-        del qr, kvr, rws, rws2, o_acc, o_blk, l_acc, l_blk, o_out, o_b2, l_b2, serial_out
-
-    # head-chunked passes on the long-sequence share, against single shot
-    chunked = None
-    if not args.skip_chunked:
-        print("[bench] head-chunked passes (S=131072)", file=sys.stderr, flush=True)
-        cw = synth.WORKLOADS["long_chunked"]
-        cq, ck, cv = (bf(x) for x in synth.draw_workload(cw))
-        co = torch.empty_like(cq)
-        c_flops = 4.0 * cw.B * cw.H * cw.S * cw.S * cw.D
-        cmax = -(-cw.H // cw.chunks)   # heads of the largest pass
-        cws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cmax, cw.D) // 4,
-                          dtype=torch.float32, device=dev)
-        times = {}
-        for name, fn in (("chunked", lambda: usp.usp_attention_fwd_chunked(cq, ck, cv, co, cw.chunks)),
-                         ("chunked_ws", lambda: usp.usp_attention_fwd_chunked_ws(cq, ck, cv, co, cw.chunks,
-                                                                                 cws)),
-                         ("single_shot", lambda: usp.usp_attention_fwd(cq, ck, cv, co))):
-            fn()
+            for i in range(3):
+                run(i)
             torch.cuda.synchronize()
-            a, b_ = ev(), ev()
-            a.record()
-            for _ in range(3):
-                fn()
-            b_.record()
-            torch.cuda.synchronize()
-            times[name] = a.elapsed_time(b_) / 3
-        chunked = {"workload": "long_chunked", "h": cw.H, "S": cw.S, "D": cw.D,
-                   "chunks": usp.usp_head_chunk_ranges(cw.H, cw.chunks), "flop": c_flops,
-                   "ms": times["chunked"], "TFLOP/s": c_flops / (times["chunked"] * 1e-3) / 1e12,
-                   "ws_ms": times["chunked_ws"],
-                   "ws_TFLOP/s": c_flops / (times["chunked_ws"] * 1e-3) / 1e12,
-                   "single_shot_ms": times["single_shot"],
-                   "single_shot_TFLOP/s": c_flops / (times["single_shot"] * 1e-3) / 1e12,
-                   "entry": "usp_attention_fwd_chunked (3 passes; ws: usp_attention_fwd_chunked_ws) "
-                            "vs usp_attention_fwd"}
-        del cq, ck, cv, co, cws
+            tw = [Timer(torch) for _ in range(4)]
+            n = max(6, reps)
+            whole = Timer(torch)
+            for i in range(n):
+                whole(run, i)
+            pk, at, up, wh = tw[0].summary(), tw[1].summary(), tw[2].summary(), whole.summary()
+            res = {"B": wl.B, "S": wl.S, "H": wl.H, "D": wl.D, "P": wl.P, "flop": flops,
+                   "buffer_sets": sets, "pack_qkv": pk, "attention": at, "unpack": up, "step": wh,
+                   "attention_TFLOP/s": tflops(flops, at["median_ms"]),
+                   "attention_frac": tflops(flops, at["median_ms"]) / PEAK_BF16_TFLOPS,
+                   "step_TFLOP/s": tflops(flops, wh["median_ms"]),
+                   "pack_qkv_GB/s": gbs(3 * 2 * wl.B * wl.S * wl.H * wl.D * 2, pk["median_ms"]),
+                   "unpack_GB/s": gbs(2 * wl.B * wl.S * wl.H * wl.D * 2, up["median_ms"])}
+            del sets_
+            return res
+
+        say("ViT-L/16 world (warm, then cold)")
+        out_extra["vit_l16_world"] = {"warm": world_leg("vit_l16", 1), "cold": world_leg("vit_l16", 3)}
+        say("indivisible long world")
+        out_extra["indivisible_long_world"] = world_leg("indivisible_long", 1)
 
     # plain device copy of 1 GiB: practical HBM reference and counter calibration
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    a, b_ = ev(), ev()
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(4):
-        dst.copy_(src)
-    b_.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2.0 * COPY_BYTES / (a.elapsed_time(b_) / 4 * 1e-3) / 1e9
+    cp = timed(torch, lambda i: dst.copy_(src), 4, warm=2)
+    copy_gbs = gbs(2.0 * COPY_BYTES, cp["median_ms"])
     del src, dst
 
+    rel = {}
     rows_bw = {}
-    if not args.skip_rows:
-        print("[bench] model-boundary row movements", file=sys.stderr, flush=True)
+    if legs_on:
+        say("world relayout bandwidth")
+        nbytes = B * S * H * D * 2
+        sets = [[world[t]] + [torch.empty_like(world[t]).copy_(world[t]) for _ in range(2)]
+                for t in range(3)]   # per tensor, three rotating copies
+        dsts = [[blocks_of(B, S, hb, D) for _ in range(3)] for _ in range(3)]
+        cb = 2 * (nbytes * 2 // h0)   # heads [0, 2) of every group of 5, read + write
+
+        def rl(name, fn, moved):
+            r = timed(torch, fn, args.relayout_reps)
+            r.update({"GB/s": gbs(moved, r["median_ms"]), "GB/s_min_time": gbs(moved, r["min_ms"]),
+                      "frac_peak": gbs(moved, r["median_ms"]) / PEAK_HBM_GBS, "bytes_rw": moved})
+            rel[name] = r
+
+        rl("pack", lambda i: usp.usp_pack_seq_to_heads(sets[0][i % 3], dsts[0][i % 3]), 2 * nbytes)
+        rl("unpack", lambda i: usp.usp_unpack_heads_to_seq(dsts[0][i % 3], sets[0][i % 3]), 2 * nbytes)
+        rl("pack_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
+            [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)]), 6 * nbytes)
+        rl("pack_chunk", lambda i: usp.usp_pack_seq_to_heads_chunk(sets[0][i % 3], dsts[0][i % 3], 0, 2),
+           cb)
+        rl("unpack_chunk", lambda i: usp.usp_unpack_heads_to_seq_chunk(dsts[0][i % 3], sets[0][i % 3],
+                                                                       0, 2), cb)
+        rl("pack_chunk_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
+            [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)], head_lo=0,
+            head_hi=2), 3 * cb)
+        for r in rel.values():
+            r["frac_of_copy"] = r["GB/s"] / copy_gbs
+        del sets, dsts
+
+        say("model-boundary row movements")
         W = H * D
-        tbr = usp.usp_balanced_ranges(S, P)
-        nbytes = B * S * W * elem
+        nb = B * S * W * 2
         fulls = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(3)]
-        shard_sets = [[torch.empty((B, tbr[r + 1] - tbr[r], W), dtype=torch.bfloat16, device=dev)
+        shard_sets = [[torch.empty((B, tb[r + 1] - tb[r], W), dtype=torch.bfloat16, device=dev)
                        for r in range(P)] for _ in range(3)]
         partials = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(P)]
-
-        def timed(fn, reps):
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            a, b_ = ev(), ev()
-            a.record()
-            for i in range(reps):
-                fn(i)
-            b_.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b_) / reps
-
         for name, fn, moved in (
-                ("scatter", lambda i: usp.usp_scatter_rows(fulls[i % 3], shard_sets[i % 3]), 2 * nbytes),
-                ("gather", lambda i: usp.usp_gather_rows(shard_sets[i % 3], fulls[i % 3]), 2 * nbytes),
+                ("scatter", lambda i: usp.usp_scatter_rows(fulls[i % 3], shard_sets[i % 3]), 2 * nb),
+                ("gather", lambda i: usp.usp_gather_rows(shard_sets[i % 3], fulls[i % 3]), 2 * nb),
                 ("reduce_scatter", lambda i: usp.usp_reduce_scatter_rows(partials, shard_sets[i % 3]),
-                 (P + 1) * nbytes)):
-            ms = timed(fn, args.relayout_reps)
-            gbs = moved / (ms * 1e-3) / 1e9
-            rows_bw[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
-                             "bytes": moved}
+                 (P + 1) * nb)):
+            r = timed(torch, fn, args.relayout_reps)
+            r.update({"GB/s": gbs(moved, r["median_ms"]), "frac_peak": gbs(moved, r["median_ms"]) /
+                      PEAK_HBM_GBS, "bytes": moved})
+            rows_bw[name] = r
         rows_bw["shape"] = {"B": B, "S": S, "W": W, "P": P, "dtype": "bf16"}
         del fulls, shard_sets, partials
 
-    rel = {}
-    if not args.skip_relayout_bw:
-        # world pack / unpack of the full [1, 32760, 40, 128] tensor, 3 rotating buffer sets
-        print("[bench] world pack/unpack bandwidth", file=sys.stderr, flush=True)
-        nbytes = B * S * H * D * elem
-        srcs = [world[0]] + [torch.empty_like(world[0]).copy_(world[0]) for _ in range(2)]
-        dsts = [[torch.empty((B, S, hb[j + 1] - hb[j], D), dtype=torch.bfloat16, device=dev)
-                 for j in range(P)] for _ in range(3)]
-        for name, fn in (("pack", lambda i: usp.usp_pack_seq_to_heads(srcs[i % 3], dsts[i % 3])),
-                         ("unpack", lambda i: usp.usp_unpack_heads_to_seq(dsts[i % 3], srcs[i % 3]))):
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            a, b_ = ev(), ev()
-            a.record()
-            for i in range(args.relayout_reps):
-                fn(i)
-            b_.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b_) / args.relayout_reps
-            gbs = 2.0 * nbytes / (ms * 1e-3) / 1e9
-            rel[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
-                         "frac_of_copy": gbs / copy_gbs, "bytes_rw": 2 * nbytes}
-        # one two-phase chunk of the same tensor: heads [0, 2) of each group of 5
-        cb = nbytes * 2 // h0
-        for name, fn in (("pack_chunk", lambda i: usp.usp_pack_seq_to_heads_chunk(
-                              srcs[i % 3], dsts[i % 3], 0, 2)),
-                         ("unpack_chunk", lambda i: usp.usp_unpack_heads_to_seq_chunk(
-                              dsts[i % 3], srcs[i % 3], 0, 2))):
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            a, b_ = ev(), ev()
-            a.record()
-            for i in range(args.relayout_reps):
-                fn(i)
-            b_.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b_) / args.relayout_reps
-            gbs = 2.0 * cb / (ms * 1e-3) / 1e9
-            rel[name] = {"us": ms * 1e3, "GB/s": gbs, "frac_peak": gbs / PEAK_HBM_GBS,
-                         "frac_of_copy": gbs / copy_gbs, "bytes_rw": 2 * cb,
-                         "heads": "[0, 2) of each group of 5"}
+    # compact per-leg figures (also kept inside the roofline object)
+    summary = {"attn_video_dit_share": {"TFLOP/s": attn_tflops, "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                                        "median_ms": t_attn["median_ms"], "min_ms": t_attn["min_ms"]},
+               "step_pack_qkv_rank0": {"GB/s": gbs(3 * share_bytes, t_pack["median_ms"]),
+                                       "frac": gbs(3 * share_bytes, t_pack["median_ms"]) / PEAK_HBM_GBS},
+               "step_unpack_o_rank0": {"GB/s": gbs(share_bytes, t_unpack["median_ms"]),
+                                       "frac": gbs(share_bytes, t_unpack["median_ms"]) / PEAK_HBM_GBS}}
+    for name, r in legs.items():
+        f = r.get("flop", attn_flops)
+        ms = r.get("median_ms", r["mean_ms"])
+        summary[name] = {"TFLOP/s": tflops(f, ms), "frac": tflops(f, ms) / PEAK_BF16_TFLOPS,
+                         "median_ms": ms}
+        if "max_abs" in r:
+            summary[name].update({"max_abs": r["max_abs"], "rel_frob": r["rel_frob"]})
+    for name, r in out_extra.items():
+        for tag, rr in ([("", r)] if "flop" in r else [("_" + k, v) for k, v in r.items()]):
+            summary[name + tag] = {"attn_TFLOP/s": rr["attention_TFLOP/s"],
+                                   "attn_frac": rr["attention_frac"],
+                                   "step_TFLOP/s": rr["step_TFLOP/s"],
+                                   "pack_qkv_GB/s": rr["pack_qkv_GB/s"], "unpack_GB/s": rr["unpack_GB/s"]}
+    for name, r in rel.items():
+        summary["relayout_" + name] = {"GB/s": r["GB/s"], "frac": r["frac_peak"]}
+    for name in ("scatter", "gather", "reduce_scatter"):
+        if name in rows_bw:
+            summary["rows_" + name] = {"GB/s": rows_bw[name]["GB/s"], "frac": rows_bw[name]["frac_peak"]}
 
     out = {
         "metric": METRIC,
-        "value": attn_flops / (pipe_ms * 1e-3) / 1e12,
+        "value": tflops(attn_flops, pipe_ms),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -852,34 +901,25 @@ def main():
         "data": "synthetic",
         "config": {"workload": "video_dit_share", "B": B, "S": S, "H": H, "h": h0, "D": D,
                    "P": P, "rank": 0,
-                   "step": "pack rank-0 shard of q,k,v -> attention on head group 0 over "
-                           "the full sequence -> unpack rank-0 rows; relayouts of neighbouring "
-                           "steps on a second stream under the attention"},
-        "attention": {"ms": attn_ms, "TFLOP/s": attn_tflops,
-                      "frac_peak": attn_tflops / PEAK_BF16_TFLOPS, "flop": attn_flops,
-                      "entry": "usp_attention_fwd_ws"},
-        "attention_no_workspace": {"ms": nows_ms,
-                                   "TFLOP/s": attn_flops / (nows_ms * 1e-3) / 1e12,
-                                   "entry": "usp_attention_fwd"},
-        "attention_gqa": gqa,
-        "ring": ring,
-        "chunked": chunked,
-        "two_phase": two_phase,
-        "step_serial": {"ms_per_step": ms_step,
-                        "TFLOP/s": attn_flops / (ms_step * 1e-3) / 1e12,
-                        "how": "the same steps on one stream: pack, attention, unpack"},
-        "step_pack_qkv": {"us": pack_ms * 1e3,
-                          "GB/s": 3 * share_bytes / (pack_ms * 1e-3) / 1e9},
-        "step_unpack_o": {"us": unpack_ms * 1e3,
-                          "GB/s": share_bytes / (unpack_ms * 1e-3) / 1e9},
+                   "step": "pack rank-0 shard of q,k,v -> attention on head group 0 -> unpack "
+                           "rank-0 rows; pipelined on two streams"},
+        "attention": dict(t_attn, **{"TFLOP/s": attn_tflops, "frac_peak": attn_tflops / PEAK_BF16_TFLOPS,
+                                     "flop": attn_flops, "entry": "usp_attention_fwd_ws"}),
+        "step_serial": {"ms_per_step": ms_step, "TFLOP/s": tflops(attn_flops, ms_step),
+                        "pack_qkv": t_pack, "attention": t_attn, "unpack_o": t_unpack},
+        "step_pack_qkv": dict(t_pack, **{"GB/s": gbs(3 * share_bytes, t_pack["median_ms"])}),
+        "step_unpack_o": dict(t_unpack, **{"GB/s": gbs(share_bytes, t_unpack["median_ms"])}),
+        "legs": legs,
+        "configs": out_extra,
         "relayout_world": rel,
         "rows_world": rows_bw,
         "copy_reference_GB/s": copy_gbs,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": stored_traffic(),
-                     "kernel": "usp_attention_fwd_ws: attn_bf16_kernel (key halves) + "
-                               "attn_merge_halves"},
+                     "kernel": "usp_attention_fwd_ws: attn_bf16_kernel + attn_merge_halves",
+                     "median_ms": t_attn["median_ms"], "min_ms": t_attn["min_ms"],
+                     "mean_ms": t_attn["mean_ms"], "legs": summary},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -53,6 +53,8 @@ enum {
 /* Largest SP degree the relayout calls accept (block pointers travel as
  * kernel arguments). */
 #define USP_MAX_PARTS 64
+/* Most tensors one usp_*_planes relayout call moves. */
+#define USP_MAX_PLANES 4
 
 /* Message for the last non-zero status returned on the calling thread
  * (thread-local; "" if none). The string stays valid until the next call. */
@@ -154,6 +156,32 @@ int usp_pack_seq_to_heads_chunk(const void* seq, void* const* blk, usp_dtype dty
 int usp_unpack_heads_to_seq_chunk(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
                                   int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
                                   int32_t head_lo, int32_t head_hi, void* stream);
+
+/*
+ * Several tensors of one shape through the same relayout in one launch
+ * (h3-blackwell-runtime distributed.py, SequenceParallelContext.seq_to_heads
+ * moves q, k and v of a layer together): plane t of n is
+ * usp_pack_seq_to_heads(seq[t], &blk[t * P], ...) (head_lo = head_hi = 0)
+ * or usp_pack_seq_to_heads_chunk(seq[t], &blk[t * P], ..., head_lo,
+ * head_hi, ...), and the unpack likewise; the planes stay separate tensors.
+ *   n:   1 .. USP_MAX_PLANES planes.
+ *   seq: host array of n device pointers (pack: sources; unpack:
+ *        destinations), each a tensor as in the single-plane call.
+ *   blk: host array of n * P device pointers, plane-major: block j of
+ *        plane t at blk[t * P + j].
+ * The result is bitwise the n single-plane calls'. Errors: n outside
+ * [1, USP_MAX_PLANES] or seq/blk NULL -> USP_EINVAL; otherwise those of the
+ * single-plane calls for every plane (the head-chunk checks when head_lo or
+ * head_hi is non-zero).
+ */
+int usp_pack_seq_to_heads_planes(int32_t n, const void* const* seq, void* const* blk,
+                                 usp_dtype dtype, int64_t B, int64_t S, int32_t H, int32_t D,
+                                 int32_t P, int32_t rank, int32_t head_lo, int32_t head_hi,
+                                 void* stream);
+int usp_unpack_heads_to_seq_planes(int32_t n, const void* const* blk, void* const* seq,
+                                   usp_dtype dtype, int64_t B, int64_t S, int32_t H, int32_t D,
+                                   int32_t P, int32_t rank, int32_t head_lo, int32_t head_hi,
+                                   void* stream);
 
 /*
  * Ragged token rows at the model boundary, without padding. A tensor

@@ -66,6 +66,17 @@ F32_MAX_ABS, F32_REL_FROB = 1e-5, 1e-5
 BF16_LSE_ABS = 2.0 ** -8 + 1e-5
 
 
+def coded(shape, dtype, seed=0):
+    """Input for the bitwise movement tests: ``index_coded`` (each element
+    its own index) while no code repeats, random codes beyond that (the
+    index code repeats every 65024 bf16 elements, so a shift by a multiple
+    of that period would go unseen)."""
+    n = int(np.prod(shape))
+    if (dtype == synth.BF16 and n <= 65024) or (dtype == synth.F32 and n < (1 << 24)):
+        return synth.index_coded(shape, dtype)
+    return synth.random_coded(shape, dtype, seed)
+
+
 def bf16_ulp(x):
     """One bf16 ulp at |x| (for grading the bf16-output epilogue)."""
     ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)

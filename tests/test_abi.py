@@ -157,6 +157,38 @@ def test_attention_ws_rejects(kw, status):
     assert usp.usp_last_error()
 
 
+def _planes(n=2, seq=True, blk=True, bad_plane=None, P=3, H=6, lo=0, hi=0):
+    seqs = (ctypes.c_void_p * 4)(*([FAKE] * 4))
+    blks = (ctypes.c_void_p * (4 * P))(*([FAKE] * (4 * P)))
+    if bad_plane is not None:
+        seqs[bad_plane] = FAKE + 4
+    return L.usp_pack_seq_to_heads_planes(n, seqs if seq else None, blks if blk else None, 1, 1, 64,
+                                          H, 64, P, -1, lo, hi, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), -1), (dict(n=5), -1), (dict(seq=False), -1), (dict(blk=False), -1),
+    (dict(bad_plane=1), -4),            # the second plane's tensor is misaligned
+    (dict(H=7, lo=0, hi=1), -1),         # head-chunk phase with ragged groups
+    (dict(lo=1, hi=1), -1),              # empty head chunk
+    (dict(P=0), -1),
+])
+def test_planes_reject(kw, status):
+    assert _planes(**kw) == status
+    assert usp.usp_last_error()
+
+
+def test_planes_binding_rejects_mismatched_planes():
+    import torch
+    a = torch.empty((1, 8, 6, 64), dtype=torch.bfloat16)
+    b = torch.empty((1, 8, 6, 64), dtype=torch.float32)
+    blocks = [[torch.empty((1, 8, 2, 64), dtype=torch.bfloat16) for _ in range(3)]] * 2
+    with pytest.raises(ValueError):
+        usp.usp_pack_seq_to_heads_planes([a, b], blocks)
+    with pytest.raises(ValueError):
+        usp.usp_pack_seq_to_heads_planes([a], blocks)
+
+
 def _attn_na(q=FAKE, i=1, out=0, B=1, S=16, h=2, D=64, lo=0, hi=2):
     return L.usp_attention_fwd_noalloc(q, FAKE, FAKE, FAKE, i, out, B, S, h, D, lo, hi, 0.0, None,
                                        None)

@@ -11,7 +11,7 @@ from oracle import ranges as R
 from oracle import relayout as X
 from ulysses_sequence_attention_amd import synth
 
-from gpu_util import DEV, log, poisoned, to_dev, to_host
+from gpu_util import coded, DEV, log, poisoned, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def test_device_ranges():
 
 def _world_roundtrip(B, S, H, D, P, dtype):
     import torch
-    seq = synth.index_coded((B, S, H, D), dtype)
+    seq = coded((B, S, H, D), dtype)
     ref_blocks = X.pack_seq_to_heads(seq, P)
     hb = R.balanced_ranges(H, P)
     d_seq = to_dev(seq, dtype)
@@ -75,7 +75,7 @@ def test_world_pack_unpack_video_dit():
                                              (2, 65537, 12, 64, 4, BF), (1, 9, 9, 8, 9, BF)])
 def test_rank_share_pack_unpack(B, S, H, D, P, dtype):
     import torch
-    seq = synth.index_coded((B, S, H, D), dtype)
+    seq = coded((B, S, H, D), dtype)
     world = X.pack_seq_to_heads(seq, P)
     hb = R.balanced_ranges(H, P)
     tb = R.balanced_ranges(S, P)
@@ -141,3 +141,67 @@ def test_world_pack_unpack_beyond_one_launch():
     assert torch.equal(back.view(torch.int16), bits)
     del bits, blocks, back
     torch.cuda.empty_cache()
+
+
+# several tensors (q, k, v) through one launch: bitwise the single-plane calls
+PLANE_CASES = [  # B, S, H, D, P, dtype, rank, (head_lo, head_hi) or None
+    (1, 32760, 40, 128, 8, BF, -1, None),      # video-DiT world
+    (1, 32760, 40, 128, 8, BF, 0, None),       # rank 0's share of it (the benched step)
+    (1, 32760, 40, 128, 8, BF, 7, (0, 2)),     # a head-chunk phase of rank 7's share
+    (2, 65537, 12, 64, 4, BF, 3, None),        # indivisible tokens, last rank
+    (2, 37, 7, 64, 3, BF, 1, None),            # ragged heads 3/2/2
+    (1, 257, 6, 64, 3, F, -1, (1, 2)),         # fp32 world, one head of each group
+]
+
+
+@pytest.mark.parametrize("B,S,H,D,P,dtype,rank,heads", PLANE_CASES)
+def test_planes_equal_single_plane_calls(B, S, H, D, P, dtype, rank, heads):
+    import torch
+    n = 3
+    tb, hb = R.balanced_ranges(S, P), R.balanced_ranges(H, P)
+    L = S if rank < 0 else tb[rank + 1] - tb[rank]
+    lo, hi = heads or (0, 0)
+    seqs = [to_dev(coded((B, L, H, D), dtype, seed=40 + t), dtype) for t in range(n)]
+    blk_a = [[poisoned((B, S, hb[j + 1] - hb[j], D), dtype) for j in range(P)] for _ in range(n)]
+    blk_b = [[poisoned((B, S, hb[j + 1] - hb[j], D), dtype) for j in range(P)] for _ in range(n)]
+    log(f"planes pack n={n} B={B} S={S} H={H} D={D} P={P} {dtype} rank={rank} heads={heads}")
+    usp.usp_pack_seq_to_heads_planes(seqs, blk_a, rank=rank, head_lo=lo, head_hi=hi)
+    for t in range(n):
+        if heads:
+            usp.usp_pack_seq_to_heads_chunk(seqs[t], blk_b[t], lo, hi, rank=rank)
+        else:
+            usp.usp_pack_seq_to_heads(seqs[t], blk_b[t], rank=rank)
+    torch.cuda.synchronize()
+    for t in range(n):
+        for j in range(P):
+            assert to_host(blk_a[t][j]).tobytes() == to_host(blk_b[t][j]).tobytes(), f"plane {t} block {j}"
+    out_a = [poisoned((B, L, H, D), dtype) for _ in range(n)]
+    out_b = [poisoned((B, L, H, D), dtype) for _ in range(n)]
+    log(f"planes unpack n={n} B={B} S={S} H={H} D={D} P={P} {dtype} rank={rank} heads={heads}")
+    usp.usp_unpack_heads_to_seq_planes(blk_a, out_a, rank=rank, head_lo=lo, head_hi=hi)
+    for t in range(n):
+        if heads:
+            usp.usp_unpack_heads_to_seq_chunk(blk_a[t], out_b[t], lo, hi, rank=rank)
+        else:
+            usp.usp_unpack_heads_to_seq(blk_a[t], out_b[t], rank=rank)
+    torch.cuda.synchronize()
+    for t in range(n):
+        got = to_host(out_a[t])
+        assert got.tobytes() == to_host(out_b[t]).tobytes(), f"plane {t}"
+        if not heads:
+            assert got.tobytes() == to_host(seqs[t]).tobytes(), f"plane {t} round trip"
+
+
+def test_planes_world_against_oracle():
+    import torch
+    B, S, H, D, P = 2, 37, 7, 64, 3
+    seqs = [coded((B, S, H, D), BF, seed=60 + t) for t in range(2)]
+    hb = R.balanced_ranges(H, P)
+    blocks = [[poisoned((B, S, hb[j + 1] - hb[j], D), BF) for j in range(P)] for _ in range(2)]
+    log("planes pack n=2 against the oracle")
+    usp.usp_pack_seq_to_heads_planes([to_dev(x, BF) for x in seqs], blocks)
+    torch.cuda.synchronize()
+    for t in range(2):
+        ref = X.pack_seq_to_heads(seqs[t], P)
+        for j in range(P):
+            assert to_host(blocks[t][j]).tobytes() == ref[j].tobytes()

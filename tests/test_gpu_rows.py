@@ -14,7 +14,7 @@ from oracle import ranges as R
 from oracle import relayout as X
 from ulysses_sequence_attention_amd import synth
 
-from gpu_util import DEV, log, poisoned, to_dev, to_host, widen
+from gpu_util import coded, DEV, log, poisoned, to_dev, to_host, widen
 
 pytestmark = pytest.mark.gpu
 BF, F = synth.BF16, synth.F32
@@ -35,7 +35,7 @@ def test_scatter_gather_bit_exact(dtype, B, S, W, P):
     import torch
     if dtype == F and W % 4:
         pytest.skip("fp32 rows need W % 4 == 0")
-    x = synth.index_coded((B, S, W), dtype)
+    x = coded((B, S, W), dtype)
     log(f"rows scatter/gather {dtype} B={B} S={S} W={W} P={P}")
     shards = _shards_like(B, S, W, P, dtype)
     usp.usp_scatter_rows(to_dev(x, dtype), shards)
@@ -53,7 +53,7 @@ def test_scatter_gather_bit_exact(dtype, B, S, W, P):
 def test_scatter_one_rank_touches_only_its_shard():
     import torch
     B, S, W, P = 2, 100, 8, 3
-    x = synth.index_coded((B, S, W), BF)
+    x = coded((B, S, W), BF)
     log("rows scatter rank 1 of 3")
     shards = _shards_like(B, S, W, P, BF)
     usp.usp_scatter_rows(to_dev(x, BF), [None, shards[1], None], rank=1)
@@ -121,7 +121,7 @@ def test_video_dit_boundary_full_size():
     B, S, W, P = 1, 32760, 5120, 8
     tb = R.balanced_ranges(S, P)
     log("rows full size: scatter/gather [1, 32760, 5120] bf16, P=8")
-    x = synth.index_coded((B, S, W), BF)
+    x = coded((B, S, W), BF)
     shards = _shards_like(B, S, W, P, BF)
     usp.usp_scatter_rows(to_dev(x, BF), shards)
     torch.cuda.synchronize()

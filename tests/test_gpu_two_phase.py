@@ -15,7 +15,7 @@ from oracle import relayout as X
 from oracle import ulysses as U
 from ulysses_sequence_attention_amd import synth
 
-from gpu_util import BF16_MAX_ABS, BF16_REL_FROB, DEV, err, log, poisoned, to_dev, to_host, widen
+from gpu_util import coded, BF16_MAX_ABS, BF16_REL_FROB, DEV, err, log, poisoned, to_dev, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def _plan(h, chunks):
 def test_chunk_phases_world(B, S, H, D, P, chunks, dtype):
     import torch
     h = H // P
-    seq = synth.index_coded((B, S, H, D), dtype)
+    seq = coded((B, S, H, D), dtype)
     d_seq = to_dev(seq, dtype)
     blocks = [poisoned((B, S, h, D), dtype) for _ in range(P)]
     ref = [to_host(b) for b in blocks]
@@ -72,7 +72,7 @@ def test_chunk_phases_world(B, S, H, D, P, chunks, dtype):
 def test_chunk_phases_rank_share(B, S, H, D, P, chunks, dtype):
     import torch
     h = H // P
-    seq = synth.index_coded((B, S, H, D), dtype)
+    seq = coded((B, S, H, D), dtype)
     tb = R.balanced_ranges(S, P)
     world = X.pack_seq_to_heads(seq, P)
     d_world = [to_dev(w, dtype) for w in world]

@@ -7,7 +7,8 @@ One rank's share of the work behind a small C ABI (``include/usp.h``,
     token and head ranges, head-chunk plans;
   * ``usp_pack_seq_to_heads`` / ``usp_unpack_heads_to_seq`` — the
     sequence-sharded <-> head-sharded relayouts around the all-to-alls, and
-    their ``_chunk`` forms, one head chunk per phase of the two-phase exchange;
+    their ``_chunk`` forms, one head chunk per phase of the two-phase exchange,
+    and ``_planes`` forms moving several tensors (q, k, v) in one launch;
   * ``usp_scatter_rows`` / ``usp_gather_rows`` / ``usp_reduce_scatter_rows``
     — ragged token rows at the model boundary;
   * ``usp_attention_fwd`` / ``usp_attention_fwd_chunked`` (``_ws``) — flash-style
@@ -32,5 +33,6 @@ from ._binding import (  # noqa: F401
     usp_attention_workspace_bytes,
     usp_balanced_ranges, usp_balanced_ranges_device,
     usp_gather_rows, usp_head_chunk_ranges, usp_last_error, usp_pack_seq_to_heads,
-    usp_pack_seq_to_heads_chunk, usp_reduce_scatter_rows, usp_scatter_rows,
-    usp_unpack_heads_to_seq, usp_unpack_heads_to_seq_chunk, usp_version)
+    usp_pack_seq_to_heads_chunk, usp_pack_seq_to_heads_planes, usp_reduce_scatter_rows,
+    usp_scatter_rows, usp_unpack_heads_to_seq, usp_unpack_heads_to_seq_chunk,
+    usp_unpack_heads_to_seq_planes, usp_version)

@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.usp_unpack_heads_to_seq.argtypes = rel
         rel_chunk = rel[:-1] + [_i32, _i32, _vp]
         L.usp_pack_seq_to_heads_chunk.argtypes = rel_chunk
+        rel_planes = [_i32, _vp, _vp, ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                      _vp]
+        L.usp_pack_seq_to_heads_planes.argtypes = rel_planes
+        L.usp_unpack_heads_to_seq_planes.argtypes = rel_planes
         L.usp_unpack_heads_to_seq_chunk.argtypes = rel_chunk
         L.usp_attention_fwd.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64,
                                         _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp]
@@ -288,6 +292,45 @@ def usp_unpack_heads_to_seq_chunk(blocks, seq, head_lo: int, head_hi: int, rank:
     _check(lib().usp_unpack_heads_to_seq_chunk(arr, _ptr(seq), _dtype(seq), B, S, H, D, P, rank,
                                                head_lo, head_hi, _stream(seq, stream)),
            "usp_unpack_heads_to_seq_chunk")
+
+
+def _planes(seqs, blocks, rank):
+    """Marshal n planes: the same checks as the single-plane calls for each
+    plane, plus one shape and dtype for all (the kernel takes one geometry)."""
+    n = len(seqs)
+    if n != len(blocks) or n < 1:
+        raise ValueError(f"{n} sequence tensors but {len(blocks)} block lists")
+    P = len(blocks[0])
+    dims = None
+    for t in range(n):
+        if len(blocks[t]) != P:
+            raise ValueError("every plane needs the same number of blocks")
+        d = _relayout_dims(seqs[t], blocks[t], rank)
+        if dims is not None and (d != dims or seqs[t].dtype != seqs[0].dtype):
+            raise ValueError(f"plane {t} has another shape or dtype than plane 0")
+        dims = d
+    sarr = (_vp * n)(*[_ptr(x) for x in seqs])
+    barr = (_vp * max(n * P, 1))(*[_ptr(b) for bl in blocks for b in bl])
+    return n, P, sarr, barr, dims
+
+
+def usp_pack_seq_to_heads_planes(seqs, blocks, rank: int = -1, head_lo: int = 0, head_hi: int = 0,
+                                 stream=None) -> None:
+    """usp_pack_seq_to_heads (head_hi = 0) or its head-chunk phase for n
+    tensors of one shape in one launch: seqs[t] -> blocks[t][j]."""
+    n, P, sarr, barr, (B, S, H, D) = _planes(seqs, blocks, rank)
+    _check(lib().usp_pack_seq_to_heads_planes(n, sarr, barr, _dtype(seqs[0]), B, S, H, D, P, rank,
+                                              head_lo, head_hi, _stream(seqs[0], stream)),
+           "usp_pack_seq_to_heads_planes")
+
+
+def usp_unpack_heads_to_seq_planes(blocks, seqs, rank: int = -1, head_lo: int = 0,
+                                   head_hi: int = 0, stream=None) -> None:
+    """The inverse of usp_pack_seq_to_heads_planes: blocks[t][j] -> seqs[t]."""
+    n, P, sarr, barr, (B, S, H, D) = _planes(seqs, blocks, rank)
+    _check(lib().usp_unpack_heads_to_seq_planes(n, barr, sarr, _dtype(seqs[0]), B, S, H, D, P, rank,
+                                                head_lo, head_hi, _stream(seqs[0], stream)),
+           "usp_unpack_heads_to_seq_planes")
 
 
 def _row_dims(full_like):

@@ -25,13 +25,14 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
 
+// per plane: the sequence-side tensor and its P head blocks
 struct Ptrs {
-  u32x4* p[USP_MAX_PARTS];
+  u32x4* seq[USP_MAX_PLANES];
+  u32x4* p[USP_MAX_PLANES][USP_MAX_PARTS];
 };
 
 struct RelayoutParams {
-  u32x4* seq;          // sequence side (source for pack, destination for unpack)
-  uint32_t n_chunks;   // chunks handled by this launch (seq side, < 2^31)
+  uint32_t n_chunks;   // chunks handled by this launch per plane (seq side, < 2^31)
   uint32_t row0;       // first seq row of this launch
   uint32_t cpr;        // chunks per seq row = H * cph
   uint32_t cph;        // chunks per head = D * esize / 16
@@ -49,8 +50,10 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 1;
 
 template <bool kPack>
-__global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutParams p, Ptrs blk) {
+__global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutParams p, Ptrs ptr) {
   const uint32_t first = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  const int t = blockIdx.y;  // plane
+  u32x4* const seq = ptr.seq[t];
   u32x4 val[kUnroll];
   u32x4* dst[kUnroll];
   const u32x4* src[kUnroll];
@@ -82,11 +85,11 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutParams p, Pt
       const uint64_t hoff = (hrow * hj + i) * p.cph + dc;
       const uint64_t soff = uint64_t(row) * p.cpr + c;
       if (kPack) {
-        src[u] = p.seq + soff;
-        dst[u] = blk.p[j] + hoff;
+        src[u] = seq + soff;
+        dst[u] = ptr.p[t][j] + hoff;
       } else {
-        src[u] = blk.p[j] + hoff;
-        dst[u] = p.seq + soff;
+        src[u] = ptr.p[t][j] + hoff;
+        dst[u] = seq + soff;
       }
     }
   }
@@ -106,8 +109,7 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutParams p, Pt
 // chunk's two addresses are the run bases plus r and no head division is
 // needed. Both sides are read and written in runs of hc * D * esize bytes.
 struct ChunkParams {
-  u32x4* seq;
-  uint32_t n_chunks;  // chunks moved by this launch (< 2^31)
+  uint32_t n_chunks;  // chunks moved by this launch per plane (< 2^31)
   uint32_t row0;      // first seq row of this launch
   uint32_t cpr;       // chunks per seq row = H * cph
   uint32_t cph;       // chunks per head
@@ -119,9 +121,11 @@ struct ChunkParams {
 };
 
 template <bool kPack>
-__global__ __launch_bounds__(kThreads) void relayout_chunk_kernel(ChunkParams p, Ptrs blk) {
+__global__ __launch_bounds__(kThreads) void relayout_chunk_kernel(ChunkParams p, Ptrs ptr) {
   const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
   if (idx >= p.n_chunks) return;
+  const int t = blockIdx.y;  // plane
+  u32x4* const seq = ptr.seq[t];
   const uint32_t lrow = p.fd_crow.div(idx);
   const uint32_t c = idx - lrow * p.crow;
   const uint32_t j = p.fd_cgrp.div(c);
@@ -133,9 +137,9 @@ __global__ __launch_bounds__(kThreads) void relayout_chunk_kernel(ChunkParams p,
   const uint64_t hoff = (hrow * p.h + p.lo) * p.cph + r;
   const uint64_t soff = uint64_t(row) * p.cpr + (uint64_t(j) * p.h + p.lo) * p.cph + r;
   if (kPack)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(p.seq + soff), blk.p[j] + hoff);
+    __builtin_nontemporal_store(__builtin_nontemporal_load(seq + soff), ptr.p[t][j] + hoff);
   else
-    __builtin_nontemporal_store(__builtin_nontemporal_load(blk.p[j] + hoff), p.seq + soff);
+    __builtin_nontemporal_store(__builtin_nontemporal_load(ptr.p[t][j] + hoff), seq + soff);
 }
 
 __global__ void ranges_kernel(int64_t total, int32_t parts, int64_t* bounds) {
@@ -168,16 +172,15 @@ int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s) {
   if (cpr >= (1u << 30) || a.S >= (int64_t(1) << 31) || rows >= (1ull << 31))
     return fail(USP_ESHAPE, "relayout sizes exceed the 32-bit index range of one row walk");
 
-  Ptrs blk{};
-  for (int j = 0; j < a.P; ++j)
-    blk.p[j] = pack ? static_cast<u32x4*>(a.blk_out[j])
-                    : const_cast<u32x4*>(static_cast<const u32x4*>(a.blk_in[j]));
-  u32x4* const seq = pack ? const_cast<u32x4*>(static_cast<const u32x4*>(a.seq_in))
-                          : static_cast<u32x4*>(a.seq_out);
+  Ptrs ptr{};
+  for (int t = 0; t < a.n; ++t) {
+    ptr.seq[t] = const_cast<u32x4*>(static_cast<const u32x4*>(a.seq[t]));
+    for (int j = 0; j < a.P; ++j)
+      ptr.p[t][j] = const_cast<u32x4*>(static_cast<const u32x4*>(a.blk[size_t(t) * a.P + j]));
+  }
 
   if (a.head_hi > 0) {  // one head-chunk phase (equal groups, checked by the caller)
     ChunkParams p;
-    p.seq = seq;
     p.cpr = uint32_t(cpr);
     p.cph = cph;
     p.h = uint32_t(a.H / a.P);
@@ -195,11 +198,11 @@ int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s) {
       const uint64_t nr = rows - r0 < max_rows ? rows - r0 : max_rows;
       p.row0 = uint32_t(r0);
       p.n_chunks = uint32_t(nr * p.crow);
-      const uint32_t grid = (p.n_chunks + kThreads - 1) / kThreads;
+      const dim3 grid((p.n_chunks + kThreads - 1) / kThreads, a.n);
       if (pack)
-        relayout_chunk_kernel<true><<<grid, kThreads, 0, s>>>(p, blk);
+        relayout_chunk_kernel<true><<<grid, kThreads, 0, s>>>(p, ptr);
       else
-        relayout_chunk_kernel<false><<<grid, kThreads, 0, s>>>(p, blk);
+        relayout_chunk_kernel<false><<<grid, kThreads, 0, s>>>(p, ptr);
       if (int st = check_launch(pack ? "head-chunk pack kernel" : "head-chunk unpack kernel"))
         return st;
     }
@@ -220,7 +223,6 @@ int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s) {
   p.fd_base = FastDiv(p.base);
   p.fd_base1 = FastDiv(p.base + 1);
   p.fd_len = FastDiv(p.len);
-  p.seq = seq;
 
   // Keep every flat chunk index of a launch below 2^31: split the row walk.
   const uint64_t max_rows = ((1ull << 31) - 1) / cpr;
@@ -229,11 +231,11 @@ int launch_relayout(const RelayoutArgs& a, bool pack, hipStream_t s) {
     p.row0 = uint32_t(r0);
     p.n_chunks = uint32_t(nr * cpr);
     const uint32_t per_block = kThreads * kUnroll;
-    const uint32_t grid = (p.n_chunks + per_block - 1) / per_block;
+    const dim3 grid((p.n_chunks + per_block - 1) / per_block, a.n);
     if (pack)
-      relayout_kernel<true><<<grid, kThreads, 0, s>>>(p, blk);
+      relayout_kernel<true><<<grid, kThreads, 0, s>>>(p, ptr);
     else
-      relayout_kernel<false><<<grid, kThreads, 0, s>>>(p, blk);
+      relayout_kernel<false><<<grid, kThreads, 0, s>>>(p, ptr);
     if (int st = check_launch(pack ? "pack kernel" : "unpack kernel")) return st;
   }
   return USP_OK;

@@ -84,6 +84,17 @@ static int check_relayout(const void* seq, const void* const* blk, usp_dtype dt,
   return USP_OK;
 }
 
+// One phase of the head-chunked exchange: equal head groups and a non-empty
+// chunk inside a group.
+static int check_chunk(int32_t H, int32_t P, int32_t head_lo, int32_t head_hi) {
+  if (H % P)
+    return fail(USP_EINVAL, "head-chunk relayouts need equal head groups (%d heads over %d ranks)", H, P);
+  if (head_lo < 0 || head_hi > H / P || head_lo >= head_hi)
+    return fail(USP_EINVAL, "head chunk [%d, %d) is empty or outside a group of %d heads", head_lo,
+                head_hi, H / P);
+  return USP_OK;
+}
+
 // Arguments of the row movements; `ptrs` are the P shard/partial/output
 // pointers, of which only ptrs[rank] must be set when rank >= 0 and the
 // array is written per rank (scatter, reduce-scatter outputs).
@@ -198,59 +209,77 @@ int usp_head_chunk_ranges(int32_t heads, int32_t chunks, int32_t* bounds) {
   return ok();
 }
 
+}  // extern "C"
+
+namespace usp {
+// n planes of one relayout (one launch): the per-plane checks of the
+// single-plane calls, plus the plane count and, for a head-chunk phase
+// (head_hi > 0), equal head groups and a chunk inside a group.
+static int relayout_planes(int32_t n, const void* const* seq, const void* const* blk, bool pack,
+                           usp_dtype dtype, int64_t B, int64_t S, int32_t H, int32_t D, int32_t P,
+                           int32_t rank, int32_t head_lo, int32_t head_hi, hipStream_t stream) {
+  if (n < 1 || n > USP_MAX_PLANES)
+    return fail(USP_EINVAL, "plane count must be in [1, %d] (got %d)", USP_MAX_PLANES, n);
+  if (!seq || !blk) return fail(USP_EINVAL, "null seq or block array");
+  for (int32_t t = 0; t < n; ++t)
+    if (int st = check_relayout(seq[t], blk + size_t(t) * (P > 0 ? P : 0), dtype, B, S, H, D, P, rank))
+      return st;
+  if (head_hi > 0 || head_lo != 0)
+    if (int st = check_chunk(H, P, head_lo, head_hi)) return st;
+  RelayoutArgs a{n, seq, blk, B, S, H, D, P, rank < 0 ? -1 : rank, esize_of(dtype), head_lo,
+                 head_hi};
+  if (int st = launch_relayout(a, pack, stream)) return st;
+  return ok();
+}
+}  // namespace usp
+
+extern "C" {
+
 int usp_pack_seq_to_heads(const void* seq, void* const* blk, usp_dtype dtype, int64_t B,
                           int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
                           void* stream) {
-  if (int st = check_relayout(seq, (const void* const*)blk, dtype, B, S, H, D, P, rank))
-    return st;
-  RelayoutArgs a{seq, nullptr, nullptr, blk, B, S, H, D, P, rank < 0 ? -1 : rank,
-                 esize_of(dtype)};
-  if (int st = launch_relayout(a, true, (hipStream_t)stream)) return st;
-  return ok();
+  return relayout_planes(1, &seq, (const void* const*)blk, true, dtype, B, S, H, D, P, rank, 0, 0,
+                         (hipStream_t)stream);
 }
 
 int usp_unpack_heads_to_seq(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
                             int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
                             void* stream) {
-  if (int st = check_relayout(seq, blk, dtype, B, S, H, D, P, rank)) return st;
-  RelayoutArgs a{nullptr, seq, blk, nullptr, B, S, H, D, P, rank < 0 ? -1 : rank,
-                 esize_of(dtype)};
-  if (int st = launch_relayout(a, false, (hipStream_t)stream)) return st;
-  return ok();
-}
-
-// One phase of the head-chunked exchange: the relayout checks, plus equal
-// head groups and a non-empty chunk inside a group.
-static int check_chunk(int32_t H, int32_t P, int32_t head_lo, int32_t head_hi) {
-  if (H % P)
-    return fail(USP_EINVAL, "head-chunk relayouts need equal head groups (%d heads over %d ranks)", H, P);
-  if (head_lo < 0 || head_hi > H / P || head_lo >= head_hi)
-    return fail(USP_EINVAL, "head chunk [%d, %d) is empty or outside a group of %d heads", head_lo,
-                head_hi, H / P);
-  return USP_OK;
+  const void* s = seq;
+  return relayout_planes(1, &s, blk, false, dtype, B, S, H, D, P, rank, 0, 0, (hipStream_t)stream);
 }
 
 int usp_pack_seq_to_heads_chunk(const void* seq, void* const* blk, usp_dtype dtype, int64_t B,
                                 int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
                                 int32_t head_lo, int32_t head_hi, void* stream) {
-  if (int st = check_relayout(seq, (const void* const*)blk, dtype, B, S, H, D, P, rank))
-    return st;
-  if (int st = check_chunk(H, P, head_lo, head_hi)) return st;
-  RelayoutArgs a{seq, nullptr, nullptr, blk, B, S, H, D, P, rank < 0 ? -1 : rank,
-                 esize_of(dtype), head_lo, head_hi};
-  if (int st = launch_relayout(a, true, (hipStream_t)stream)) return st;
-  return ok();
+  if (head_hi <= 0) return fail(USP_EINVAL, "head chunk [%d, %d) is empty", head_lo, head_hi);
+  return relayout_planes(1, &seq, (const void* const*)blk, true, dtype, B, S, H, D, P, rank,
+                         head_lo, head_hi, (hipStream_t)stream);
 }
 
 int usp_unpack_heads_to_seq_chunk(const void* const* blk, void* seq, usp_dtype dtype, int64_t B,
                                   int64_t S, int32_t H, int32_t D, int32_t P, int32_t rank,
                                   int32_t head_lo, int32_t head_hi, void* stream) {
-  if (int st = check_relayout(seq, blk, dtype, B, S, H, D, P, rank)) return st;
-  if (int st = check_chunk(H, P, head_lo, head_hi)) return st;
-  RelayoutArgs a{nullptr, seq, blk, nullptr, B, S, H, D, P, rank < 0 ? -1 : rank,
-                 esize_of(dtype), head_lo, head_hi};
-  if (int st = launch_relayout(a, false, (hipStream_t)stream)) return st;
-  return ok();
+  if (head_hi <= 0) return fail(USP_EINVAL, "head chunk [%d, %d) is empty", head_lo, head_hi);
+  const void* s = seq;
+  return relayout_planes(1, &s, blk, false, dtype, B, S, H, D, P, rank, head_lo, head_hi,
+                         (hipStream_t)stream);
+}
+
+int usp_pack_seq_to_heads_planes(int32_t n, const void* const* seq, void* const* blk,
+                                 usp_dtype dtype, int64_t B, int64_t S, int32_t H, int32_t D,
+                                 int32_t P, int32_t rank, int32_t head_lo, int32_t head_hi,
+                                 void* stream) {
+  return relayout_planes(n, seq, (const void* const*)blk, true, dtype, B, S, H, D, P, rank,
+                         head_lo, head_hi, (hipStream_t)stream);
+}
+
+int usp_unpack_heads_to_seq_planes(int32_t n, const void* const* blk, void* const* seq,
+                                   usp_dtype dtype, int64_t B, int64_t S, int32_t H, int32_t D,
+                                   int32_t P, int32_t rank, int32_t head_lo, int32_t head_hi,
+                                   void* stream) {
+  return relayout_planes(n, (const void* const*)seq, blk, false, dtype, B, S, H, D, P, rank,
+                         head_lo, head_hi, (hipStream_t)stream);
 }
 
 int usp_scatter_rows(const void* full, void* const* shards, usp_dtype dtype, int64_t B, int64_t S,

@@ -39,10 +39,10 @@ struct FastDiv {
 int launch_ranges_device(int64_t total, int32_t parts, int64_t* d_bounds, hipStream_t s);
 
 struct RelayoutArgs {
-  const void* seq_in;          // pack: source seq; unpack: unused
-  void* seq_out;               // unpack: destination seq; pack: unused
-  const void* const* blk_in;   // unpack: P source blocks
-  void* const* blk_out;        // pack: P destination blocks
+  // n planes (tensors of one shape, e.g. q, k, v) moved by one launch
+  int32_t n;
+  const void* const* seq;   // n sequence-side tensors (pack: sources; unpack: destinations)
+  const void* const* blk;   // n * P head blocks, plane-major: blk[t * P + j]
   int64_t B, S;
   int32_t H, D, P, rank, esize;
   // one phase of the head-chunked exchange: heads [head_lo, head_hi) of each

@@ -165,8 +165,27 @@ def index_coded(shape, dtype: str) -> np.ndarray:
         if n >= (1 << 24):
             raise ValueError("index-coded f32 tensors must have < 2**24 elements")
         return idx.astype(np.float32).reshape(shape)
-    code = (idx % 65024).astype(np.uint32)
+    return _finite_bf16_pattern(idx % 65024).reshape(shape)
+
+
+def _finite_bf16_pattern(code: np.ndarray) -> np.ndarray:
+    """Codes 0 .. 65023 one-to-one onto the uint16 patterns whose high byte
+    is neither 0x7F nor 0xFF (no Inf/NaN pattern)."""
+    code = np.asarray(code).astype(np.uint32)
     hi = code >> 8                              # 0 .. 253
     lo = code & 0xFF
     hi = np.where(hi >= 0x7F, hi + 1, hi)       # 0..0x7E, 0x80..0xFE
-    return ((hi << 8) | lo).astype(np.uint16).reshape(shape)
+    return ((hi << 8) | lo).astype(np.uint16)
+
+
+def random_coded(shape, dtype: str, seed: int) -> np.ndarray:
+    """Tensor of independent random element codes (``default_rng(seed)``):
+    bf16: uniform over the 65024 finite patterns of ``index_coded``; f32:
+    integers below 2**24 as float32 (exact). Unlike ``index_coded`` nothing
+    repeats with a period, so a block of elements moved to a wrong place
+    differs from what belongs there with overwhelming probability, at any
+    size (the bitwise relayout tests on full-size tensors use it)."""
+    rng = np.random.default_rng(seed)
+    if dtype == F32:
+        return rng.integers(0, 1 << 24, size=shape).astype(np.float32)
+    return _finite_bf16_pattern(rng.integers(0, 65024, size=shape))
