@@ -171,15 +171,16 @@ def sq_summary(dirs, out_txt):
         if n_mfma is not None:
             lines.append(f"  MFMA instructions {n_mfma:.4e} x 32768 flop (32x32x16) = "
                          f"{n_mfma * 32768:.4e} ({n_mfma * 32768 / ATTN_FLOPS:.4f}x algorithmic)")
-        busy, gui = a.get("SQ_VALU_MFMA_BUSY_CYCLES"), a.get("GRBM_GUI_ACTIVE")
-        if busy is not None and gui:
-            # GRBM_GUI_ACTIVE counts each XCD's active cycles (8 instances):
-            # the kernel's cycles are gui / 8; 1024 SIMDs
-            cyc = gui / 8
-            lines.append(f"  GRBM_GUI_ACTIVE / 8 XCDs = {cyc:.4e} cycles"
+        busy, sqb = a.get("SQ_VALU_MFMA_BUSY_CYCLES"), a.get("SQ_BUSY_CYCLES")
+        if busy is not None and sqb:
+            # SQ_BUSY_CYCLES sums the busy cycles of the 32 shader engines: a
+            # dispatch that keeps every engine busy lasts sqb / 32 cycles
+            cyc = sqb / 32
+            lines.append(f"  SQ_BUSY_CYCLES / 32 engines = {cyc:.4e} cycles"
                          + (f" (= {cyc / (dur * 1e-9) / 1e9:.3f} GHz over the dispatch)" if dur else ""))
-            lines.append(f"  matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = "
-                         f"{busy / (1024 * cyc):.3f}")
+            lines.append(f"  matrix cores: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs = {busy / 1024:.4e} cycles "
+                         f"= {busy / (1024 * cyc):.3f} of the dispatch ({busy / 1024 / (n_mfma / 1024):.1f} "
+                         f"cycles per MFMA)" if n_mfma else "")
         coex = a.get("SQ_VALU_MFMA_COEXEC_CYCLES")
         if coex is not None and busy:
             lines.append(f"  VALU issued while the matrix core is busy: {coex / busy:.3f} of busy cycles")
@@ -329,6 +330,56 @@ def oracle_parts(data, target_s):
                       f"{s['wall_s']:.1f} s, fp64 NumPy, {cores} procs",
             "parts": parts}
 
+def short_kernel_name(name):
+    """A readable name for a kernel of this benchmark in a trace."""
+    kind = kernel_kind(name)
+    if kind:
+        return {"attention": "attn_bf16_kernel<D=128, key halves> (fwd_ws)",
+                "attention_groups": "attn_bf16_kernel<D=128, key groups> (fwd)",
+                "merge": "attn_merge_halves<D=128>", "copy": "__amd_rocclr_copyBuffer",
+                "pack": "relayout_kernel<pack>", "unpack": "relayout_kernel<unpack>"}[kind]
+    n = name.replace("void ", "").replace("usp::(anonymous namespace)::", "")
+    return n[:56]
+
+
+def trace_summary(dirs, out_txt, warmup, steps):
+    """Summarise a rocprofv3 --kernel-trace run of this benchmark: calls and
+    average / minimum / maximum duration per kernel, and the key-half
+    attention kernel's durations per call; the serial steps' timed calls are
+    dispatches warmup + 1 .. warmup + steps of that kernel (and of the
+    merge), whose mean is compared with the events of the same run."""
+    rows = []
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            with open(path) as f:
+                rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = {}
+    for r in rows:
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(us)
+    total = sum(sum(v) for v in per.values())
+    lines = [f"# kernel source: attn_bf16.hip sha256 {source_digest()}", "",
+             f"{'kernel':56s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{name:56s} {len(v):6d} {np.mean(v):9.1f} {min(v):9.1f} {max(v):9.1f} "
+                     f"{100 * sum(v) / total:6.2f}")
+    att = per.get(short_kernel_name("attn_bf16_kernel<128, 8, 1, 2,"), [])
+    mrg = per.get(short_kernel_name("attn_merge_halves"), [])
+    lines += ["", "key-half attn_bf16_kernel durations per call (us), in order: " +
+              " ".join(f"{x:.0f}" for x in att)]
+    if len(att) >= warmup + steps and len(mrg) >= warmup + steps:
+        a = float(np.mean(att[warmup:warmup + steps]))
+        m = float(np.mean(mrg[warmup:warmup + steps]))
+        lines.append(f"serial steps' timed calls ({steps} after {warmup} warmup): attn_bf16_kernel "
+                     f"{a:.1f} us + attn_merge_halves {m:.1f} us = {a + m:.1f} us per call")
+    text = "\n".join(lines)
+    print(text)
+    if out_txt:
+        with open(out_txt, "w") as f:
+            f.write(text + "\n")
+
+
 class Timer:
     """HIP events around every call of a leg on one stream; summary in ms."""
 
@@ -375,6 +426,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="minimum untimed warm-up time before the timed steps")
     ap.add_argument("--relayout-reps", type=int, default=6)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle's video-DiT attention sample")
@@ -386,6 +439,12 @@ def main():
     ap.add_argument("--pmc-sq", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 SQ/GRBM counter runs of this benchmark and exit")
     ap.add_argument("--pmc-out", metavar="FILE", help="text file for --pmc-sq's summary")
+    ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of this benchmark and exit "
+                         "(with the run's --steps and --warmup)")
+    ap.add_argument("--trace-out", metavar="FILE", help="text file for --trace-summary")
+    ap.add_argument("--trace-json", metavar="FILE",
+                    help="the traced run's JSON line (gives its warm-up and timed step counts)")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -393,6 +452,14 @@ def main():
         return
     if args.pmc_sq:
         sq_summary(args.pmc_sq, args.pmc_out)
+        return
+    if args.trace_summary:
+        warm, steps = args.warmup, args.steps
+        if args.trace_json:  # the traced run's own output: its warm-up and timed steps
+            with open(args.trace_json) as f:
+                run = json.loads(f.read().strip().splitlines()[-1])
+            warm, steps = run["config"]["warmup_steps_done"], run["steps"]
+        trace_summary(args.trace_summary, args.trace_out, warm, steps)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not "
@@ -462,9 +529,17 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    say(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    # warm-up: W steps, and more until the GPU has been busy for
+    # --warmup-seconds (a fresh process's first attention calls run up to 25%
+    # slower while the shader clock ramps up); none of it is timed
+    say(f"warmup {args.warmup} steps (at least {args.warmup_seconds} s)")
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t0 < args.warmup_seconds:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
@@ -530,8 +605,12 @@ def main():
             p_unpack(i)
         main_s.wait_event(ev_unp[(n - 1) % 2])
 
-    pipelined(args.warmup)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_pwarm = 0
+    while n_pwarm < args.warmup or time.perf_counter() - t0 < args.warmup_seconds / 2:
+        pipelined(max(args.warmup, 4))
+        torch.cuda.synchronize()
+        n_pwarm += max(args.warmup, 4)
     say(f"timing {args.steps} pipelined steps")
     a, b_ = ev(), ev()
     a.record(main_s)
@@ -900,7 +979,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "video_dit_share", "B": B, "S": S, "H": H, "h": h0, "D": D,
-                   "P": P, "rank": 0,
+                   "P": P, "rank": 0, "warmup_steps_done": n_warm,
                    "step": "pack rank-0 shard of q,k,v -> attention on head group 0 -> unpack "
                            "rank-0 rows; pipelined on two streams"},
         "attention": dict(t_attn, **{"TFLOP/s": attn_tflops, "frac_peak": attn_tflops / PEAK_BF16_TFLOPS,
