@@ -132,25 +132,29 @@ def test_chunked_bitwise_equals_single_shot_small(h, chunks):
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
 
 
-# Launch plans on a device with 256 CUs: tiles of 256 query rows; whole
-# rounds of 256 tiles run as 8-wave workgroups, a last round of t <= 128
-# tiles as 2t 4-wave workgroups of 128 rows (one per CU).
-TAIL_CASES = [  # B, S, h, D, plan
-    (1, 257, 50, 128, "100 tiles, all in 4-wave halves (second halves past S)"),
-    (1, 513, 25, 64, "75 tiles, all in 4-wave halves"),
-    (1, 1000, 2, 128, "8 tiles, all in 4-wave halves"),
-    (1, 257, 178, 64, "356 tiles: 256 whole, 100 in halves"),
-    (1, 257, 100, 128, "200 tiles: a tail over half the CUs runs whole"),
-    (3, 64, 7, 128, "21 tiles of one key tile each, in halves"),
+# The key walk's branches. Keys are walked in tiles of BN (64 at D = 128,
+# 128 at D = 64), nkt = ceil(S / BN) tiles, split once into halves of
+# floor(nkt / 2) and the rest (the second holds the partial last tile); a
+# half walks pairs of unguarded steps while every load lies before its last
+# tile, then guarded steps, then a single step when its length is even, then
+# the masked last tile. Query rows run in tiles of 256 (the last one partial).
+EDGE_CASES = [  # B, S, h, D, what the case exercises
+    (3, 64, 7, 128, "nkt = 1: the first half is empty, the second one whole tile"),
+    (2, 37, 3, 64, "nkt = 1 with a partial tile: 37 of 128 keys, one partial query tile"),
+    (1, 100, 5, 128, "nkt = 2: one tile per half, the second partial"),
+    (1, 257, 6, 128, "nkt = 5 (odd): halves of 2 and 3 tiles, one key past a whole tile"),
+    (1, 513, 4, 64, "nkt = 5 at D = 64, partial last tile of 1 key, 3 query tiles"),
+    (1, 1000, 2, 128, "nkt = 16: halves of 8 with unguarded pairs, guarded pairs and a single step"),
+    (1, 4157, 3, 128, "nkt = 65: halves of 32 and 33, long unguarded runs, a 61-key last tile"),
 ]
 
 
-@pytest.mark.parametrize("B,S,h,D,plan", TAIL_CASES)
-def test_tail_round_plans(B, S, h, D, plan):
+@pytest.mark.parametrize("B,S,h,D,plan", EDGE_CASES)
+def test_key_walk_edge_cases(B, S, h, D, plan):
     q, k, v = synth.draw_qkv(B, S, h, D, seed=11 + S + h)
     qf, kf, vf = (widen(x, BF) for x in (q, k, v))
     ref, ref_lse = A.attention(qf, kf, vf, return_lse=True)
-    log(f"attention tail plan B={B} S={S} h={h} D={D}: {plan}")
+    log(f"attention edge case B={B} S={S} h={h} D={D}: {plan}")
     out, lse = _run(q, k, v, BF, F, want_lse=True)
     ma, rf = err(out, ref)
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
@@ -161,9 +165,10 @@ def test_tail_round_plans(B, S, h, D, plan):
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_rows_bitwise_independent_of_launch(D):
-    """40 heads at once are 160 tiles, a tail over more than half the CUs, so
-    every tile runs in an 8-wave workgroup; head ranges of 10 heads are 40
-    tiles each, all in 4-wave halves. Both give the same bits."""
+    """A row's arithmetic depends on S, D and its own head only: 40 heads in
+    one launch (160 query tiles, 320 key-half workgroups) and four launches
+    of 10 heads (80 workgroups each, a different spread over the CUs and XCDs)
+    give the same bits."""
     q, k, v = synth.draw_qkv(1, 1000, 40, D, seed=31)
     log(f"attention D={D}: 40 heads in one launch vs four launches of 10 heads")
     one = _run(q, k, v, BF, F)
@@ -369,16 +374,26 @@ def _risky_rows(qf, kf, b, hd, n):
     return np.unique(np.concatenate([order1, order2]))
 
 
-def _check_sampled(out, q, k, v, dtype, B, S, rows_per_head, lse=None):
-    """Compare ``out`` against the oracle on ``rows_per_head[(b, head)]``."""
+def _check_sampled(out, q, k, v, dtype, B, S, rows_per_head, lse=None, out_bf16=None):
+    """Compare ``out`` (the fp32-output epilogue) against the oracle on
+    ``rows_per_head[(b, head)]``; ``out_bf16`` (the bf16-output epilogue of
+    the same call, bf16 bits) is graded per element on the same rows within
+    max(1e-2, one bf16 ulp of the reference)."""
     qf, kf, vf = (widen(x, dtype) for x in (q, k, v))
     par = A.attention_parallel(qf, kf, vf, rows_per_head=rows_per_head,
                                workers=min(16, A.host_cores()))
-    got, ref, lg, lr = [], [], [], []
+    got, ref, lg, lr, gb = [], [], [], [], []
     for (b, hd), (rows, o, ls) in par.items():
         got.append(out[b, rows, hd]); ref.append(o)
+        if out_bf16 is not None:
+            gb.append(widen(out_bf16[b, rows, hd], BF))
         if lse is not None:
             lg.append(lse[b, hd, rows]); lr.append(ls)
+    if out_bf16 is not None:
+        r = np.concatenate(ref)
+        d = np.abs(np.concatenate(gb) - r)
+        log(f"sampled bf16-output epilogue: max_abs={d.max():.3e}")
+        assert np.all(d <= np.maximum(BF16_MAX_ABS, bf16_ulp(r))), float(d.max())
     ma, rf = err(np.concatenate(got), np.concatenate(ref))
     log(f"sampled parity: {sum(len(r) for r in rows_per_head.values())} rows "
         f"max_abs={ma:.3e} rel_frob={rf:.3e}")
@@ -418,11 +433,19 @@ def test_video_dit_share_full_size():
     torch.cuda.synchronize()
     assert to_host(o2).tobytes() == out.tobytes()
     assert lse2.cpu().numpy().tobytes() == lse.cpu().numpy().tobytes()
-    del ws, o2, lse2
+    # the benched epilogue (bf16 output, workspace): the fp32 result rounded
+    # to nearest even, bit for bit, over the whole output
+    log("workload video_dit_share: attention block 0, bf16 output, workspace")
+    ob = poisoned((w.B, w.S, h0, w.D), BF)
+    usp.usp_attention_fwd_ws(blocks[0], blocks[1], blocks[2], ob, ws)
+    torch.cuda.synchronize()
+    out_b = to_host(ob)
+    assert out_b.tobytes() == synth.f32_to_bf16_bits(out).tobytes()
+    del ws, o2, lse2, ob
     sl = slice(hb[0], hb[1])
     rows = {(0, hd): _sample_rows(w.S, 256, 30 + hd) for hd in range(h0)}
     _check_sampled(out, q[:, :, sl], k[:, :, sl], v[:, :, sl], BF, w.B, w.S, rows,
-                   lse=lse.cpu().numpy())
+                   lse=lse.cpu().numpy(), out_bf16=out_b)
 
 
 def test_long_chunked_full_size():
@@ -447,6 +470,10 @@ def test_indivisible_long_full_size():
     log("workload indivisible_long: pack -> attention x4 -> unpack (S=65537)")
     out = _ulysses_gpu(w, q, k, v, F)
     assert not np.any(np.isnan(out))
+    log("workload indivisible_long: the same with bf16 output")
+    out_b = _ulysses_gpu(w, q, k, v, BF)
+    # the bf16-output epilogue is the fp32 result rounded to nearest even, everywhere
+    assert out_b.tobytes() == synth.f32_to_bf16_bits(out).tobytes()
     kf = widen(k, BF)
     qf = widen(q, BF)
     rows = {}
@@ -457,7 +484,7 @@ def test_indivisible_long_full_size():
                 r = np.unique(np.concatenate([r, _risky_rows(qf, kf, b, hd, 400)]))
             rows[(b, hd)] = r
     del kf, qf
-    _check_sampled(out, q, k, v, BF, w.B, w.S, rows)
+    _check_sampled(out, q, k, v, BF, w.B, w.S, rows, out_bf16=out_b)
 
 
 def test_gqa_video_share_full_size():

@@ -641,6 +641,24 @@ __global__ __launch_bounds__(256) void attn_merge_halves(Params p) {
   if (p.lse && ch == 0) p.lse[(size_t(b) * p.h + head) * p.Sq + row] = fmaf(mx, p.scale, logf(lt));
 }
 
+// Whether a row's key walk is split into two halves: a function of the key
+// count and the tile size only, so every launch form and head range gives a
+// row the same arithmetic. Short walks (under 8 tiles) are not split: the
+// merge would cost more than the balance gains. Very long ones (over 1024
+// tiles) are not either: ceil(S / 256) query tiles then fill at least a
+// round of workgroups per head and batch row, so whole walks leave a short
+// tail and save the merge.
+#ifndef USP_SPLIT_MIN
+#define USP_SPLIT_MIN 8
+#endif
+#ifndef USP_SPLIT_MAX
+#define USP_SPLIT_MAX 1024
+#endif
+bool split_keys(int64_t Sk, int BN) {
+  const int64_t nkt = (Sk + BN - 1) / BN;
+  return nkt >= USP_SPLIT_MIN && nkt <= USP_SPLIT_MAX;
+}
+
 // Bytes of the key-half workspace for `tiles` tiles of 256 rows.
 size_t halves_ws_bytes(int64_t tiles, int D) {
   return size_t(tiles) * 2 * kTileRows * (size_t(D) + 3) * sizeof(float);
@@ -648,6 +666,11 @@ size_t halves_ws_bytes(int64_t tiles, int D) {
 
 template <int D, int BN, bool kOutBf16>
 int launch_tiles(Params& p, int64_t tiles, void* ws, hipStream_t s) {
+  if (!split_keys(p.Sk, BN)) {
+    // whole key walks in 256-row workgroups: no state to merge, no workspace
+    attn_bf16_kernel<D, 8, 1, 1, BN, kOutBf16><<<unsigned(tiles), 512, 0, s>>>(p);
+    return check_launch("attn_bf16_kernel (whole walks)");
+  }
   if (!ws) {
     // key groups: two 128-row workgroups per tile
     attn_bf16_kernel<D, 8, 2, 1, BN, kOutBf16><<<unsigned(tiles * 2), 512, 0, s>>>(p);
