@@ -134,12 +134,13 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // 16 bytes per lane from global memory straight into LDS
-// (buffer_load_dwordx4 ... lds): lane i reads base + voff (a 32-bit byte
-// offset; base wave-uniform, the buffer descriptor built from it in scalar
-// registers: raw buffer, stride 0, no range clamp in practice since offsets
-// stay inside the tensor) and its bytes land at lds_base + 16 i, lds_base
-// uniform over the wave (M0). Per-lane addressing is a fixed 32-bit offset,
-// so a load costs no per-lane address arithmetic.
+// (buffer_load_dwordx4 ... lds): lane i reads resource base + soff + voff
+// (soff a wave-uniform byte offset in a scalar register, voff the lane's
+// 32-bit byte offset; raw buffer, stride 0, no range clamp in practice since
+// offsets stay inside the tensor) and its bytes land at lds_addr + 16 i,
+// lds_addr uniform over the wave (M0). Per-lane addressing is a fixed 32-bit
+// offset and the resource is built once, so a load costs no per-lane and
+// almost no scalar address arithmetic.
 //
 // Written as inline assembly on purpose: issued through the compiler's
 // builtin, the load counts as an LDS write of unknown address, and the
@@ -149,20 +150,28 @@ __device__ __forceinline__ float sum_halves(float x) {
 // (measured: 4-5% of the kernel's time). The kernel waits for its own loads
 // (loads_done) before the barrier that publishes them. The instruction has
 // no register result. The host pass sees an empty body.
-__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, void* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource at `addr` (bytes, wave-uniform) covering 2^31 - 1 bytes.
+__device__ __forceinline__ i32x4 buffer_rsrc(uint64_t addr) {
   i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
-  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu));
   r[2] = 0x7fffffff;
   r[3] = 0x00020000;
-  const int m0 = __builtin_amdgcn_readfirstlane(
-      int(uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds_base))));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  return r;
+}
+
+// 16 bytes per lane from rsrc + soff + voff (soff wave-uniform) straight into
+// LDS at lds_addr + 16 lane (lds_addr wave-uniform, an LDS byte address).
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t soff, uint32_t voff,
+                                           uint32_t lds_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int m0 = __builtin_amdgcn_readfirstlane(int(lds_addr));
+  const int so = __builtin_amdgcn_readfirstlane(int(soff));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(r)
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(so)
                : "memory", "m0");
 #endif
 }
@@ -199,8 +208,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 
   // ---- XCD-aware workgroup -> (batch, head, query tile, sub-tile[, part])
   const int u = xcd_remap(blockIdx.x, gridDim.x);
-  const int part = PARTS == 2 ? u / p.n_tiles : 0;
-  const int lid = PARTS == 2 ? u % p.n_tiles : u / SUB, sub = PARTS == 2 ? 0 : u % SUB;
+  // key halves: the two halves of a tile are adjacent logical ids, so that
+  // the XCD-aware remap puts both on one XCD, where they share the tile's Q
+  const int part = PARTS == 2 ? (u & 1) : 0;
+  const int lid = PARTS == 2 ? (u >> 1) : u / SUB, sub = PARTS == 2 ? 0 : u % SUB;
   const int qt = lid % p.n_qtiles;
   const int bh = lid / p.n_qtiles;
   const int head = p.head_lo + bh % p.nheads;
@@ -257,23 +268,45 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
   const uint32_t vgo = uint32_t((lr0 * rsk + (lpos ^ swz_v(lr0)) * 8) * 2);
   // A tile that runs past Sk loads key row Sk - 1 in place of the missing rows:
   // finite data whose scores the mask sets to -inf (weight 0).
-  auto issue = [&](const uint16_t* src, uint32_t go, int lbase, int t0, bool guard, bool is_v) {
+  //
+  // Addressing: one buffer resource per tensor at (batch b, key 0, K/V head)
+  // for the whole walk, the tile's first key row and the load's row block as
+  // the scalar offset, the lane's chunk as the vector offset. Where one
+  // (batch, head) slab spans 2^31 bytes or more (the range of a resource and
+  // of its offsets) the resource is rebuilt at every tile's first key row.
+  const uint32_t rsk2 = uint32_t(rsk * 2);  // K/V token row stride, bytes
+  const bool rebase = uint64_t(Sk) * rsk2 >= 0x7fffffffull;
+  const uint64_t kaddr = reinterpret_cast<uint64_t>(p.k + hbk);
+  const uint64_t vaddr = reinterpret_cast<uint64_t>(p.v + hbk);
+  const i32x4 krs = buffer_rsrc(kaddr), vrs = buffer_rsrc(vaddr);
+  const uint32_t lds_grp =
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)) +
+      uint32_t(grp * 4 * TB) + uint32_t(w * 1024);
+  auto issue = [&](const i32x4& rs0, uint64_t addr, uint32_t go, int lbase, int t0, bool guard,
+                   bool is_v) {
+    i32x4 rs = rs0;
+    uint32_t s0 = uint32_t(t0) * rsk2;
+    if (rebase) {
+      rs = buffer_rsrc(addr + uint64_t(t0) * rsk2);
+      s0 = 0;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint16_t* base = src + hbk + size_t(t0) * rsk;
-      uint32_t off;
+      uint32_t soff = s0, off;
       if (guard) {  // rows are clamped relative to the tile's first row (< Sk)
         const int r = GW * RPI * i + lr0, rc = min(r, Sk - 1 - t0);
         off = uint32_t((rc * rsk + (lpos ^ (is_v ? swz_v(r) : swz_k(r))) * 8) * 2);
       } else {
-        base += size_t(GW * RPI * i) * rsk;
+        soff += uint32_t(GW * RPI * i) * rsk2;
         off = go;
       }
-      load_lds16(base, off, glds + lbase + (w + GW * i) * 1024);
+      load_lds16(rs, soff, off, lds_grp + uint32_t(lbase + GW * i * 1024));
     }
   };
-  auto load_k = [&](int buf, int t0, bool guard) { issue(p.k, kgo, buf * TB, t0, guard, false); };
-  auto load_v = [&](int buf, int t0, bool guard) { issue(p.v, vgo, (2 + buf) * TB, t0, guard, true); };
+  auto load_k = [&](int buf, int t0, bool guard) { issue(krs, kaddr, kgo, buf * TB, t0, guard, false); };
+  auto load_v = [&](int buf, int t0, bool guard) {
+    issue(vrs, vaddr, vgo, (2 + buf) * TB, t0, guard, true);
+  };
   // the wave's direct loads have landed in LDS (a barrier then publishes them)
   auto loads_done = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
