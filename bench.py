@@ -43,7 +43,10 @@ a leg says "cold"):
     sequence (B=1, S=131072, h=8, 3/3/2) against single shot; the same step
     as the two-phase exchange (per head chunk 2/2/1: pack, attention,
     unpack); the world relayouts of the [1, 32760, 40, 128] tensor (one
-    tensor, and q, k, v in one launch; whole groups and one head chunk); the
+    tensor, and q, k, v in one launch; whole groups and one head chunk) and
+    rank 0's share of them (pack of q, k, v; unpack of one tensor), these
+    also timed back to back (mean of calls between two events: the launch
+    and event overhead of a 16 us call is a sixth of it); the
     model-boundary row movements at [1, 32760, 5120]; a 1 GiB device copy as
     the practical HBM reference.
 
@@ -402,15 +405,61 @@ class Timer:
                 "mean_ms": float(ms.mean()), "calls": int(len(ms))}
 
 
-def timed(torch, fn, reps, warm=3):
-    """Median / minimum / mean of ``reps`` calls of ``fn(i)`` after ``warm``."""
+_SPIN = {"cycles_per_ms": None}
+
+
+def queue_ahead(torch, host_ms):
+    """Queue a GPU spin of about ``host_ms`` + 1 ms (capped at 250 ms) in
+    front of work about to be enqueued. The calls timed behind it then find
+    the GPU busy and run back to back, so the events around a short call
+    measure the GPU's time for it, not the host's argument marshalling and
+    launch (which for a 16 us relayout is longer than the kernel)."""
+    if _SPIN["cycles_per_ms"] is None:
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(4_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN["cycles_per_ms"] = 4_000_000 / max(a.elapsed_time(b), 1e-3)
+    ms = min(host_ms + 1.0, 250.0)
+    torch.cuda._sleep(int(ms * _SPIN["cycles_per_ms"]))
+
+
+def host_ms_per_call(torch, fn, warm):
+    """Warm-up calls of ``fn(i)``; returns the host's enqueue time per call (ms)."""
+    t0 = time.perf_counter()
     for i in range(warm):
         fn(i)
+    host = (time.perf_counter() - t0) * 1e3 / max(warm, 1)
     torch.cuda.synchronize()
+    return host
+
+
+def timed(torch, fn, reps, warm=3):
+    """Median / minimum / mean of ``reps`` calls of ``fn(i)`` after ``warm``,
+    each between two HIP events, issued behind a GPU spin (queue_ahead)."""
+    host = host_ms_per_call(torch, fn, warm)
+    queue_ahead(torch, 1.5 * host * reps)
     t = Timer(torch)
     for i in range(reps):
         t(fn, i)
     return t.summary()
+
+
+def back_to_back(torch, fn, reps, warm=3):
+    """Mean per call of ``reps`` calls of ``fn(i)`` issued back to back
+    between two HIP events (no event between calls) behind a GPU spin, in ms."""
+    host = host_ms_per_call(torch, fn, warm)
+    queue_ahead(torch, 1.5 * host * reps)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 def tflops(flops, ms):
@@ -858,11 +907,10 @@ def main():
                 tw[1].ev.append((a_, b2))
                 tw[2](usp.usp_unpack_heads_to_seq, ob, out)
 
-            for i in range(3):
-                run(i)
-            torch.cuda.synchronize()
+            host = host_ms_per_call(torch, run, 3)
             tw = [Timer(torch) for _ in range(4)]
             n = max(6, reps)
+            queue_ahead(torch, 1.5 * host * n)
             whole = Timer(torch)
             for i in range(n):
                 whole(run, i)
@@ -916,6 +964,25 @@ def main():
         rl("pack_chunk_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
             [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)], head_lo=0,
             head_hi=2), 3 * cb)
+        # rank 0's share, as in the step (one call moves one shard per
+        # tensor): per call with events, and back to back; sources and
+        # destinations rotate over 9 sets (377 MB of blocks)
+        len0 = tb[1] - tb[0]
+        shares = [[torch.empty((B, len0, H, D), dtype=torch.bfloat16, device=dev).normal_()
+                   for _ in range(3)] for _ in range(3)]
+        sb = 2 * B * len0 * H * D * 2
+        share_legs = (
+            ("pack_qkv_rank0", lambda i: usp.usp_pack_seq_to_heads_planes(
+                [shares[t][i % 3] for t in range(3)], [dsts[t][(i + t) % 3] for t in range(3)], rank=0),
+             3 * sb),
+            ("unpack_rank0", lambda i: usp.usp_unpack_heads_to_seq(
+                dsts[i % 9 // 3][i % 3], shares[i % 9 // 3][i % 3], rank=0), sb))
+        for name, fn, moved in share_legs:
+            rl(name, fn, moved)
+            ms_b2b = back_to_back(torch, fn, args.relayout_reps)
+            rel[name].update({"back_to_back_ms": ms_b2b, "GB/s_back_to_back": gbs(moved, ms_b2b),
+                              "frac_peak_back_to_back": gbs(moved, ms_b2b) / PEAK_HBM_GBS})
+        del shares
         for r in rel.values():
             r["frac_of_copy"] = r["GB/s"] / copy_gbs
         del sets, dsts
@@ -961,6 +1028,9 @@ def main():
                                    "pack_qkv_GB/s": rr["pack_qkv_GB/s"], "unpack_GB/s": rr["unpack_GB/s"]}
     for name, r in rel.items():
         summary["relayout_" + name] = {"GB/s": r["GB/s"], "frac": r["frac_peak"]}
+        if "GB/s_back_to_back" in r:
+            summary["relayout_" + name].update({"GB/s_back_to_back": r["GB/s_back_to_back"],
+                                                "frac_back_to_back": r["frac_peak_back_to_back"]})
     for name in ("scatter", "gather", "reduce_scatter"):
         if name in rows_bw:
             summary["rows_" + name] = {"GB/s": rows_bw[name]["GB/s"], "frac": rows_bw[name]["frac_peak"]}

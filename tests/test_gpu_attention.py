@@ -520,3 +520,45 @@ def test_very_long_sequence_sampled():
     extra = np.array([255, 256, half - 1, half, half + 1, S - 257, S - 256])
     rows = {(0, 0): np.unique(np.concatenate([_sample_rows(S, 40, 92), extra]))}
     _check_sampled(out, q, k, v, BF, B, S, rows, lse=lse)
+
+
+@pytest.mark.parametrize("S,h,D,what", [
+    (61700, 136, 128, "key halves / key groups, ragged last tile"),
+    (262147, 64, 64, "whole walks (4097 key tiles), ragged last tile"),
+])
+def test_slab_beyond_2gib(S, h, D, what):
+    """A (batch, K/V head) slab of S * h * D * 2 >= 2^31 bytes: the K/V
+    loads then rebuild their buffer resource at every tile instead of
+    offsetting one resource. Only the last head is computed (the other heads
+    hold zeros and must stay untouched in the output); the workspace and
+    default entry points agree bit for bit, and sampled rows match the
+    oracle."""
+    import torch
+    assert S * h * D * 2 >= 2 ** 31 - 1
+    hd = h - 1
+    q1, k1, v1 = synth.draw_qkv(1, S, 1, D, seed=97)
+    dev = {}
+    for name, x in (("q", q1), ("k", k1), ("v", v1)):
+        t = torch.zeros((1, S, h, D), dtype=torch.bfloat16, device=DEV)
+        t[:, :, hd:hd + 1] = to_dev(x, BF)
+        dev[name] = t
+    outs = []
+    for use_ws in (True, False):
+        log(f"attention slab beyond 2 GiB ({what}): S={S} h={h} D={D} head {hd} ws={use_ws}")
+        o = poisoned((1, S, h, D), F)
+        lse = torch.full((1, h, S), float("nan"), device=DEV)
+        if use_ws:
+            nb = usp.usp_attention_workspace_bytes(usp.USP_BF16, 1, S, 1, D)
+            ws = torch.full((nb // 4,), float("nan"), device=DEV)
+            usp.usp_attention_fwd_ws(dev["q"], dev["k"], dev["v"], o, ws, head_lo=hd, head_hi=h, lse=lse)
+        else:
+            usp.usp_attention_fwd(dev["q"], dev["k"], dev["v"], o, head_lo=hd, head_hi=h, lse=lse)
+        torch.cuda.synchronize()
+        assert bool(torch.isnan(o[:, :, :hd]).all()) and bool(torch.isnan(lse[:, :hd]).all())
+        outs.append((to_host(o[:, :, hd:h]), lse[:, hd:h].cpu().numpy()))
+        del o, lse
+    (out, lse), (out2, lse2) = outs
+    assert out.tobytes() == out2.tobytes() and lse.tobytes() == lse2.tobytes()
+    assert not np.any(np.isnan(out))
+    rows = {(0, 0): np.unique(np.concatenate([_sample_rows(S, 24, 98), [0, S - 1]]))}
+    _check_sampled(out, q1, k1, v1, BF, 1, S, rows, lse=lse)
