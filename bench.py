@@ -87,6 +87,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "ulysses_sequence_attention_amd", "csrc", "attn_bf16.hip")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_video_dit_share_traffic.json")
 COPY_BYTES = 1 << 30
+# groups of legs besides the step (--legs selects some, e.g. for a profiler run)
+LEG_GROUPS = ("single", "gqa", "ring", "chunked", "two_phase", "worlds", "relayout", "rows")
 
 
 def source_digest(path=ATTN_SRC) -> str:
@@ -109,17 +111,28 @@ def stored_traffic():
 
 def kernel_kind(name):
     """Short name of a kernel of this benchmark from its rocprofv3 name."""
-    return ("attention" if "attn_bf16_kernel<128, 8, 1, 2," in name else
-            "attention_groups" if "attn_bf16_kernel<128, 8, 2, 1," in name else
-            "merge" if "attn_merge_halves" in name else
-            "copy" if "copyBuffer" in name else
-            "pack" if "relayout_kernel<true>" in name else
-            "unpack" if "relayout_kernel<false>" in name else None)
+    for key, kind in (("attn_bf16_kernel<128, 8, 1, 2, 64, true>", "attention"),
+                      ("attn_bf16_kernel<128, 8, 1, 2, 64, false>", "attention_f32out"),
+                      ("attn_bf16_kernel<128, 8, 2, 1, 64, true>", "attention_groups"),
+                      ("attn_bf16_kernel<128, 8, 2, 1, 64, false>", "attention_groups_f32out"),
+                      ("attn_bf16_kernel<128, 8, 1, 1, 64, true>", "attention_whole"),
+                      ("attn_merge_halves<128, true>", "merge"),
+                      ("attn_merge_halves<128, false>", "merge_f32out"),
+                      ("copyBuffer", "copy"),
+                      ("relayout_kernel<true>", "pack"), ("relayout_kernel<false>", "unpack"),
+                      ("relayout_chunk_kernel<true>", "pack_chunk"),
+                      ("relayout_chunk_kernel<false>", "unpack_chunk"),
+                      ("lse_merge_kernel", "lse_merge")):
+        if key in name:
+            return kind
+    return None
 
 
-def read_pmc(dirs):
+def read_pmc(dirs, by_grid=False):
     """rocprofv3 --pmc CSVs under ``dirs`` -> {(kind, counter): {dispatch: value}},
-    each value summed over the counter's instances (SEs, SIMDs, channels)."""
+    each value summed over the counter's instances (SEs, SIMDs, channels);
+    with ``by_grid`` the kind carries the dispatch's thread count,
+    "kind[threads]"."""
     per = {}
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -128,6 +141,8 @@ def read_pmc(dirs):
                     kind = kernel_kind(r["Kernel_Name"])
                     if kind is None:
                         continue
+                    if by_grid:
+                        kind = f"{kind}[{int(r['Grid_Size'])}]"
                     key = (kind, r["Counter_Name"])
                     per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
                     per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
@@ -205,15 +220,59 @@ def sq_summary(dirs, out_txt):
             f.write(text + "\n")
 
 
+def copy_factors(per):
+    """Calibration of FETCH_SIZE and WRITE_SIZE (KiB per dispatch) on the
+    1 GiB copies: bytes per KiB counted, read and write."""
+    # the runtime's copy kernel also serves small copies (a clone, a compare):
+    # calibrate on the 1 GiB copies only, the dispatches of at least half the
+    # largest count
+    cp = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = per.get(("copy", ctr))
+        if v:
+            mx = max(v.values())
+            cp[ctr] = float(np.mean([x for x in v.values() if x >= 0.5 * mx]))
+    ff = COPY_BYTES / (cp["FETCH_SIZE"] * 1024) if cp.get("FETCH_SIZE") else None
+    fw = COPY_BYTES / (cp["WRITE_SIZE"] * 1024) if cp.get("WRITE_SIZE") else None
+    return ff, fw
+
+
+def relayout_pmc_summary(dirs, out_txt):
+    """HBM bytes per dispatch of the relayout kernels from FETCH_SIZE and
+    WRITE_SIZE runs of this benchmark, per launch shape (thread count), with
+    the algorithmic bytes each way: every thread moves one 16-byte chunk, so
+    threads x 16 B (the last workgroup's idle threads aside)."""
+    ff, fw = copy_factors(read_pmc(dirs))
+    per = read_pmc(dirs, by_grid=True)
+    lines = [f"copy calibration ({COPY_BYTES} B read and written per dispatch): "
+             f"FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}" if ff and fw else "copy calibration missing",
+             "",
+             f"{'dispatch (kernel[threads])':42s} {'n':>3s} {'alg MB each way':>15s} "
+             f"{'HBM read MB':>11s} {'HBM write MB':>12s}"]
+    kinds = sorted({k for k, c in per if k.split("[")[0] in ("pack", "unpack", "pack_chunk", "unpack_chunk")},
+                   key=lambda k: (k.split("[")[0], -int(k.split("[")[1][:-1])))
+    for k in kinds:
+        f_k, w_k = per.get((k, "FETCH_SIZE")), per.get((k, "WRITE_SIZE"))
+        if not f_k or not w_k or not ff or not fw:
+            continue
+        threads = int(k.split("[")[1][:-1])
+        rb = float(np.mean(list(f_k.values()))) * 1024 * ff
+        wb = float(np.mean(list(w_k.values()))) * 1024 * fw
+        lines.append(f"{k:42s} {len(f_k):3d} {threads * 16 / 1e6:15.1f} {rb / 1e6:11.1f} {wb / 1e6:12.1f}")
+    text = "\n".join(lines)
+    print(text)
+    if out_txt:
+        with open(out_txt, "w") as f:
+            f.write(text + "\n")
+
+
 def pmc_summary(dirs, out_json):
     """Parse rocprofv3 --pmc counter CSVs (FETCH_SIZE and WRITE_SIZE runs of
     this benchmark) into per-kernel KiB per dispatch, calibrate both counters
     on the plain copy kernel (COPY_BYTES read and written per dispatch), and
     write the attention kernel's HBM traffic per launch to ``out_json``."""
     per = read_pmc(dirs)
-    # the runtime's copy kernel also serves small copies (a clone, a compare):
-    # calibrate on the 1 GiB copies only, the dispatches of at least half the
-    # largest count
+    ff, fw = copy_factors(per)
     for key in [k for k in per if k[0] == "copy"]:
         mx = max(per[key].values())
         per[key] = {d: v for d, v in per[key].items() if v >= 0.5 * mx}
@@ -221,10 +280,6 @@ def pmc_summary(dirs, out_json):
     lines = ["kernel     counter      KiB/dispatch  dispatches"]
     for (kind, ctr), val in sorted(avg.items()):
         lines.append(f"{kind:10s} {ctr:12s} {val:12.1f}  {len(per[(kind, ctr)])}")
-    f_copy = avg.get(("copy", "FETCH_SIZE"))
-    w_copy = avg.get(("copy", "WRITE_SIZE"))
-    ff = COPY_BYTES / (f_copy * 1024) if f_copy else None
-    fw = COPY_BYTES / (w_copy * 1024) if w_copy else None
     lines.append(f"copy calibration ({COPY_BYTES} B read and written per dispatch): "
                  f"FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}" if ff and fw else
                  "copy calibration missing")
@@ -338,9 +393,17 @@ def short_kernel_name(name):
     kind = kernel_kind(name)
     if kind:
         return {"attention": "attn_bf16_kernel<D=128, key halves> (fwd_ws)",
+                "attention_f32out": "attn_bf16_kernel<D=128, key halves, f32 out>",
                 "attention_groups": "attn_bf16_kernel<D=128, key groups> (fwd)",
-                "merge": "attn_merge_halves<D=128>", "copy": "__amd_rocclr_copyBuffer",
-                "pack": "relayout_kernel<pack>", "unpack": "relayout_kernel<unpack>"}[kind]
+                "attention_groups_f32out": "attn_bf16_kernel<D=128, key groups, f32 out>",
+                "attention_whole": "attn_bf16_kernel<D=128, whole walks>",
+                "merge": "attn_merge_halves<D=128>",
+                "merge_f32out": "attn_merge_halves<D=128, f32 out>",
+                "copy": "__amd_rocclr_copyBuffer",
+                "pack": "relayout_kernel<pack>", "unpack": "relayout_kernel<unpack>",
+                "pack_chunk": "relayout_chunk_kernel<pack>",
+                "unpack_chunk": "relayout_chunk_kernel<unpack>",
+                "lse_merge": "lse_merge_kernel"}[kind]
     n = name.replace("void ", "").replace("usp::(anonymous namespace)::", "")
     return n[:56]
 
@@ -357,18 +420,23 @@ def trace_summary(dirs, out_txt, warmup, steps):
             with open(path) as f:
                 rows += list(csv.DictReader(f))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    per = {}
+    per, per_grid = {}, {}
     for r in rows:
         us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        per.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(us)
+        name = short_kernel_name(r["Kernel_Name"])
+        per.setdefault(name, []).append(us)
+        wgs = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) * int(r["Grid_Size_Y"]) * \
+            int(r["Grid_Size_Z"])
+        per_grid.setdefault((name, wgs), []).append(us)
     total = sum(sum(v) for v in per.values())
     lines = [f"# kernel source: attn_bf16.hip sha256 {source_digest()}", "",
-             f"{'kernel':56s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
-    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{name:56s} {len(v):6d} {np.mean(v):9.1f} {min(v):9.1f} {max(v):9.1f} "
+             f"{'kernel':56s} {'workgroups':>10s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
+             f"{'max_us':>9s} {'pct':>6s}"]
+    for (name, wgs), v in sorted(per_grid.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{name:56s} {wgs:10d} {len(v):6d} {np.mean(v):9.1f} {min(v):9.1f} {max(v):9.1f} "
                      f"{100 * sum(v) / total:6.2f}")
-    att = per.get(short_kernel_name("attn_bf16_kernel<128, 8, 1, 2,"), [])
-    mrg = per.get(short_kernel_name("attn_merge_halves"), [])
+    att = per.get(short_kernel_name("attn_bf16_kernel<128, 8, 1, 2, 64, true>"), [])
+    mrg = per.get(short_kernel_name("attn_merge_halves<128, true>"), [])
     lines += ["", "key-half attn_bf16_kernel durations per call (us), in order: " +
               " ".join(f"{x:.0f}" for x in att)]
     if len(att) >= warmup + steps and len(mrg) >= warmup + steps:
@@ -483,11 +551,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-legs", action="store_true",
                     help="time only the video-DiT step (for profiler runs)")
+    ap.add_argument("--legs", metavar="LIST",
+                    help="comma-separated leg groups to run besides the step (default: all): "
+                         + ",".join(LEG_GROUPS))
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 counter runs of this benchmark and exit")
     ap.add_argument("--pmc-sq", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 SQ/GRBM counter runs of this benchmark and exit")
     ap.add_argument("--pmc-out", metavar="FILE", help="text file for --pmc-sq's summary")
+    ap.add_argument("--pmc-relayout", nargs="+", metavar="DIR",
+                    help="summarise FETCH_SIZE / WRITE_SIZE runs of the relayout legs and exit "
+                         "(text to --pmc-out)")
     ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
                     help="summarise a rocprofv3 --kernel-trace run of this benchmark and exit "
                          "(with the run's --steps and --warmup)")
@@ -498,6 +572,9 @@ def main():
 
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, TRAFFIC_JSON)
+        return
+    if args.pmc_relayout:
+        relayout_pmc_summary(args.pmc_relayout, args.pmc_out)
         return
     if args.pmc_sq:
         sq_summary(args.pmc_sq, args.pmc_out)
@@ -525,6 +602,13 @@ def main():
     w = synth.WORKLOADS["video_dit_share"]
     B, S, H, D, P = w.B, w.S, w.H, w.D, w.P
     legs_on = not args.skip_legs
+    chosen = None if args.legs is None else set(args.legs.split(","))
+    if chosen is not None and not chosen <= set(LEG_GROUPS):
+        raise SystemExit(f"--legs: unknown group(s) {sorted(chosen - set(LEG_GROUPS))}; "
+                         f"known: {','.join(LEG_GROUPS)}")
+
+    def on(group):
+        return legs_on and (chosen is None or group in chosen)
     names = ["video_dit_share"] + (["vit_l16", "indivisible_long", "long_chunked", "tiny_fp32"]
                                    if legs_on or not args.no_cpu_baseline else [])
     data = {}
@@ -679,256 +763,262 @@ def main():
     reps = max(5, args.steps // 4)
     blk0 = (blocks[0][0], blocks[1][0], blocks[2][0])
     if legs_on:
-        say("attention without workspace / without allocation / softmax scale 1")
-        legs["attn_no_workspace"] = timed(torch, lambda i: usp.usp_attention_fwd(*blk0, oblocks[0]), reps)
-        legs["attn_noalloc"] = timed(torch, lambda i: usp.usp_attention_fwd_noalloc(*blk0, oblocks[0]),
-                                     reps)
-        o_s1 = torch.empty((B, S, h0, D), dtype=torch.float32, device=dev)
-        legs["attn_scale1"] = timed(torch, lambda i: usp.usp_attention_fwd_ws(*blk0, o_s1, ws, scale=1.0),
-                                    reps)
-        # the scale-1 reading against the oracle on sampled rows (ungraded)
-        from oracle import attention as A
-        rows = np.sort(np.random.default_rng(7).choice(S, 48, replace=False))
-        qh, kh, vh = (synth.bf16_bits_to_f32(np.ascontiguousarray(x[:, :, :h0])).astype(np.float64)
-                      for x in data["video_dit_share"])
-        got = o_s1.cpu().numpy().astype(np.float64)
-        dmax, num, den = 0.0, 0.0, 0.0
-        for hd in range(h0):
-            ref, _ = A.attention_rows(qh, kh, vh, 0, hd, rows, scale=1.0)
-            d = got[0, rows, hd] - ref
-            dmax = max(dmax, float(np.abs(d).max()))
-            num += float((d * d).sum())
-            den += float((ref * ref).sum())
-        legs["attn_scale1"].update({"max_abs": dmax, "rel_frob": (num / den) ** 0.5,
-                                    "rows_checked": 48 * h0})
-        del o_s1, qh, kh, vh
+        if on("single"):
+            say("attention without workspace / without allocation / softmax scale 1")
+            legs["attn_no_workspace"] = timed(torch, lambda i: usp.usp_attention_fwd(*blk0, oblocks[0]), reps)
+            legs["attn_noalloc"] = timed(torch, lambda i: usp.usp_attention_fwd_noalloc(*blk0, oblocks[0]),
+                                         reps)
+            o_s1 = torch.empty((B, S, h0, D), dtype=torch.float32, device=dev)
+            legs["attn_scale1"] = timed(torch, lambda i: usp.usp_attention_fwd_ws(*blk0, o_s1, ws, scale=1.0),
+                                        reps)
+            # the scale-1 reading against the oracle on sampled rows (ungraded)
+            from oracle import attention as A
+            rows = np.sort(np.random.default_rng(7).choice(S, 48, replace=False))
+            qh, kh, vh = (synth.bf16_bits_to_f32(np.ascontiguousarray(x[:, :, :h0])).astype(np.float64)
+                          for x in data["video_dit_share"])
+            got = o_s1.cpu().numpy().astype(np.float64)
+            dmax, num, den = 0.0, 0.0, 0.0
+            for hd in range(h0):
+                ref, _ = A.attention_rows(qh, kh, vh, 0, hd, rows, scale=1.0)
+                d = got[0, rows, hd] - ref
+                dmax = max(dmax, float(np.abs(d).max()))
+                num += float((d * d).sum())
+                den += float((ref * ref).sum())
+            legs["attn_scale1"].update({"max_abs": dmax, "rel_frob": (num / den) ** 0.5,
+                                        "rows_checked": 48 * h0})
+            del o_s1, qh, kh, vh
 
-        # grouped K/V heads: rank 0's share of the grouped video-DiT workload
-        say("attention with grouped K/V heads")
-        gw = synth.WORKLOADS["gqa_video_share"]
-        gq, gk, gv = synth.draw_workload(gw)
-        ghq = usp.usp_balanced_ranges(gw.H, gw.P)
-        ghk = usp.usp_balanced_ranges(gw.kv_heads, gw.P)
-        q0 = bf(gq[:, :, ghq[0]:ghq[1]])
-        k0, v0 = (bf(x[:, :, ghk[0]:ghk[1]]) for x in (gk, gv))
-        del gq, gk, gv
-        o0 = torch.empty_like(q0)
-        gh = ghq[1] - ghq[0]
-        gws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, gw.B, gw.S, gh, gw.D),
-                          dtype=torch.uint8, device=dev)
-        legs["attn_gqa"] = timed(torch, lambda i: usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws), reps)
-        legs["attn_gqa"]["flop"] = 4.0 * gw.B * gh * gw.S * gw.S * gw.D
-        del q0, k0, v0, o0, gws
+        if on("gqa"):
+            # grouped K/V heads: rank 0's share of the grouped video-DiT workload
+            say("attention with grouped K/V heads")
+            gw = synth.WORKLOADS["gqa_video_share"]
+            gq, gk, gv = synth.draw_workload(gw)
+            ghq = usp.usp_balanced_ranges(gw.H, gw.P)
+            ghk = usp.usp_balanced_ranges(gw.kv_heads, gw.P)
+            q0 = bf(gq[:, :, ghq[0]:ghq[1]])
+            k0, v0 = (bf(x[:, :, ghk[0]:ghk[1]]) for x in (gk, gv))
+            del gq, gk, gv
+            o0 = torch.empty_like(q0)
+            gh = ghq[1] - ghq[0]
+            gws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, gw.B, gw.S, gh, gw.D),
+                              dtype=torch.uint8, device=dev)
+            legs["attn_gqa"] = timed(torch, lambda i: usp.usp_attention_fwd_gqa(q0, k0, v0, o0, ws=gws), reps)
+            legs["attn_gqa"]["flop"] = 4.0 * gw.B * gh * gw.S * gw.S * gw.D
+            del q0, k0, v0, o0, gws
 
-        # one rank's Ulysses+Ring pass: two key blocks, then the merge
-        say("Ulysses+Ring pass")
-        rw = synth.WORKLOADS["video_dit_ring"]
-        rq, rk, rv = (bf(x) for x in synth.draw_workload(rw))
-        rT = usp.usp_balanced_ranges(rw.S, rw.ring)
-        rc = usp.usp_balanced_ranges(rw.H, rw.P)
-        rh = rc[1] - rc[0]
+        if on("ring"):
+            # one rank's Ulysses+Ring pass: two key blocks, then the merge
+            say("Ulysses+Ring pass")
+            rw = synth.WORKLOADS["video_dit_ring"]
+            rq, rk, rv = (bf(x) for x in synth.draw_workload(rw))
+            rT = usp.usp_balanced_ranges(rw.S, rw.ring)
+            rc = usp.usp_balanced_ranges(rw.H, rw.P)
+            rh = rc[1] - rc[0]
 
-        def head_group0(x, i):
-            bl = blocks_of(rw.B, rT[i + 1] - rT[i], rc, rw.D)
-            usp.usp_pack_seq_to_heads(x[:, rT[i]:rT[i + 1]].contiguous(), bl)
-            return bl[0]
+            def head_group0(x, i):
+                bl = blocks_of(rw.B, rT[i + 1] - rT[i], rc, rw.D)
+                usp.usp_pack_seq_to_heads(x[:, rT[i]:rT[i + 1]].contiguous(), bl)
+                return bl[0]
 
-        qr = head_group0(rq, 0)
-        kvr = [(head_group0(rk, i), head_group0(rv, i)) for i in range(rw.ring)]
-        del rq, rk, rv
-        Sq = rT[1] - rT[0]
-        rws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, rw.B, Sq, rh, rw.D),
-                          dtype=torch.uint8, device=dev)
-        rws2 = torch.empty_like(rws)
-        o_acc = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.float32, device=dev)
-        l_acc = torch.empty((rw.B, rh, Sq), dtype=torch.float32, device=dev)
-        o_b2 = [torch.empty_like(o_acc) for _ in range(2)]
-        l_b2 = [torch.empty_like(l_acc) for _ in range(2)]
-        o_out = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.bfloat16, device=dev)
-        order = [0] + [(0 - i) % rw.ring for i in range(1, rw.ring)]
-        side = torch.cuda.Stream()
-        ev_blk = [torch.cuda.Event() for _ in range(2)]
-        ev_fold = [torch.cuda.Event() for _ in range(2)]
+            qr = head_group0(rq, 0)
+            kvr = [(head_group0(rk, i), head_group0(rv, i)) for i in range(rw.ring)]
+            del rq, rk, rv
+            Sq = rT[1] - rT[0]
+            rws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, rw.B, Sq, rh, rw.D),
+                              dtype=torch.uint8, device=dev)
+            rws2 = torch.empty_like(rws)
+            o_acc = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.float32, device=dev)
+            l_acc = torch.empty((rw.B, rh, Sq), dtype=torch.float32, device=dev)
+            o_b2 = [torch.empty_like(o_acc) for _ in range(2)]
+            l_b2 = [torch.empty_like(l_acc) for _ in range(2)]
+            o_out = torch.empty((rw.B, Sq, rh, rw.D), dtype=torch.bfloat16, device=dev)
+            order = [0] + [(0 - i) % rw.ring for i in range(1, rw.ring)]
+            side = torch.cuda.Stream()
+            ev_blk = [torch.cuda.Event() for _ in range(2)]
+            ev_fold = [torch.cuda.Event() for _ in range(2)]
 
-        def ring_pass(i, two_streams=True):
-            # the second block's attention on a second stream (a ring delivers
-            # it long before the first is done); folds in ring order on the first
-            ms_ = torch.cuda.current_stream()
-            st2 = side if two_streams else ms_
-            start = torch.cuda.Event()
-            start.record(ms_)
-            st2.wait_event(start)
-            for e in ev_fold:
-                e.record(ms_)
-            usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws, stream=ms_)
-            for n, blk in enumerate(order[1:]):
-                s2 = n % 2
-                st2.wait_event(ev_fold[s2])
-                usp.usp_attention_fwd_block(qr, *kvr[blk], o_b2[s2], lse=l_b2[s2],
-                                            ws=rws2 if two_streams else rws, stream=st2)
-                ev_blk[s2].record(st2)
-                ms_.wait_event(ev_blk[s2])
-                last = n == len(order) - 2
-                usp.usp_attention_merge(o_acc, l_acc, o_b2[s2], l_b2[s2], o_out if last else o_acc,
-                                        None if last else l_acc, stream=ms_)
-                ev_fold[s2].record(ms_)
+            def ring_pass(i, two_streams=True):
+                # the second block's attention on a second stream (a ring delivers
+                # it long before the first is done); folds in ring order on the first
+                ms_ = torch.cuda.current_stream()
+                st2 = side if two_streams else ms_
+                start = torch.cuda.Event()
+                start.record(ms_)
+                st2.wait_event(start)
+                for e in ev_fold:
+                    e.record(ms_)
+                usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws, stream=ms_)
+                for n, blk in enumerate(order[1:]):
+                    s2 = n % 2
+                    st2.wait_event(ev_fold[s2])
+                    usp.usp_attention_fwd_block(qr, *kvr[blk], o_b2[s2], lse=l_b2[s2],
+                                                ws=rws2 if two_streams else rws, stream=st2)
+                    ev_blk[s2].record(st2)
+                    ms_.wait_event(ev_blk[s2])
+                    last = n == len(order) - 2
+                    usp.usp_attention_merge(o_acc, l_acc, o_b2[s2], l_b2[s2], o_out if last else o_acc,
+                                            None if last else l_acc, stream=ms_)
+                    ev_fold[s2].record(ms_)
 
-        legs["ring_one_stream"] = timed(torch, lambda i: ring_pass(i, False), reps)
-        one = o_out.clone()
-        legs["ring"] = timed(torch, ring_pass, reps)
-        if not torch.equal(one, o_out):
-            raise RuntimeError("the two-stream ring pass changed the output")
-        legs["ring"]["flop"] = 4.0 * rw.B * rh * Sq * rw.S * rw.D
-        del qr, kvr, rws, rws2, o_acc, l_acc, o_b2, l_b2, o_out, one
+            legs["ring_one_stream"] = timed(torch, lambda i: ring_pass(i, False), reps)
+            one = o_out.clone()
+            legs["ring"] = timed(torch, ring_pass, reps)
+            if not torch.equal(one, o_out):
+                raise RuntimeError("the two-stream ring pass changed the output")
+            legs["ring"]["flop"] = 4.0 * rw.B * rh * Sq * rw.S * rw.D
+            del qr, kvr, rws, rws2, o_acc, l_acc, o_b2, l_b2, o_out, one
 
-        # head-chunked passes on the long-sequence share, against single shot
-        say("head-chunked passes (S=131072)")
-        cw = synth.WORKLOADS["long_chunked"]
-        cq, ck, cv = (bf(x) for x in data["long_chunked"])
-        co = torch.empty_like(cq)
-        cmax = -(-cw.H // cw.chunks)
-        cws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cmax, cw.D),
-                          dtype=torch.uint8, device=dev)
-        fws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cw.H, cw.D),
-                          dtype=torch.uint8, device=dev)
-        c_flops = 4.0 * cw.B * cw.H * cw.S * cw.S * cw.D
-        for name, fn in (("chunked", lambda i: usp.usp_attention_fwd_chunked(cq, ck, cv, co, cw.chunks)),
-                         ("chunked_ws", lambda i: usp.usp_attention_fwd_chunked_ws(cq, ck, cv, co,
-                                                                                   cw.chunks, cws)),
-                         ("single_shot", lambda i: usp.usp_attention_fwd(cq, ck, cv, co)),
-                         ("single_shot_ws", lambda i: usp.usp_attention_fwd_ws(cq, ck, cv, co, fws))):
-            legs["long_" + name] = timed(torch, fn, 3, warm=1)
-            legs["long_" + name]["flop"] = c_flops
-        del cq, ck, cv, co, cws, fws
+        if on("chunked"):
+            # head-chunked passes on the long-sequence share, against single shot
+            say("head-chunked passes (S=131072)")
+            cw = synth.WORKLOADS["long_chunked"]
+            cq, ck, cv = (bf(x) for x in data["long_chunked"])
+            co = torch.empty_like(cq)
+            cmax = -(-cw.H // cw.chunks)
+            cws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cmax, cw.D),
+                              dtype=torch.uint8, device=dev)
+            fws = torch.empty(usp.usp_attention_workspace_bytes(usp.USP_BF16, cw.B, cw.S, cw.H, cw.D),
+                              dtype=torch.uint8, device=dev)
+            c_flops = 4.0 * cw.B * cw.H * cw.S * cw.S * cw.D
+            for name, fn in (("chunked", lambda i: usp.usp_attention_fwd_chunked(cq, ck, cv, co, cw.chunks)),
+                             ("chunked_ws", lambda i: usp.usp_attention_fwd_chunked_ws(cq, ck, cv, co,
+                                                                                       cw.chunks, cws)),
+                             ("single_shot", lambda i: usp.usp_attention_fwd(cq, ck, cv, co)),
+                             ("single_shot_ws", lambda i: usp.usp_attention_fwd_ws(cq, ck, cv, co, fws))):
+                legs["long_" + name] = timed(torch, fn, 3, warm=1)
+                legs["long_" + name]["flop"] = c_flops
+            del cq, ck, cv, co, cws, fws
 
-        # the two-phase exchange on the same share: per head chunk (2/2/1 of
-        # the 5 heads), pack rank 0's rows of the chunk's heads (q, k, v in one
-        # launch), attention on them, unpack them. Overlapped: a chunk's pack
-        # for the next step and its unpack for this step go to the second
-        # stream as soon as this step's attention of that chunk is done.
-        say("two-phase steps")
-        kc = usp.usp_head_chunk_ranges(h0, 3)
-        ch = [(kc[c], kc[c + 1]) for c in range(len(kc) - 1)]
-        ws_c = torch.empty(usp.usp_attention_workspace_bytes(
-            usp.USP_BF16, B, S, max(hi - lo for lo, hi in ch), D), dtype=torch.uint8, device=dev)
-        e_cp = [torch.cuda.Event() for _ in ch]
-        e_ca = [torch.cuda.Event() for _ in ch]
-        e_cu = [torch.cuda.Event() for _ in ch]
-        for e in e_ca + e_cu:
-            e.record(main_s)
+        if on("two_phase"):
+            # the two-phase exchange on the same share: per head chunk (2/2/1 of
+            # the 5 heads), pack rank 0's rows of the chunk's heads (q, k, v in one
+            # launch), attention on them, unpack them. Overlapped: a chunk's pack
+            # for the next step and its unpack for this step go to the second
+            # stream as soon as this step's attention of that chunk is done.
+            say("two-phase steps")
+            kc = usp.usp_head_chunk_ranges(h0, 3)
+            ch = [(kc[c], kc[c + 1]) for c in range(len(kc) - 1)]
+            ws_c = torch.empty(usp.usp_attention_workspace_bytes(
+                usp.USP_BF16, B, S, max(hi - lo for lo, hi in ch), D), dtype=torch.uint8, device=dev)
+            e_cp = [torch.cuda.Event() for _ in ch]
+            e_ca = [torch.cuda.Event() for _ in ch]
+            e_cu = [torch.cuda.Event() for _ in ch]
+            for e in e_ca + e_cu:
+                e.record(main_s)
 
-        def tp_pack(c, stream):
-            usp.usp_pack_seq_to_heads_planes(shard, blocks, rank=0, head_lo=ch[c][0],
-                                             head_hi=ch[c][1], stream=stream)
+            def tp_pack(c, stream):
+                usp.usp_pack_seq_to_heads_planes(shard, blocks, rank=0, head_lo=ch[c][0],
+                                                 head_hi=ch[c][1], stream=stream)
 
-        def tp_attn(c):
-            usp.usp_attention_fwd_ws(*blk0, oblocks[0], ws_c, head_lo=ch[c][0], head_hi=ch[c][1],
-                                     stream=main_s)
+            def tp_attn(c):
+                usp.usp_attention_fwd_ws(*blk0, oblocks[0], ws_c, head_lo=ch[c][0], head_hi=ch[c][1],
+                                         stream=main_s)
 
-        def tp_unpack(c, stream):
-            usp.usp_unpack_heads_to_seq_chunk(oblocks, oshard, ch[c][0], ch[c][1], rank=0,
-                                              stream=stream)
+            def tp_unpack(c, stream):
+                usp.usp_unpack_heads_to_seq_chunk(oblocks, oshard, ch[c][0], ch[c][1], rank=0,
+                                                  stream=stream)
 
-        def tp_serial(n):
-            for _ in range(n):
-                for c in range(len(ch)):
-                    tp_pack(c, main_s)
-                    tp_attn(c)
-                    tp_unpack(c, main_s)
+            def tp_serial(n):
+                for _ in range(n):
+                    for c in range(len(ch)):
+                        tp_pack(c, main_s)
+                        tp_attn(c)
+                        tp_unpack(c, main_s)
 
-        def tp_pipelined(n):
-            io_s.wait_stream(main_s)
-            for c in range(len(ch)):
-                io_s.wait_event(e_ca[c])
-                tp_pack(c, io_s)
-                e_cp[c].record(io_s)
-            for i in range(n):
-                for c in range(len(ch)):
-                    main_s.wait_event(e_cp[c])
-                    main_s.wait_event(e_cu[c])
-                    tp_attn(c)
-                    e_ca[c].record(main_s)
+            def tp_pipelined(n):
+                io_s.wait_stream(main_s)
                 for c in range(len(ch)):
                     io_s.wait_event(e_ca[c])
-                    if i + 1 < n:
-                        tp_pack(c, io_s)
-                        e_cp[c].record(io_s)
-                    tp_unpack(c, io_s)
-                    e_cu[c].record(io_s)
-            main_s.wait_stream(io_s)
+                    tp_pack(c, io_s)
+                    e_cp[c].record(io_s)
+                for i in range(n):
+                    for c in range(len(ch)):
+                        main_s.wait_event(e_cp[c])
+                        main_s.wait_event(e_cu[c])
+                        tp_attn(c)
+                        e_ca[c].record(main_s)
+                    for c in range(len(ch)):
+                        io_s.wait_event(e_ca[c])
+                        if i + 1 < n:
+                            tp_pack(c, io_s)
+                            e_cp[c].record(io_s)
+                        tp_unpack(c, io_s)
+                        e_cu[c].record(io_s)
+                main_s.wait_stream(io_s)
 
-        for name, fn in (("two_phase_serial", tp_serial), ("two_phase", tp_pipelined)):
-            fn(args.warmup)
-            torch.cuda.synchronize()
-            a, b_ = ev(), ev()
-            a.record(main_s)
-            fn(args.steps)
-            b_.record(main_s)
-            torch.cuda.synchronize()
-            legs[name] = {"mean_ms": a.elapsed_time(b_) / args.steps, "steps": args.steps,
-                          "flop": attn_flops}
-            got = oshard.clone()
-            step()
-            torch.cuda.synchronize()
-            if not torch.equal(got, oshard):
-                raise RuntimeError(f"{name} steps differ from a single-shot step")
-        del ws_c
+            for name, fn in (("two_phase_serial", tp_serial), ("two_phase", tp_pipelined)):
+                fn(args.warmup)
+                torch.cuda.synchronize()
+                a, b_ = ev(), ev()
+                a.record(main_s)
+                fn(args.steps)
+                b_.record(main_s)
+                torch.cuda.synchronize()
+                legs[name] = {"mean_ms": a.elapsed_time(b_) / args.steps, "steps": args.steps,
+                              "flop": attn_flops}
+                got = oshard.clone()
+                step()
+                torch.cuda.synchronize()
+                if not torch.equal(got, oshard):
+                    raise RuntimeError(f"{name} steps differ from a single-shot step")
+            del ws_c
 
-        # the other workloads' whole worlds: pack q, k, v -> attention of every
-        # head group -> unpack, with each part timed
-        def world_leg(name, sets):
-            wl = synth.WORKLOADS[name]
-            tbw = usp.usp_balanced_ranges(wl.S, wl.P)
-            hbw = usp.usp_balanced_ranges(wl.H, wl.P)
-            del tbw
-            host = data[name]
-            sets_ = []
-            for si in range(sets):
-                qkv = [bf(x) for x in host]
-                bl = [blocks_of(wl.B, wl.S, hbw, wl.D) for _ in range(3)]
-                ob = blocks_of(wl.B, wl.S, hbw, wl.D)
-                out = torch.empty((wl.B, wl.S, wl.H, wl.D), dtype=torch.bfloat16, device=dev)
-                wsw = torch.empty(usp.usp_attention_workspace_bytes(
-                    usp.USP_BF16, wl.B, wl.S, max(hbw[j + 1] - hbw[j] for j in range(wl.P)), wl.D),
-                    dtype=torch.uint8, device=dev)
-                sets_.append((qkv, bl, ob, out, wsw))
-            flops = 4.0 * wl.B * wl.H * wl.S * wl.S * wl.D
-            tw = [Timer(torch) for _ in range(4)]
+        if on("worlds"):
+            # the other workloads' whole worlds: pack q, k, v -> attention of every
+            # head group -> unpack, with each part timed
+            def world_leg(name, sets):
+                wl = synth.WORKLOADS[name]
+                tbw = usp.usp_balanced_ranges(wl.S, wl.P)
+                hbw = usp.usp_balanced_ranges(wl.H, wl.P)
+                del tbw
+                host = data[name]
+                sets_ = []
+                for si in range(sets):
+                    qkv = [bf(x) for x in host]
+                    bl = [blocks_of(wl.B, wl.S, hbw, wl.D) for _ in range(3)]
+                    ob = blocks_of(wl.B, wl.S, hbw, wl.D)
+                    out = torch.empty((wl.B, wl.S, wl.H, wl.D), dtype=torch.bfloat16, device=dev)
+                    wsw = torch.empty(usp.usp_attention_workspace_bytes(
+                        usp.USP_BF16, wl.B, wl.S, max(hbw[j + 1] - hbw[j] for j in range(wl.P)), wl.D),
+                        dtype=torch.uint8, device=dev)
+                    sets_.append((qkv, bl, ob, out, wsw))
+                flops = 4.0 * wl.B * wl.H * wl.S * wl.S * wl.D
+                tw = [Timer(torch) for _ in range(4)]
 
-            def run(i):
-                qkv, bl, ob, out, wsw = sets_[i % sets]
-                tw[0](usp.usp_pack_seq_to_heads_planes, qkv, bl)
-                a_ = torch.cuda.Event(enable_timing=True)
-                a_.record()
-                for j in range(wl.P):
-                    usp.usp_attention_fwd_ws(bl[0][j], bl[1][j], bl[2][j], ob[j], wsw)
-                b2 = torch.cuda.Event(enable_timing=True)
-                b2.record()
-                tw[1].ev.append((a_, b2))
-                tw[2](usp.usp_unpack_heads_to_seq, ob, out)
+                def run(i):
+                    qkv, bl, ob, out, wsw = sets_[i % sets]
+                    tw[0](usp.usp_pack_seq_to_heads_planes, qkv, bl)
+                    a_ = torch.cuda.Event(enable_timing=True)
+                    a_.record()
+                    for j in range(wl.P):
+                        usp.usp_attention_fwd_ws(bl[0][j], bl[1][j], bl[2][j], ob[j], wsw)
+                    b2 = torch.cuda.Event(enable_timing=True)
+                    b2.record()
+                    tw[1].ev.append((a_, b2))
+                    tw[2](usp.usp_unpack_heads_to_seq, ob, out)
 
-            host = host_ms_per_call(torch, run, 3)
-            tw = [Timer(torch) for _ in range(4)]
-            n = max(6, reps)
-            queue_ahead(torch, 1.5 * host * n)
-            whole = Timer(torch)
-            for i in range(n):
-                whole(run, i)
-            pk, at, up, wh = tw[0].summary(), tw[1].summary(), tw[2].summary(), whole.summary()
-            res = {"B": wl.B, "S": wl.S, "H": wl.H, "D": wl.D, "P": wl.P, "flop": flops,
-                   "buffer_sets": sets, "pack_qkv": pk, "attention": at, "unpack": up, "step": wh,
-                   "attention_TFLOP/s": tflops(flops, at["median_ms"]),
-                   "attention_frac": tflops(flops, at["median_ms"]) / PEAK_BF16_TFLOPS,
-                   "step_TFLOP/s": tflops(flops, wh["median_ms"]),
-                   "pack_qkv_GB/s": gbs(3 * 2 * wl.B * wl.S * wl.H * wl.D * 2, pk["median_ms"]),
-                   "unpack_GB/s": gbs(2 * wl.B * wl.S * wl.H * wl.D * 2, up["median_ms"])}
-            del sets_
-            return res
+                host = host_ms_per_call(torch, run, 3)
+                tw = [Timer(torch) for _ in range(4)]
+                n = max(6, reps)
+                queue_ahead(torch, 1.5 * host * n)
+                whole = Timer(torch)
+                for i in range(n):
+                    whole(run, i)
+                pk, at, up, wh = tw[0].summary(), tw[1].summary(), tw[2].summary(), whole.summary()
+                res = {"B": wl.B, "S": wl.S, "H": wl.H, "D": wl.D, "P": wl.P, "flop": flops,
+                       "buffer_sets": sets, "pack_qkv": pk, "attention": at, "unpack": up, "step": wh,
+                       "attention_TFLOP/s": tflops(flops, at["median_ms"]),
+                       "attention_frac": tflops(flops, at["median_ms"]) / PEAK_BF16_TFLOPS,
+                       "step_TFLOP/s": tflops(flops, wh["median_ms"]),
+                       "pack_qkv_GB/s": gbs(3 * 2 * wl.B * wl.S * wl.H * wl.D * 2, pk["median_ms"]),
+                       "unpack_GB/s": gbs(2 * wl.B * wl.S * wl.H * wl.D * 2, up["median_ms"])}
+                del sets_
+                return res
 
-        say("ViT-L/16 world (warm, then cold)")
-        out_extra["vit_l16_world"] = {"warm": world_leg("vit_l16", 1), "cold": world_leg("vit_l16", 3)}
-        say("indivisible long world")
-        out_extra["indivisible_long_world"] = world_leg("indivisible_long", 1)
+            say("ViT-L/16 world (warm, then cold)")
+            out_extra["vit_l16_world"] = {"warm": world_leg("vit_l16", 1), "cold": world_leg("vit_l16", 3)}
+            say("indivisible long world")
+            out_extra["indivisible_long_world"] = world_leg("indivisible_long", 1)
 
     # plain device copy of 1 GiB: practical HBM reference and counter calibration
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -940,71 +1030,73 @@ def main():
     rel = {}
     rows_bw = {}
     if legs_on:
-        say("world relayout bandwidth")
-        nbytes = B * S * H * D * 2
-        sets = [[world[t]] + [torch.empty_like(world[t]).copy_(world[t]) for _ in range(2)]
-                for t in range(3)]   # per tensor, three rotating copies
-        dsts = [[blocks_of(B, S, hb, D) for _ in range(3)] for _ in range(3)]
-        cb = 2 * (nbytes * 2 // h0)   # heads [0, 2) of every group of 5, read + write
+        if on("relayout"):
+            say("world relayout bandwidth")
+            nbytes = B * S * H * D * 2
+            sets = [[world[t]] + [torch.empty_like(world[t]).copy_(world[t]) for _ in range(2)]
+                    for t in range(3)]   # per tensor, three rotating copies
+            dsts = [[blocks_of(B, S, hb, D) for _ in range(3)] for _ in range(3)]
+            cb = 2 * (nbytes * 2 // h0)   # heads [0, 2) of every group of 5, read + write
 
-        def rl(name, fn, moved):
-            r = timed(torch, fn, args.relayout_reps)
-            r.update({"GB/s": gbs(moved, r["median_ms"]), "GB/s_min_time": gbs(moved, r["min_ms"]),
-                      "frac_peak": gbs(moved, r["median_ms"]) / PEAK_HBM_GBS, "bytes_rw": moved})
-            rel[name] = r
+            def rl(name, fn, moved):
+                r = timed(torch, fn, args.relayout_reps)
+                r.update({"GB/s": gbs(moved, r["median_ms"]), "GB/s_min_time": gbs(moved, r["min_ms"]),
+                          "frac_peak": gbs(moved, r["median_ms"]) / PEAK_HBM_GBS, "bytes_rw": moved})
+                rel[name] = r
 
-        rl("pack", lambda i: usp.usp_pack_seq_to_heads(sets[0][i % 3], dsts[0][i % 3]), 2 * nbytes)
-        rl("unpack", lambda i: usp.usp_unpack_heads_to_seq(dsts[0][i % 3], sets[0][i % 3]), 2 * nbytes)
-        rl("pack_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
-            [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)]), 6 * nbytes)
-        rl("pack_chunk", lambda i: usp.usp_pack_seq_to_heads_chunk(sets[0][i % 3], dsts[0][i % 3], 0, 2),
-           cb)
-        rl("unpack_chunk", lambda i: usp.usp_unpack_heads_to_seq_chunk(dsts[0][i % 3], sets[0][i % 3],
-                                                                       0, 2), cb)
-        rl("pack_chunk_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
-            [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)], head_lo=0,
-            head_hi=2), 3 * cb)
-        # rank 0's share, as in the step (one call moves one shard per
-        # tensor): per call with events, and back to back; sources and
-        # destinations rotate over 9 sets (377 MB of blocks)
-        len0 = tb[1] - tb[0]
-        shares = [[torch.empty((B, len0, H, D), dtype=torch.bfloat16, device=dev).normal_()
-                   for _ in range(3)] for _ in range(3)]
-        sb = 2 * B * len0 * H * D * 2
-        share_legs = (
-            ("pack_qkv_rank0", lambda i: usp.usp_pack_seq_to_heads_planes(
-                [shares[t][i % 3] for t in range(3)], [dsts[t][(i + t) % 3] for t in range(3)], rank=0),
-             3 * sb),
-            ("unpack_rank0", lambda i: usp.usp_unpack_heads_to_seq(
-                dsts[i % 9 // 3][i % 3], shares[i % 9 // 3][i % 3], rank=0), sb))
-        for name, fn, moved in share_legs:
-            rl(name, fn, moved)
-            ms_b2b = back_to_back(torch, fn, args.relayout_reps)
-            rel[name].update({"back_to_back_ms": ms_b2b, "GB/s_back_to_back": gbs(moved, ms_b2b),
-                              "frac_peak_back_to_back": gbs(moved, ms_b2b) / PEAK_HBM_GBS})
-        del shares
-        for r in rel.values():
-            r["frac_of_copy"] = r["GB/s"] / copy_gbs
-        del sets, dsts
+            rl("pack", lambda i: usp.usp_pack_seq_to_heads(sets[0][i % 3], dsts[0][i % 3]), 2 * nbytes)
+            rl("unpack", lambda i: usp.usp_unpack_heads_to_seq(dsts[0][i % 3], sets[0][i % 3]), 2 * nbytes)
+            rl("pack_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
+                [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)]), 6 * nbytes)
+            rl("pack_chunk", lambda i: usp.usp_pack_seq_to_heads_chunk(sets[0][i % 3], dsts[0][i % 3], 0, 2),
+               cb)
+            rl("unpack_chunk", lambda i: usp.usp_unpack_heads_to_seq_chunk(dsts[0][i % 3], sets[0][i % 3],
+                                                                           0, 2), cb)
+            rl("pack_chunk_qkv", lambda i: usp.usp_pack_seq_to_heads_planes(
+                [sets[t][i % 3] for t in range(3)], [dsts[t][i % 3] for t in range(3)], head_lo=0,
+                head_hi=2), 3 * cb)
+            # rank 0's share, as in the step (one call moves one shard per
+            # tensor): per call with events, and back to back; sources and
+            # destinations rotate over 9 sets (377 MB of blocks)
+            len0 = tb[1] - tb[0]
+            shares = [[torch.empty((B, len0, H, D), dtype=torch.bfloat16, device=dev).normal_()
+                       for _ in range(3)] for _ in range(3)]
+            sb = 2 * B * len0 * H * D * 2
+            share_legs = (
+                ("pack_qkv_rank0", lambda i: usp.usp_pack_seq_to_heads_planes(
+                    [shares[t][i % 3] for t in range(3)], [dsts[t][(i + t) % 3] for t in range(3)], rank=0),
+                 3 * sb),
+                ("unpack_rank0", lambda i: usp.usp_unpack_heads_to_seq(
+                    dsts[i % 9 // 3][i % 3], shares[i % 9 // 3][i % 3], rank=0), sb))
+            for name, fn, moved in share_legs:
+                rl(name, fn, moved)
+                ms_b2b = back_to_back(torch, fn, args.relayout_reps)
+                rel[name].update({"back_to_back_ms": ms_b2b, "GB/s_back_to_back": gbs(moved, ms_b2b),
+                                  "frac_peak_back_to_back": gbs(moved, ms_b2b) / PEAK_HBM_GBS})
+            del shares
+            for r in rel.values():
+                r["frac_of_copy"] = r["GB/s"] / copy_gbs
+            del sets, dsts
 
-        say("model-boundary row movements")
-        W = H * D
-        nb = B * S * W * 2
-        fulls = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(3)]
-        shard_sets = [[torch.empty((B, tb[r + 1] - tb[r], W), dtype=torch.bfloat16, device=dev)
-                       for r in range(P)] for _ in range(3)]
-        partials = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(P)]
-        for name, fn, moved in (
-                ("scatter", lambda i: usp.usp_scatter_rows(fulls[i % 3], shard_sets[i % 3]), 2 * nb),
-                ("gather", lambda i: usp.usp_gather_rows(shard_sets[i % 3], fulls[i % 3]), 2 * nb),
-                ("reduce_scatter", lambda i: usp.usp_reduce_scatter_rows(partials, shard_sets[i % 3]),
-                 (P + 1) * nb)):
-            r = timed(torch, fn, args.relayout_reps)
-            r.update({"GB/s": gbs(moved, r["median_ms"]), "frac_peak": gbs(moved, r["median_ms"]) /
-                      PEAK_HBM_GBS, "bytes": moved})
-            rows_bw[name] = r
-        rows_bw["shape"] = {"B": B, "S": S, "W": W, "P": P, "dtype": "bf16"}
-        del fulls, shard_sets, partials
+        if on("rows"):
+            say("model-boundary row movements")
+            W = H * D
+            nb = B * S * W * 2
+            fulls = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(3)]
+            shard_sets = [[torch.empty((B, tb[r + 1] - tb[r], W), dtype=torch.bfloat16, device=dev)
+                           for r in range(P)] for _ in range(3)]
+            partials = [torch.randn((B, S, W), device=dev).to(torch.bfloat16) for _ in range(P)]
+            for name, fn, moved in (
+                    ("scatter", lambda i: usp.usp_scatter_rows(fulls[i % 3], shard_sets[i % 3]), 2 * nb),
+                    ("gather", lambda i: usp.usp_gather_rows(shard_sets[i % 3], fulls[i % 3]), 2 * nb),
+                    ("reduce_scatter", lambda i: usp.usp_reduce_scatter_rows(partials, shard_sets[i % 3]),
+                     (P + 1) * nb)):
+                r = timed(torch, fn, args.relayout_reps)
+                r.update({"GB/s": gbs(moved, r["median_ms"]), "frac_peak": gbs(moved, r["median_ms"]) /
+                          PEAK_HBM_GBS, "bytes": moved})
+                rows_bw[name] = r
+            rows_bw["shape"] = {"B": B, "S": S, "W": W, "P": P, "dtype": "bf16"}
+            del fulls, shard_sets, partials
 
     # compact per-leg figures (also kept inside the roofline object)
     summary = {"attn_video_dit_share": {"TFLOP/s": attn_tflops, "frac": attn_tflops / PEAK_BF16_TFLOPS,
