@@ -208,10 +208,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
 
   // ---- XCD-aware workgroup -> (batch, head, query tile, sub-tile[, part])
   const int u = xcd_remap(blockIdx.x, gridDim.x);
-  // key halves: the two halves of a tile are adjacent logical ids, so that
-  // the XCD-aware remap puts both on one XCD, where they share the tile's Q
-  const int part = PARTS == 2 ? (u & 1) : 0;
-  const int lid = PARTS == 2 ? (u >> 1) : u / SUB, sub = PARTS == 2 ? 0 : u % SUB;
+  // key halves: part-major ids, so that the workgroups an XCD runs at once
+  // walk the same key half of one head (one K/V stream per L2; with the two
+  // halves of a tile side by side the K/V bytes fetched per call rose from
+  // 420 to 713 MB)
+  const int part = PARTS == 2 ? u / p.n_tiles : 0;
+  const int lid = PARTS == 2 ? u % p.n_tiles : u / SUB, sub = PARTS == 2 ? 0 : u % SUB;
   const int qt = lid % p.n_qtiles;
   const int bh = lid / p.n_qtiles;
   const int head = p.head_lo + bh % p.nheads;
