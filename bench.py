@@ -435,6 +435,11 @@ def trace_summary(dirs, out_txt, warmup, steps):
     for (name, wgs), v in sorted(per_grid.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{name:56s} {wgs:10d} {len(v):6d} {np.mean(v):9.1f} {min(v):9.1f} {max(v):9.1f} "
                      f"{100 * sum(v) / total:6.2f}")
+    lines += ["", "durations in dispatch order (us), for the library's kernels with at most 64 dispatches "
+                  "of one launch shape:"]
+    for (name, wgs), v in sorted(per_grid.items(), key=lambda kv: -sum(kv[1])):
+        if len(v) <= 64 and ("attn" in name or "relayout" in name or "merge" in name):
+            lines.append(f"  {name} [{wgs} workgroups]: " + " ".join(f"{x:.1f}" for x in v))
     att = per.get(short_kernel_name("attn_bf16_kernel<128, 8, 1, 2, 64, true>"), [])
     mrg = per.get(short_kernel_name("attn_merge_halves<128, true>"), [])
     lines += ["", "key-half attn_bf16_kernel durations per call (us), in order: " +
@@ -444,6 +449,14 @@ def trace_summary(dirs, out_txt, warmup, steps):
         m = float(np.mean(mrg[warmup:warmup + steps]))
         lines.append(f"serial steps' timed calls ({steps} after {warmup} warmup): attn_bf16_kernel "
                      f"{a:.1f} us + attn_merge_halves {m:.1f} us = {a + m:.1f} us per call")
+        # the step's relayouts: rank 0's pack of q, k, v and unpack of o, one
+        # dispatch each per step, in the same order as the attention
+        share = [(k, v) for k, v in per_grid.items() if k[0] in ("relayout_kernel<pack>", "relayout_kernel<unpack>")
+                 and len(v) == len(att)]
+        for (name, wgs), v in sorted(share):
+            x = float(np.mean(v[warmup:warmup + steps]))
+            lines.append(f"serial steps' timed calls: {name} [{wgs} workgroups] {x:.1f} us "
+                         f"(minimum {min(v[warmup:warmup + steps]):.1f})")
     text = "\n".join(lines)
     print(text)
     if out_txt:
@@ -496,20 +509,34 @@ def queue_ahead(torch, host_ms):
 
 
 def host_ms_per_call(torch, fn, warm):
-    """Warm-up calls of ``fn(i)``; returns the host's enqueue time per call (ms)."""
+    """Warm-up calls of ``fn(i)``; returns the host's enqueue time and the
+    GPU's time per call (ms)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     t0 = time.perf_counter()
     for i in range(warm):
         fn(i)
     host = (time.perf_counter() - t0) * 1e3 / max(warm, 1)
+    b.record()
     torch.cuda.synchronize()
-    return host
+    return host, a.elapsed_time(b) / max(warm, 1)
+
+
+def spin_if_host_bound(torch, host, gpu, calls):
+    """Queue a spin ahead of ``calls`` timed calls when the host's enqueue
+    time per call is not well below the GPU's (short calls); long calls keep
+    the GPU busy by themselves and are timed without one (a spin idles all
+    but one CU, and the clock then starts the first timed call lower)."""
+    if host > 0.5 * gpu:
+        queue_ahead(torch, 1.5 * host * calls)
 
 
 def timed(torch, fn, reps, warm=3):
     """Median / minimum / mean of ``reps`` calls of ``fn(i)`` after ``warm``,
-    each between two HIP events, issued behind a GPU spin (queue_ahead)."""
-    host = host_ms_per_call(torch, fn, warm)
-    queue_ahead(torch, 1.5 * host * reps)
+    each between two HIP events; short calls are issued behind a GPU spin
+    (queue_ahead)."""
+    host, gpu = host_ms_per_call(torch, fn, warm)
+    spin_if_host_bound(torch, host, gpu, reps)
     t = Timer(torch)
     for i in range(reps):
         t(fn, i)
@@ -519,8 +546,8 @@ def timed(torch, fn, reps, warm=3):
 def back_to_back(torch, fn, reps, warm=3):
     """Mean per call of ``reps`` calls of ``fn(i)`` issued back to back
     between two HIP events (no event between calls) behind a GPU spin, in ms."""
-    host = host_ms_per_call(torch, fn, warm)
-    queue_ahead(torch, 1.5 * host * reps)
+    host, gpu = host_ms_per_call(torch, fn, warm)
+    spin_if_host_bound(torch, host, gpu, reps)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(reps):
@@ -997,10 +1024,10 @@ def main():
                     tw[1].ev.append((a_, b2))
                     tw[2](usp.usp_unpack_heads_to_seq, ob, out)
 
-                host = host_ms_per_call(torch, run, 3)
+                host, gpu = host_ms_per_call(torch, run, 3)
                 tw = [Timer(torch) for _ in range(4)]
                 n = max(6, reps)
-                queue_ahead(torch, 1.5 * host * n)
+                spin_if_host_bound(torch, host, gpu, n)
                 whole = Timer(torch)
                 for i in range(n):
                     whole(run, i)
