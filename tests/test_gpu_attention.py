@@ -140,10 +140,16 @@ def test_chunked_bitwise_equals_single_shot_small(h, chunks):
 # the masked last tile. Query rows run in tiles of 256 (the last one partial).
 EDGE_CASES = [  # B, S, h, D, what the case exercises
     (3, 64, 7, 128, "nkt = 1: the first half is empty, the second one whole tile"),
-    (2, 37, 3, 64, "nkt = 1 with a partial tile: 37 of 128 keys, one partial query tile"),
+    (2, 37, 3, 64, "short walk at D = 64: one partial 64-key tile (37 keys), one 128-row "
+                   "workgroup with rows and one without"),
     (1, 100, 5, 128, "nkt = 2: one tile per half, the second partial"),
     (1, 257, 6, 128, "nkt = 5 (odd): halves of 2 and 3 tiles, one key past a whole tile"),
-    (1, 513, 4, 64, "nkt = 5 at D = 64, partial last tile of 1 key, 3 query tiles"),
+    (1, 513, 4, 64, "short walk at D = 64: 9 tiles of 64 keys, the last of 1 key; the sixth "
+                    "128-row workgroup of each head holds 1 row"),
+    (1, 896, 2, 64, "D = 64 at the short-walk limit: 14 tiles of 64 keys (7 of 128), "
+                    "unguarded pairs of steps"),
+    (1, 897, 2, 64, "D = 64 just past it: 8 tiles of 128 keys split into halves of 4, "
+                    "a 1-key last tile"),
     (1, 1000, 2, 128, "nkt = 16: halves of 8 with unguarded pairs, guarded pairs and a single step"),
     (1, 4157, 3, 128, "nkt = 65: halves of 32 and 33, long unguarded runs, a 61-key last tile"),
 ]

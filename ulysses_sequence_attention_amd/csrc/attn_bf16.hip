@@ -177,9 +177,11 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t soff, uint32_t v
 }
 
 // KG key groups of NW / KG waves share a workgroup; PARTS = 2 makes each
-// workgroup walk one key half and leave its state in the workspace.
+// workgroup walk one key half and leave its state in the workspace. NW = 4
+// (short walks at D = 64: 128-row workgroups, 64-key tiles) asks for three
+// workgroups per CU, i.e. at most 168 VGPRs per lane.
 template <int D, int NW, int KG, int PARTS, int BN, bool kOutBf16>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void attn_bf16_kernel(Params p) {
   constexpr int QB = 1;                         // 32-row query blocks per wave
   constexpr int GW = NW / KG;                   // waves per key group
   static_assert(GW * KG == NW && KG <= 2, "one or two key groups of equal size");
@@ -699,8 +701,28 @@ size_t halves_ws_bytes(int64_t tiles, int D) {
   return size_t(tiles) * 2 * kTileRows * (size_t(D) + 3) * sizeof(float);
 }
 
+// Short walks at D = 64: fewer than USP_SPLIT_MIN key tiles of BN, walked in
+// 64-key tiles by 4-wave workgroups of 128 rows, three per CU (164 VGPRs),
+// instead of 8-wave workgroups of 256 rows, one per CU. A short walk is
+// mostly the fixed cost of its workgroup; the smaller workgroups pad a
+// ragged last query tile less and fill the CUs in fewer rounds (ViT-L/16,
+// S = 577: 768 row-slots of 128 in one round against 384 of 256 in one and
+// a half; 378 against 307 TF/s). Measured: no gain at longer walks, and
+// 64-key tiles in 8-wave workgroups lose 13% at S = 65537.
+constexpr int kShortBN = 64;
+bool short_walk(int64_t Sk, int D, int BN) {
+  return D == 64 && (Sk + BN - 1) / BN < USP_SPLIT_MIN;
+}
+
 template <int D, int BN, bool kOutBf16>
 int launch_tiles(Params& p, int64_t tiles, void* ws, hipStream_t s) {
+  if constexpr (D == 64) {
+    if (short_walk(p.Sk, D, BN)) {
+      // two 128-row workgroups per 256-row tile; no state to merge
+      attn_bf16_kernel<D, 4, 1, 1, kShortBN, kOutBf16><<<unsigned(tiles * 2), 256, 0, s>>>(p);
+      return check_launch("attn_bf16_kernel (short walks)");
+    }
+  }
   if (!split_keys(p.Sk, BN)) {
     // whole key walks in 256-row workgroups: no state to merge, no workspace
     attn_bf16_kernel<D, 8, 1, 1, BN, kOutBf16><<<unsigned(tiles), 512, 0, s>>>(p);
