@@ -45,15 +45,19 @@
 // (v_dot2c_f32_bf16 against (1, 1)), so the rounding of a dominant weight
 // cancels between numerator and denominator.
 //
-// Key halves. Every row's key range is split once, at key tile
-// floor(nkt / 2) (nkt = ceil(Sk / BN)), into two walks whose softmax states
-// (reference maximum m, row sum l, unnormalised O) are merged at the end
-// with weights 2^(c (m_i - M)), M the larger maximum. The split point
-// depends on Sk and D only, so a row's bits never depend on the launch (its
-// head range, batch, the query block it sits in or the device); splitting the work this way gives 2x
-// as many work units, which keeps the last round of a launch from running
-// half empty (a workgroup fills a CU, and at S = 32760, 128 tiles of 256
-// rows per head, a head is exactly one round of 256 half-walks). Two forms:
+// Key halves. For walks of 8 to 1024 key tiles (nkt = ceil(Sk / BN)) every
+// row's key range is split once, at key tile floor(nkt / 2), into two walks
+// whose softmax states (reference maximum m, row sum l, unnormalised O) are
+// merged at the end with weights 2^(c (m_i - M)), M the larger maximum.
+// Whether and where a walk splits depends on Sk and D only, so a row's bits
+// never depend on the launch (its head range, batch, the query block it sits
+// in or the device). Splitting gives 2x as many work units, which keeps the
+// last round of a launch from running half empty (a workgroup fills a CU,
+// and at S = 32760, 128 tiles of 256 rows per head, a head is exactly one
+// round of 256 half-walks); an even split, since the longer half sets every
+// CU's finish time. Shorter and longer walks run whole (at D = 64 a short
+// walk runs in 4-wave workgroups of 128 rows with 64-key tiles, three per
+// CU). Two forms of the split:
 //   * key groups (usp_attention_fwd): a workgroup of 8 waves is two groups
 //     of 4 waves that walk the two halves for the same 128 rows, each with
 //     its own K/V buffers, and merge through LDS;
