@@ -301,6 +301,19 @@ def pmc_summary(dirs, out_json):
     print("\n".join(lines))
 
 
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def oracle_parts(data, target_s):
     """Time the oracle (float64 NumPy) on the workloads of this benchmark, per
     configuration and part, on every host core this process may use (the
@@ -384,6 +397,7 @@ def oracle_parts(data, target_s):
          {(0, hd): np.arange(q.shape[1]) for hd in range(q.shape[2])}, note="every row")
     s = parts["attention_video_dit_share"]
     return {"value": value / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": host_cpu_model(),
             "sample": f"{s['rows']} of {s['of_rows']} rows (5 heads) of the S=32760 D=128 share, "
                       f"{s['wall_s']:.1f} s, fp64 NumPy, {cores} procs",
             "parts": parts}
