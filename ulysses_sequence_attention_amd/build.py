@@ -3,7 +3,10 @@
 Usage: ``python -m ulysses_sequence_attention_amd.build [--verbose]``.
 Compiles every ``csrc/*.hip`` with hipcc for gfx950 into ``_build/`` at the
 repository root and links ``ulysses_sequence_attention_amd/libusp.so``.
-Always recompiles, also when a built library is already present.
+Always recompiles, also when a built library is already present. Also
+builds the plain C consumers of the ABI under ``tests/c_abi``: one that runs
+on the GPU, and a host-only one linked against a copy of the library whose
+host code carries the AddressSanitizer (``_build/asan``).
 """
 from __future__ import annotations
 
@@ -60,6 +63,44 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+# Host AddressSanitizer build: the library's host code instrumented (the
+# device code is not: every -fsanitize= sits behind -Xarch_host), linked into
+# the plain C host check of tests/c_abi, which needs no GPU.
+ASAN_BUILD = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_BUILD, "libusp_asan.so")
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "usp_host_check.c")
+HOST_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "usp_host_check")
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """Compile libusp with the host AddressSanitizer into _build/asan and the
+    host-only C check against it (tests/c_abi/usp_host_check)."""
+    os.makedirs(ASAN_BUILD, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    flags = FLAGS + ASAN_FLAGS
+    objs = []
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        jobs = []
+        for src in sources:
+            obj = os.path.join(ASAN_BUILD, os.path.basename(src)[:-4] + ".o")
+            objs.append(obj)
+            jobs.append(ex.submit(_run, [HIPCC, *flags, "-c", src, "-o", obj], verbose))
+        for j in jobs:
+            j.result()
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_FLAGS, "-o", ASAN_LIB, *objs],
+         verbose)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    tmp = HOST_CHECK_BIN + ".tmp"
+    _run([clang, "-std=c11", "-O1", "-g", "-Wall", *ASAN_FLAGS, "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROOT, "include"), HOST_CHECK_SRC, "-o", tmp,
+          "-L", ASAN_BUILD, "-lusp_asan", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../../_build/asan", "-Wl,-rpath," + os.path.join(rocm, "lib")], verbose)
+    os.replace(tmp, HOST_CHECK_BIN)
+    return HOST_CHECK_BIN
+
+
 C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "usp_abi_check.c")
 C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "usp_abi_check")
 
@@ -82,3 +123,4 @@ if __name__ == "__main__":
     extra = [a for a in sys.argv[1:] if a != "--verbose"]
     print(build(verbose="--verbose" in sys.argv, extra_flags=extra))
     print(build_c_check(verbose="--verbose" in sys.argv))
+    print(build_host_check(verbose="--verbose" in sys.argv))
