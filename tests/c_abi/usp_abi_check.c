@@ -109,6 +109,76 @@ static void check_relayout(void) {
   free(back);
 }
 
+/* Two tensors of one shape in one launch (the q, k, v form): the blocks the
+ * planes call writes equal those of one single-tensor call per tensor, and
+ * its unpack of rank 1's rows rebuilds rank 1's shards of both tensors. */
+static void check_relayout_planes(void) {
+  enum { T = 2, P = 3 };
+  const int64_t B = 1, S = 257;
+  const int32_t H = 6, D = 128;
+  const size_t n = (size_t)B * S * H * D;
+  int64_t hb[P + 1], tb[P + 1];
+  CHECK(usp_balanced_ranges(H, P, hb) == USP_OK && usp_balanced_ranges(S, P, tb) == USP_OK,
+        "plane ranges");
+  uint16_t* host = (uint16_t*)malloc(n * 2 * T);
+  fill_bf16(host, n, 11);
+  fill_bf16(host + n, n, 12);
+  void* seq[T];
+  void* blk[T * P];
+  void* ref[P];
+  size_t bn[P];
+  for (int t = 0; t < T; ++t) {
+    seq[t] = dev_alloc(n * 2);
+    HIP_OK(hipMemcpy(seq[t], host + t * n, n * 2, hipMemcpyHostToDevice));
+  }
+  for (int j = 0; j < P; ++j) {
+    bn[j] = (size_t)B * S * (hb[j + 1] - hb[j]) * D;
+    ref[j] = dev_alloc(bn[j] * 2);
+    for (int t = 0; t < T; ++t) blk[t * P + j] = dev_alloc(bn[j] * 2);
+  }
+  CHECK(usp_pack_seq_to_heads_planes(T, (const void* const*)seq, blk, USP_BF16, B, S, H, D, P, -1, 0,
+                                     0, NULL) == USP_OK,
+        "planes pack");
+  uint16_t* a = (uint16_t*)malloc(n * 2);
+  uint16_t* r = (uint16_t*)malloc(n * 2);
+  for (int t = 0; t < T; ++t) {
+    CHECK(usp_pack_seq_to_heads(seq[t], ref, USP_BF16, B, S, H, D, P, -1, NULL) == USP_OK,
+          "single-tensor pack");
+    HIP_OK(hipDeviceSynchronize());
+    for (int j = 0; j < P; ++j) {
+      HIP_OK(hipMemcpy(a, blk[t * P + j], bn[j] * 2, hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(r, ref[j], bn[j] * 2, hipMemcpyDeviceToHost));
+      CHECK(memcmp(a, r, bn[j] * 2) == 0, "planes pack equals the single-tensor pack (tensor %d, block %d)",
+            t, j);
+    }
+  }
+  const int64_t len1 = tb[2] - tb[1];
+  const size_t ns = (size_t)B * len1 * H * D;
+  void* sh[T];
+  for (int t = 0; t < T; ++t) {
+    sh[t] = dev_alloc(ns * 2);
+    HIP_OK(hipMemset(sh[t], 0xff, ns * 2));
+  }
+  CHECK(usp_unpack_heads_to_seq_planes(T, (const void* const*)blk, sh, USP_BF16, B, S, H, D, P, 1, 0, 0,
+                                       NULL) == USP_OK,
+        "planes unpack of rank 1's rows");
+  HIP_OK(hipDeviceSynchronize());
+  for (int t = 0; t < T; ++t) {
+    HIP_OK(hipMemcpy(a, sh[t], ns * 2, hipMemcpyDeviceToHost));
+    CHECK(memcmp(a, host + t * n + (size_t)tb[1] * H * D, ns * 2) == 0,
+          "rank 1's shard of tensor %d bit for bit", t);
+    HIP_OK(hipFree(sh[t]));
+    HIP_OK(hipFree(seq[t]));
+  }
+  for (int j = 0; j < P; ++j) {
+    HIP_OK(hipFree(ref[j]));
+    for (int t = 0; t < T; ++t) HIP_OK(hipFree(blk[t * P + j]));
+  }
+  free(host);
+  free(a);
+  free(r);
+}
+
 /* The two-phase exchange: pack and unpack one head chunk at a time (equal
  * head groups of 3 heads, plan 2/1) rebuild the tensor bit for bit, and each
  * pack phase leaves the other heads of a block as they were. */
@@ -368,6 +438,7 @@ int main(void) {
   check_ranges();
   check_device_ranges();
   check_relayout();
+  check_relayout_planes();
   check_relayout_chunks();
   check_rows();
   check_attention();

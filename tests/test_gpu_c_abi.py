@@ -1,7 +1,8 @@
 """The C ABI from a plain C program (tests/c_abi/usp_abi_check.c, built by
 __graft_entry__.build()): libusp with the HIP runtime and no PyTorch in the
 process. The program checks range splits, the relayout round trip bit for
-bit, the agreement of the attention entry points bit for bit and error
+bit (single tensors and several in one launch), the agreement of the
+attention entry points bit for bit and error
 codes; its exit status is the verdict."""
 import os
 import subprocess
