@@ -19,10 +19,14 @@
  * Conventions shared by every call:
  *   - All tensors are dense row-major, element type USP_F32 (4 bytes) or
  *     USP_BF16 (2 bytes, bfloat16). Device pointers must be 16-byte aligned.
- *   - The caller owns every buffer. The library never allocates, frees or
- *     synchronizes; device work is enqueued on the caller's stream
- *     (a hipStream_t passed as void*; NULL = the default stream) and the call
- *     returns without waiting for it.
+ *   - The caller owns every buffer it passes. The library never
+ *     synchronizes; device work is enqueued on the caller's stream (a
+ *     hipStream_t passed as void*; NULL = the default stream) and the call
+ *     returns without waiting for it. The only device memory the library
+ *     takes itself: an attention call given no workspace takes one, where
+ *     its shape needs one, from a stream-ordered pool the library keeps per
+ *     device (allocated and returned on the caller's stream; never during
+ *     graph capture), and usp_attention_fwd_noalloc's static scratch array.
  *   - Every call returns USP_OK (0) or a negative status. On error nothing is
  *     launched and no output is written; usp_last_error() gives a message.
  *   - Sizes are validated against overflow; a launch failure reported by the
@@ -242,9 +246,17 @@ int usp_reduce_scatter_rows(const void* const* partials, void* const* out, usp_d
  * Scores, softmax and accumulation are fp32. The result for a head depends
  * only on that head's inputs, never on [head_lo, head_hi), B or the device:
  * a head computed in any sub-range is bitwise equal to the same head computed
- * single-shot. Nothing is allocated: with bf16 inputs one kernel runs, in
- * which two groups of waves walk the two key halves (split at a point set by
- * S and D only) of 128 query rows and merge their softmax states in LDS.
+ * single-shot. With bf16 inputs and keys that split in halves (walks of 8 to
+ * 1024 key tiles, a rule of S and D only), the call takes the workspace of
+ * usp_attention_fwd_ws from a stream-ordered memory pool the library keeps
+ * per device (hipMallocFromPoolAsync before the kernels, hipFreeAsync after
+ * them, on `stream`; the pool keeps the memory for later calls) and runs the
+ * same kernels, with the same bits. While `stream` is being captured into a
+ * graph, when the pool cannot serve, or with the environment variable
+ * USP_ATTENTION_POOL=0 (read at every call), it allocates nothing and runs a
+ * kernel in which two groups of waves walk the two key halves of 128 query
+ * rows and merge their softmax states in LDS: the same bits again. Shapes
+ * whose keys do not split need no workspace at all.
  * Errors: h < 1, head range empty or outside [0, h) -> USP_EINVAL;
  *   B < 1, S < 1 or sizes overflowing -> USP_ESHAPE; unsupported
  *   in_dt/out_dt pair -> USP_EDTYPE; unsupported D -> USP_ENOSYS; misaligned
@@ -271,8 +283,9 @@ int usp_attention_workspace_bytes(usp_dtype in_dt, int64_t B, int64_t S, int32_t
  * each tile of 256 query rows is computed by two workgroups, one per key
  * half, that leave their unnormalised softmax state in `ws`; a second
  * kernel merges the halves exactly as usp_attention_fwd's workgroups merge
- * them in LDS. This keeps one K/V stream per workgroup (the key-group kernel
- * of usp_attention_fwd streams two per 128 rows) and is the faster path.
+ * them in LDS. This keeps one K/V stream per workgroup (the key-group kernel,
+ * which usp_attention_fwd runs when it cannot take a workspace, streams two
+ * per 128 rows) and is the faster path.
  *   ws, ws_bytes: device buffer, 16-byte aligned, of at least
  *                 usp_attention_workspace_bytes(in_dt, B, S, head_hi -
  *                 head_lo, D) bytes, owned by the caller; its contents on
@@ -325,9 +338,10 @@ int usp_attention_fwd_noalloc(const void* q, const void* k, const void* v, void*
  * h_kv = h is usp_attention_fwd. The result of a query head depends only on
  * its inputs (bitwise, as for usp_attention_fwd), so a caller may run head
  * chunks over any query-head ranges.
- *   ws, ws_bytes: NULL for the no-workspace kernels, or a workspace as for
+ *   ws, ws_bytes: NULL (the call then takes a workspace from the pool, as
+ *                 usp_attention_fwd does), or a workspace as for
  *                 usp_attention_fwd_ws (sized by usp_attention_workspace_bytes
- *                 for head_hi - head_lo heads); both give the same bits.
+ *                 for head_hi - head_lo heads); all give the same bits.
  * Errors as usp_attention_fwd_ws, plus: h_kv < 1, h_kv > h or h not a
  * multiple of h_kv -> USP_EINVAL.
  */
@@ -348,9 +362,10 @@ int usp_attention_fwd_gqa(const void* q, const void* k, const void* v, void* o, 
  *   q, o: device [B][Sq][h][D];  k, v: device [B][Sk][h_kv][D].
  *   lse:  NULL, or device fp32 [B][h][Sq] receiving the natural-log
  *         normaliser over this block's Sk keys (what the merge needs).
- *   ws, ws_bytes: NULL, or a workspace as for usp_attention_fwd_ws sized by
+ *   ws, ws_bytes: NULL (a workspace from the pool, as usp_attention_fwd),
+ *         or a workspace as for usp_attention_fwd_ws sized by
  *         usp_attention_workspace_bytes(in_dt, B, Sq, head_hi - head_lo, D)
- *         (it depends on the query rows only); both give the same bits.
+ *         (it depends on the query rows only); all give the same bits.
  * Sq = Sk with the same tensors is usp_attention_fwd_gqa, bit for bit, and a
  * query row's result depends only on its own row and the key block: running
  * a query block as any split of its rows gives the same bits.

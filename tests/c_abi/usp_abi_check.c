@@ -11,6 +11,7 @@
  * itself, finite outputs, and error codes with their messages. Exit status 0
  * when every check holds.
  */
+#define _DEFAULT_SOURCE /* setenv, unsetenv */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
@@ -283,6 +284,15 @@ static void check_attention(void) {
   HIP_OK(hipDeviceSynchronize());
   HIP_OK(hipMemcpy(b, chunked_ws_out, n * 4, hipMemcpyDeviceToHost));
   CHECK(memcmp(a, b, n * 4) == 0, "attention without allocation equals the default bit for bit");
+  /* with the library's workspace pool switched off, the default call runs the
+   * key-group kernel (700 keys split in halves at D = 128): the same bits */
+  setenv("USP_ATTENTION_POOL", "0", 1);
+  CHECK(usp_attention_fwd(qkv[0], qkv[1], qkv[2], chunked_ws_out, USP_BF16, USP_F32, B, S, h, D, 0, h,
+                          0.0f, NULL, NULL) == USP_OK, "usp_attention_fwd without the pool");
+  unsetenv("USP_ATTENTION_POOL");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(b, chunked_ws_out, n * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(a, b, n * 4) == 0, "the key-group kernel equals the default bit for bit");
   CHECK(usp_attention_fwd_noalloc(qkv[0], qkv[1], qkv[2], chunked_ws_out, USP_BF16, USP_F32, 2, 16384,
                                   8, D, 0, 8, 0.0f, NULL, NULL) == USP_EINVAL &&
             strstr(usp_last_error(), "scratch") != NULL,

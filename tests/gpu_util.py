@@ -9,6 +9,26 @@ from ulysses_sequence_attention_amd import synth
 DEV = "cuda:0"
 
 
+class no_pool:
+    """Within the block, attention calls given no workspace run the key-group
+    kernel instead of taking a workspace from the library's pool (the
+    library reads USP_ATTENTION_POOL at every call)."""
+
+    def __enter__(self):
+        import os
+        self._old = os.environ.get("USP_ATTENTION_POOL")
+        os.environ["USP_ATTENTION_POOL"] = "0"
+        return self
+
+    def __exit__(self, *exc):
+        import os
+        if self._old is None:
+            os.environ.pop("USP_ATTENTION_POOL", None)
+        else:
+            os.environ["USP_ATTENTION_POOL"] = self._old
+        return False
+
+
 def log(msg):
     """Name the case before each GPU step so a failing run says what it ran."""
     print(f"[gpu] {msg}", flush=True)

@@ -14,7 +14,7 @@ from oracle import relayout as X
 from ulysses_sequence_attention_amd import synth
 
 from gpu_util import (BF16_LSE_ABS, BF16_MAX_ABS, BF16_REL_FROB, DEV, F32_MAX_ABS, F32_REL_FROB, bf16_ulp, err,
-                      log, poisoned, to_dev, to_host, widen)
+                      log, no_pool, poisoned, to_dev, to_host, widen)
 
 pytestmark = pytest.mark.gpu
 BF, F = synth.BF16, synth.F32
@@ -162,6 +162,9 @@ def test_key_walk_edge_cases(B, S, h, D, plan):
     ref, ref_lse = A.attention(qf, kf, vf, return_lse=True)
     log(f"attention edge case B={B} S={S} h={h} D={D}: {plan}")
     out, lse = _run(q, k, v, BF, F, want_lse=True)
+    with no_pool():  # the key-group kernel where the keys split: the same bits
+        out_kg, lse_kg = _run(q, k, v, BF, F, want_lse=True)
+    assert out.tobytes() == out_kg.tobytes() and lse.tobytes() == lse_kg.tobytes()
     ma, rf = err(out, ref)
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
     assert np.max(np.abs(lse - ref_lse)) <= BF16_LSE_ABS
@@ -181,6 +184,10 @@ def test_rows_bitwise_independent_of_launch(D):
     parts = np.concatenate([_run(q, k, v, BF, F, lo=lo, hi=lo + 10)[:, :, lo:lo + 10]
                             for lo in range(0, 40, 10)], axis=2)
     assert one.tobytes() == parts.tobytes()
+    with no_pool():  # the key-group kernel: the same bits in either spread
+        parts = np.concatenate([_run(q, k, v, BF, F, lo=lo, hi=lo + 10)[:, :, lo:lo + 10]
+                                for lo in range(0, 40, 10)], axis=2)
+        assert one.tobytes() == parts.tobytes() == _run(q, k, v, BF, F).tobytes()
     sub = slice(0, 40, 13)
     ref = A.attention(*(widen(x[:, :, sub], BF) for x in (q, k, v)))
     ma, rf = err(one[:, :, sub], ref)
@@ -207,6 +214,9 @@ def test_exact_tile_multiples(B, S, h, D):
     assert np.max(np.abs(lse - ref_lse)) <= BF16_LSE_ABS
     out_ws, lse_ws = _run_ws(q, k, v, BF, F, want_lse=True)
     assert out.tobytes() == out_ws.tobytes() and lse.tobytes() == lse_ws.tobytes()
+    with no_pool():
+        out_kg, lse_kg = _run(q, k, v, BF, F, want_lse=True)
+    assert out.tobytes() == out_kg.tobytes() and lse.tobytes() == lse_kg.tobytes()
 
 
 WS_CASES = [  # B, S, h, D: one key tile (empty first half), odd key-tile counts, both D
@@ -222,12 +232,16 @@ def test_workspace_path_bitwise_equals_default(B, S, h, D):
     for out_dtype in (F, BF):
         a, la = _run(q, k, v, BF, out_dtype, want_lse=True)
         b, lb = _run_ws(q, k, v, BF, out_dtype, want_lse=True)
-        assert a.tobytes() == b.tobytes()
-        assert la.tobytes() == lb.tobytes()
+        with no_pool():  # the key-group kernel, where the keys split
+            c, lc = _run(q, k, v, BF, out_dtype, want_lse=True)
+        assert a.tobytes() == b.tobytes() == c.tobytes()
+        assert la.tobytes() == lb.tobytes() == lc.tobytes()
     if h > 1:
         a = _run(q, k, v, BF, F, lo=1, hi=h)
         b = _run_ws(q, k, v, BF, F, lo=1, hi=h)
-        assert a.tobytes() == b.tobytes()
+        with no_pool():
+            c = _run(q, k, v, BF, F, lo=1, hi=h)
+        assert a.tobytes() == b.tobytes() == c.tobytes()
         assert np.all(np.isnan(b[:, :, 0]))
     ref = A.attention(*(widen(x, BF) for x in (q, k, v)))
     ma, rf = err(_run_ws(q, k, v, BF, F), ref)
@@ -273,8 +287,11 @@ def test_gqa_parity_and_bitwise_forms(B, S, h, hkv, D):
     ma, rf = err(out, ref)
     assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
     assert np.max(np.abs(lse - ref_lse)) <= BF16_LSE_ABS
-    # the workspace form, and query-head ranges cutting through a group
+    # the workspace form, the key-group kernel, and query-head ranges cutting
+    # through a group
     assert _run_gqa(q, k, v, BF, F, use_ws=True).tobytes() == out.tobytes()
+    with no_pool():
+        assert _run_gqa(q, k, v, BF, F).tobytes() == out.tobytes()
     cut = max(1, h // 2 + (1 if h > 2 else 0))
     parts = np.concatenate([_run_gqa(q, k, v, BF, F, lo=0, hi=cut)[:, :, :cut],
                             _run_gqa(q, k, v, BF, F, lo=cut, hi=h)[:, :, cut:]], axis=2)
@@ -510,15 +527,16 @@ def test_gqa_video_share_full_size():
 
 
 def test_very_long_sequence_sampled():
-    """S = 1048583 (16384 key tiles and a ragged tail, one head, D = 128):
-    the key-half and key-group kernels agree bit for bit, and sampled rows
-    (the ends and rows around 256-row tile and key-half boundaries) match the
-    oracle over all keys."""
+    """S = 1048583 (16385 key tiles with a ragged tail, one head, D = 128;
+    past the split range, so every entry point walks each row's keys whole):
+    the default and workspace entry points agree bit for bit, and sampled
+    rows (the ends and rows around 256-row tiles and the middle key tile)
+    match the oracle over all keys."""
     B, S, h, D = 1, 1_048_583, 1, 128
     q, k, v = synth.draw_qkv(B, S, h, D, seed=91)
-    log(f"attention very long sequence S={S} (key groups)")
+    log(f"attention very long sequence S={S} (default)")
     out, lse = _run(q, k, v, BF, F, want_lse=True)
-    log(f"attention very long sequence S={S} (key halves, workspace)")
+    log(f"attention very long sequence S={S} (workspace)")
     out_ws, lse_ws = _run_ws(q, k, v, BF, F, want_lse=True)
     assert out.tobytes() == out_ws.tobytes() and lse.tobytes() == lse_ws.tobytes()
     assert not np.any(np.isnan(out))
@@ -536,9 +554,9 @@ def test_slab_beyond_2gib(S, h, D, what):
     """A (batch, K/V head) slab of S * h * D * 2 >= 2^31 bytes: the K/V
     loads then rebuild their buffer resource at every tile instead of
     offsetting one resource. Only the last head is computed (the other heads
-    hold zeros and must stay untouched in the output); the workspace and
-    default entry points agree bit for bit, and sampled rows match the
-    oracle."""
+    hold zeros and must stay untouched in the output); the workspace form,
+    the default call and the key-group kernel agree bit for bit, and sampled
+    rows match the oracle."""
     import torch
     assert S * h * D * 2 >= 2 ** 31 - 1
     hd = h - 1
@@ -549,22 +567,27 @@ def test_slab_beyond_2gib(S, h, D, what):
         t[:, :, hd:hd + 1] = to_dev(x, BF)
         dev[name] = t
     outs = []
-    for use_ws in (True, False):
-        log(f"attention slab beyond 2 GiB ({what}): S={S} h={h} D={D} head {hd} ws={use_ws}")
+    for form in ("workspace", "default", "no pool"):
+        log(f"attention slab beyond 2 GiB ({what}): S={S} h={h} D={D} head {hd} {form}")
         o = poisoned((1, S, h, D), F)
         lse = torch.full((1, h, S), float("nan"), device=DEV)
-        if use_ws:
+        if form == "workspace":
             nb = usp.usp_attention_workspace_bytes(usp.USP_BF16, 1, S, 1, D)
             ws = torch.full((nb // 4,), float("nan"), device=DEV)
             usp.usp_attention_fwd_ws(dev["q"], dev["k"], dev["v"], o, ws, head_lo=hd, head_hi=h, lse=lse)
-        else:
+            del ws
+        elif form == "default":
             usp.usp_attention_fwd(dev["q"], dev["k"], dev["v"], o, head_lo=hd, head_hi=h, lse=lse)
+        else:
+            with no_pool():  # the key-group kernel where the keys split
+                usp.usp_attention_fwd(dev["q"], dev["k"], dev["v"], o, head_lo=hd, head_hi=h, lse=lse)
         torch.cuda.synchronize()
         assert bool(torch.isnan(o[:, :, :hd]).all()) and bool(torch.isnan(lse[:, :hd]).all())
         outs.append((to_host(o[:, :, hd:h]), lse[:, hd:h].cpu().numpy()))
         del o, lse
-    (out, lse), (out2, lse2) = outs
-    assert out.tobytes() == out2.tobytes() and lse.tobytes() == lse2.tobytes()
+    (out, lse) = outs[0]
+    for out2, lse2 in outs[1:]:
+        assert out.tobytes() == out2.tobytes() and lse.tobytes() == lse2.tobytes()
     assert not np.any(np.isnan(out))
     rows = {(0, 0): np.unique(np.concatenate([_sample_rows(S, 24, 98), [0, S - 1]]))}
     _check_sampled(out, q1, k1, v1, BF, 1, S, rows, lse=lse)

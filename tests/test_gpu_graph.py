@@ -1,6 +1,6 @@
-"""The hot path under HIP graph capture. The library never allocates or
-synchronizes and takes a caller workspace, so a whole step — pack of Q, K,
-V, attention of every head group, unpack — can be captured once and
+"""The hot path under HIP graph capture. Given a caller workspace the library
+neither allocates nor synchronizes, so a whole step — pack of Q, K, V,
+attention of every head group, unpack — can be captured once and
 replayed. Each replay follows new inputs copied into the captured buffers
 and eager work on the device, and is compared bit for bit with the same step
 run eagerly."""

@@ -12,9 +12,10 @@ One rank's share of the work behind a small C ABI (``include/usp.h``,
   * ``usp_scatter_rows`` / ``usp_gather_rows`` / ``usp_reduce_scatter_rows``
     — ragged token rows at the model boundary;
   * ``usp_attention_fwd`` / ``usp_attention_fwd_chunked`` (``_ws``) — flash-style
-    non-causal attention over the full sequence for a head group;
-    ``usp_attention_fwd_ws`` the same with a caller workspace (faster, same
-    bits), sized by ``usp_attention_workspace_bytes``;
+    non-causal attention over the full sequence for a head group (a
+    workspace, where needed, from the library's stream-ordered pool);
+    ``usp_attention_fwd_ws`` the same with a caller workspace (same kernels,
+    same bits), sized by ``usp_attention_workspace_bytes``;
     ``usp_attention_fwd_noalloc`` the same with the library's static scratch
     (for callers that cannot allocate); ``usp_attention_fwd_gqa`` with
     grouped key/value heads;

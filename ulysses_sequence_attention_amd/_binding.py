@@ -396,7 +396,9 @@ def usp_reduce_scatter_rows(partials, out, rank: int = -1, stream=None) -> None:
 
 def usp_attention_fwd(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
                       lse=None, stream=None) -> None:
-    """Attention over heads [head_lo, head_hi) of q, k, v, o [B,S,h,D]."""
+    """Attention over heads [head_lo, head_hi) of q, k, v, o [B,S,h,D]; a
+    workspace, where the shape needs one, comes from the library's
+    stream-ordered pool (USP_ATTENTION_POOL=0 in the environment: none)."""
     _attn_io(q, k, v, o, lse)
     B, S, h, D = q.shape
     hi = h if head_hi is None else head_hi

@@ -781,6 +781,17 @@ int launch(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool attention_bf16_splits(int64_t Sk, int32_t D) {
+  switch (D) {
+    case 128:
+      return split_keys(Sk, USP_D128_BN);
+    case 64:
+      return split_keys(Sk, USP_D64_BN);
+    default:
+      return false;
+  }
+}
+
 size_t attention_bf16_ws_bytes(int64_t B, int64_t S, int32_t heads, int32_t D) {
   return halves_ws_bytes((S + kTileRows - 1) / kTileRows * heads * B, D);
 }

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 #include <string>
@@ -164,8 +166,73 @@ static int check_attention(const AttnArgs& a) {
   return USP_OK;
 }
 
+// ---- the workspace pool of the calls given no workspace --------------------
+// A bf16 call whose keys split in halves and that brings no workspace takes
+// one from a stream-ordered memory pool the library keeps per device (the
+// key-half kernels and their merge, then hipFreeAsync on the same stream), so
+// it runs the same kernels as the workspace form, with the same bits. The pool
+// keeps freed memory for the next call (release threshold at its maximum):
+// after the first calls an allocation is a pool lookup. Where the pool cannot
+// be used — the stream is being captured into a graph, the allocation fails,
+// or the environment sets USP_ATTENTION_POOL=0 — the call runs the key-group
+// kernel, which needs no workspace and gives the same bits.
+constexpr int kMaxPoolDevices = 64;
+static std::mutex g_pool_mu;
+static hipMemPool_t g_pool[kMaxPoolDevices];
+
+static bool pool_allowed(hipStream_t s) {
+  const char* e = getenv("USP_ATTENTION_POOL");
+  if (e && e[0] == '0') return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs == hipStreamCaptureStatusNone;
+}
+
+// The pool of the device that runs `s`, created on first use; nullptr if
+// the runtime refuses (the caller then runs without a workspace).
+static hipMemPool_t device_pool(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxPoolDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pool[dev]) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof props);
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess || !pool) return nullptr;
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    g_pool[dev] = pool;
+  }
+  return g_pool[dev];
+}
+
 static int run_attention(const AttnArgs& a, hipStream_t s) {
-  return a.in_dt == USP_F32 ? launch_attention_f32(a, s) : launch_attention_bf16(a, s);
+  if (a.in_dt == USP_F32) return launch_attention_f32(a, s);
+  if (!a.ws && attention_bf16_splits(a.Sk, a.D) && pool_allowed(s)) {
+    const size_t need = attention_bf16_ws_bytes(a.B, a.S, a.head_hi - a.head_lo, a.D);
+    hipMemPool_t pool = device_pool(s);
+    void* ws = nullptr;
+    if (pool && hipMallocFromPoolAsync(&ws, need, pool, s) == hipSuccess && ws) {
+      AttnArgs b = a;
+      b.ws = ws;
+      b.ws_bytes = need;
+      const int st = launch_attention_bf16(b, s);
+      if (hipFreeAsync(ws, s) != hipSuccess && st == USP_OK)
+        return fail(USP_EHIP, "hipFreeAsync of the attention workspace failed");
+      return st;
+    }
+    (void)hipGetLastError();  // the pool could not serve: run without a workspace
+  }
+  return launch_attention_bf16(a, s);
 }
 
 }  // namespace usp

@@ -90,5 +90,8 @@ int launch_attention_merge(const MergeArgs& a, hipStream_t s);
 int launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 // Workspace bytes the bf16 key-half path needs for B x heads x S rows.
 size_t attention_bf16_ws_bytes(int64_t B, int64_t S, int32_t heads, int32_t D);
+// Whether bf16 attention over Sk keys at head dim D splits each row's keys in
+// halves (the form that takes a workspace, or the key-group kernel without).
+bool attention_bf16_splits(int64_t Sk, int32_t D);
 
 }  // namespace usp
