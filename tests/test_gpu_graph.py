@@ -81,3 +81,44 @@ def test_step_replays_from_a_captured_graph(phases):
         torch.cuda.synchronize()
         assert torch.equal(got, out), f"replay {i} differs from the eager step"
         assert not torch.isnan(got.float()).any()
+
+
+def test_default_attention_under_capture():
+    """usp_attention_fwd given no workspace, captured into a graph: while the
+    stream is capturing the call takes nothing from the library's pool and
+    runs the key-group kernel (1000 keys at D = 128 split in halves). Every
+    replay, with new inputs copied in and eager work between, equals the
+    eager call (which takes its workspace from the pool) bit for bit."""
+    import torch
+    B, S, h, D = 1, 1000, 4, 128
+    q, k, v = (torch.empty((B, S, h, D), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    o = torch.empty((B, S, h, D), dtype=torch.float32, device=DEV)
+
+    def load(seed):
+        for dst, src in zip((q, k, v), synth.draw_qkv(B, S, h, D, seed)):
+            dst.copy_(to_dev(src, synth.BF16))
+
+    load(200)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):             # warm-up outside the capture
+        usp.usp_attention_fwd(q, k, v, o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    log("capture usp_attention_fwd without a workspace")
+    with torch.cuda.graph(graph):
+        usp.usp_attention_fwd(q, k, v, o)
+    torch.cuda.synchronize()
+    for i, seed in enumerate((201, 202, 203)):
+        load(seed)
+        junk = torch.randn(1024, 1024, device=DEV) @ torch.randn(1024, 1024, device=DEV)
+        log(f"graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = o.clone()
+        del junk
+        log(f"eager call {i}")
+        usp.usp_attention_fwd(q, k, v, o)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), o.view(torch.int32)), f"replay {i}"
