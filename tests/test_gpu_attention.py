@@ -591,3 +591,32 @@ def test_slab_beyond_2gib(S, h, D, what):
     assert not np.any(np.isnan(out))
     rows = {(0, 0): np.unique(np.concatenate([_sample_rows(S, 24, 98), [0, S - 1]]))}
     _check_sampled(out, q1, k1, v1, BF, 1, S, rows, lse=lse)
+
+
+def test_default_call_on_two_streams():
+    """The workspace pool under concurrent use: two streams, each running the
+    default call (keys split in halves, so each call takes a workspace from
+    the pool) on its own inputs several times over, interleaved; every output
+    equals the same call run alone, bit for bit."""
+    import torch
+    B, S, h, D = 1, 3000, 6, 128
+    ins = [[to_dev(x, BF) for x in synth.draw_qkv(B, S, h, D, seed=71 + i)] for i in range(2)]
+    ref = []
+    for q, k, v in ins:
+        o = torch.empty((B, S, h, D), dtype=torch.float32, device=DEV)
+        usp.usp_attention_fwd(q, k, v, o)
+        torch.cuda.synchronize()
+        ref.append(o.clone())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.full((B, S, h, D), float("nan"), device=DEV) for _ in range(4)] for _ in range(2)]
+    torch.cuda.synchronize()
+    log("default attention on two streams at once")
+    for r in range(4):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                q, k, v = ins[i]
+                usp.usp_attention_fwd(q, k, v, outs[i][r], stream=st)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(4):
+            assert torch.equal(outs[i][r].view(torch.int32), ref[i].view(torch.int32)), (i, r)
