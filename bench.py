@@ -39,7 +39,8 @@ a leg says "cold"):
     K rows x 8);
   * usp_attention_fwd_gqa on rank 0's share of the grouped video-DiT
     workload; one rank's Ulysses+Ring pass (video-DiT over 4 x 2 ranks: two
-    key blocks, then the merge); the head-chunked passes on the long
+    key blocks, then the merge; the second block on a second stream with
+    whole key walks, and on one stream with the block call); the head-chunked passes on the long
     sequence (B=1, S=131072, h=8, 3/3/2) against single shot; the same step
     as the two-phase exchange (per head chunk 2/2/1: pack, attention,
     unpack); the world relayouts of the [1, 32760, 40, 128] tensor (one
@@ -116,6 +117,7 @@ def kernel_kind(name):
                       ("attn_bf16_kernel<128, 8, 2, 1, 64, true>", "attention_groups"),
                       ("attn_bf16_kernel<128, 8, 2, 1, 64, false>", "attention_groups_f32out"),
                       ("attn_bf16_kernel<128, 8, 1, 1, 64, true>", "attention_whole"),
+                      ("attn_bf16_kernel<128, 8, 1, 1, 64, false>", "attention_whole_f32out"),
                       ("attn_merge_halves<128, true>", "merge"),
                       ("attn_merge_halves<128, false>", "merge_f32out"),
                       ("copyBuffer", "copy"),
@@ -411,6 +413,7 @@ def short_kernel_name(name):
                 "attention_groups": "attn_bf16_kernel<D=128, key groups> (fwd)",
                 "attention_groups_f32out": "attn_bf16_kernel<D=128, key groups, f32 out>",
                 "attention_whole": "attn_bf16_kernel<D=128, whole walks>",
+                "attention_whole_f32out": "attn_bf16_kernel<D=128, whole walks, f32 out>",
                 "merge": "attn_merge_halves<D=128>",
                 "merge_f32out": "attn_merge_halves<D=128, f32 out>",
                 "copy": "__amd_rocclr_copyBuffer",
@@ -471,6 +474,20 @@ def trace_summary(dirs, out_txt, warmup, steps):
             x = float(np.mean(v[warmup:warmup + steps]))
             lines.append(f"serial steps' timed calls: {name} [{wgs} workgroups] {x:.1f} us "
                          f"(minimum {min(v[warmup:warmup + steps]):.1f})")
+    # ring passes: from the start of the earlier of the two block attention
+    # dispatches before each log-sum-exp merge to that merge's end (on two
+    # streams the blocks run at once, so their durations do not add up)
+    spans, attn_rows = [], []
+    for r in rows:
+        name = short_kernel_name(r["Kernel_Name"])
+        if name.startswith("attn_bf16_kernel"):
+            attn_rows.append(r)
+        elif name == "lse_merge_kernel" and len(attn_rows) >= 2:
+            t0 = min(int(x["Start_Timestamp"]) for x in attn_rows[-2:])
+            spans.append((int(r["End_Timestamp"]) - t0) / 1e3)
+    if spans:
+        lines += ["", "ring passes, kernel time from the first block's start to the merge's end (us), in "
+                      "order: " + " ".join(f"{x:.1f}" for x in spans)]
     text = "\n".join(lines)
     print(text)
     if out_txt:
@@ -879,8 +896,11 @@ def main():
             ev_fold = [torch.cuda.Event() for _ in range(2)]
 
             def ring_pass(i, two_streams=True):
-                # the second block's attention on a second stream (a ring delivers
-                # it long before the first is done); folds in ring order on the first
+                # two streams: the later blocks' attention on a second stream (a ring
+                # delivers a block long before the one before it is done), whole key
+                # walks so the two launches fill each other's last rounds; one stream:
+                # the block call, whose key halves fill a launch's last round alone.
+                # Folds in ring order on the first stream.
                 ms_ = torch.cuda.current_stream()
                 st2 = side if two_streams else ms_
                 start = torch.cuda.Event()
@@ -888,12 +908,17 @@ def main():
                 st2.wait_event(start)
                 for e in ev_fold:
                     e.record(ms_)
-                usp.usp_attention_fwd_block(qr, *kvr[order[0]], o_acc, lse=l_acc, ws=rws, stream=ms_)
+
+                def block(kv, o_, l_, ws_, st_):
+                    if two_streams:
+                        usp.usp_attention_fwd_block_whole(qr, *kv, o_, lse=l_, stream=st_)
+                    else:
+                        usp.usp_attention_fwd_block(qr, *kv, o_, lse=l_, ws=ws_, stream=st_)
+                block(kvr[order[0]], o_acc, l_acc, rws, ms_)
                 for n, blk in enumerate(order[1:]):
                     s2 = n % 2
                     st2.wait_event(ev_fold[s2])
-                    usp.usp_attention_fwd_block(qr, *kvr[blk], o_b2[s2], lse=l_b2[s2],
-                                                ws=rws2 if two_streams else rws, stream=st2)
+                    block(kvr[blk], o_b2[s2], l_b2[s2], rws2 if two_streams else rws, st2)
                     ev_blk[s2].record(st2)
                     ms_.wait_event(ev_blk[s2])
                     last = n == len(order) - 2
@@ -902,12 +927,20 @@ def main():
                     ev_fold[s2].record(ms_)
 
             legs["ring_one_stream"] = timed(torch, lambda i: ring_pass(i, False), reps)
-            one = o_out.clone()
             legs["ring"] = timed(torch, ring_pass, reps)
-            if not torch.equal(one, o_out):
+            two = o_out.clone()
+            # the same whole-walk launches serialised on one stream: the same bits
+            ms_ = torch.cuda.current_stream()
+            usp.usp_attention_fwd_block_whole(qr, *kvr[order[0]], o_acc, lse=l_acc, stream=ms_)
+            for blk in order[1:]:
+                usp.usp_attention_fwd_block_whole(qr, *kvr[blk], o_b2[0], lse=l_b2[0], stream=ms_)
+                usp.usp_attention_merge(o_acc, l_acc, o_b2[0], l_b2[0], o_out if blk == order[-1] else o_acc,
+                                        None if blk == order[-1] else l_acc, stream=ms_)
+            torch.cuda.synchronize()
+            if not torch.equal(two, o_out):
                 raise RuntimeError("the two-stream ring pass changed the output")
             legs["ring"]["flop"] = 4.0 * rw.B * rh * Sq * rw.S * rw.D
-            del qr, kvr, rws, rws2, o_acc, l_acc, o_b2, l_b2, o_out, one
+            del qr, kvr, rws, rws2, o_acc, l_acc, o_b2, l_b2, o_out, two
 
         if on("chunked"):
             # head-chunked passes on the long-sequence share, against single shot

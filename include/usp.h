@@ -379,6 +379,28 @@ int usp_attention_fwd_block(const void* q, const void* k, const void* v, void* o
                             float scale, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * usp_attention_fwd_block for the key blocks of a ring pass that run at the
+ * same time on separate streams (Ulysses+Ring, maxdiffusion PR #428
+ * description; a ring brings the next K/V block while the rank still
+ * attends to the current one). It computes the same O and lse, but every query row walks
+ * all Sk keys in one pass: no key-half split, so no workspace and no merge
+ * of halves. Launches on two streams then fill each other's last rounds of
+ * work; a launch alone runs a part-empty last round wherever
+ * B * (head_hi - head_lo) * ceil(Sq / 256) is not a multiple of the CU count
+ * (usp_attention_fwd_block is the form for one stream).
+ * Where usp_attention_fwd_block does not split the keys (fp32 inputs; bf16
+ * with fewer than 8 or more than 1024 key tiles of 64 keys at D = 128, of 128
+ * at D = 64) both give the same bits; elsewhere they differ by rounding only.
+ * A query row's result depends only on its own row and the key block, as for
+ * usp_attention_fwd_block. Allocates nothing. Arguments and errors as
+ * usp_attention_fwd_block without ws and ws_bytes.
+ */
+int usp_attention_fwd_block_whole(const void* q, const void* k, const void* v, void* o,
+                                  usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t Sq,
+                                  int64_t Sk, int32_t h, int32_t h_kv, int32_t D, int32_t head_lo,
+                                  int32_t head_hi, float scale, float* lse, void* stream);
+
+/*
  * Log-sum-exp merge of two attention results of the same query rows over
  * disjoint key blocks (the fold of one Ulysses+Ring step; softmax over the
  * union of the two key sets). For heads n in [head_lo, head_hi):

@@ -423,6 +423,13 @@ static void check_block_and_merge(void) {
   int lse_ok = 1;
   for (size_t i = 0; i < nl; ++i) lse_ok &= fabsf(b[i] - (a[i] + 0.69314718f)) <= 2e-6f * (1.0f + fabsf(a[i]));
   CHECK(lse_ok, "merging a result with itself adds log 2 to lse");
+  /* 300 keys at D = 64 are too few to split: whole walks give the same bits */
+  CHECK(usp_attention_fwd_block_whole(q, k, v, o3, USP_BF16, USP_F32, B, S, S, h, hkv, D, 0, h, 0.0f,
+                                      l3, NULL) == USP_OK, "usp_attention_fwd_block_whole");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(a, o2, nq * 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(b, o3, nq * 4, hipMemcpyDeviceToHost));
+  CHECK(memcmp(a, b, nq * 4) == 0, "whole walks over a block too short to split equal the block call");
   void* pq = q;
   HIP_OK(hipFree(pq));
   HIP_OK(hipFree(k));

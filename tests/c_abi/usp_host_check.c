@@ -212,6 +212,15 @@ static void check_attention_rejections(void) {
   EXPECT_ERR(usp_attention_fwd_block(q, k, v, o, USP_BF16, USP_F32, 1, 1000, 0, 4, 4, 128, 0, 4, 0.f,
                                      NULL, NULL, 0, NULL),
              USP_ESHAPE);
+  EXPECT_ERR(usp_attention_fwd_block_whole(q, k, v, o, USP_BF16, USP_F32, 1, 1000, 0, 4, 4, 128, 0, 4,
+                                           0.f, NULL, NULL),
+             USP_ESHAPE);
+  EXPECT_ERR(usp_attention_fwd_block_whole(q, k, v, o, USP_BF16, USP_F32, 1, 1000, 500, 6, 4, 128, 0, 6,
+                                           0.f, NULL, NULL),
+             USP_EINVAL);
+  EXPECT_ERR(usp_attention_fwd_block_whole(q, k, v, o, USP_BF16, USP_F32, 1, 1000, 500, 4, 4, 96, 0, 4,
+                                           0.f, NULL, NULL),
+             USP_ENOSYS);
   EXPECT_ERR(usp_attention_merge((const float*)q, (const float*)k, (const float*)q, (const float*)k, q,
                                  NULL, USP_BF16, 1, 100, 4, 128, 0, 4, NULL),
              USP_EINVAL);

@@ -293,6 +293,23 @@ def test_attention_block_rejects(kw, status):
     assert usp.usp_last_error()
 
 
+def _attn_block_whole(q=FAKE, k=FAKE, Sq=16, Sk=40, h=4, hkv=2, lo=0, hi=4, D=64, i=1, out=0,
+                      lse=None):
+    return L.usp_attention_fwd_block_whole(q, k, FAKE, FAKE, i, out, 1, Sq, Sk, h, hkv, D, lo, hi,
+                                           0.0, lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Sk=0), -2), (dict(Sq=0), -2), (dict(Sk=2**31), -2), (dict(hkv=3), -1),
+    (dict(hkv=0), -1), (dict(lo=2, hi=2), -1), (dict(hi=5), -1), (dict(k=None), -1),
+    (dict(q=None), -1), (dict(k=FAKE + 8), -4), (dict(lse=FAKE + 2), -4), (dict(D=80), -5),
+    (dict(i=1, D=32), -5), (dict(i=0, out=1), -3), (dict(i=5), -3), (dict(out=3), -3),
+])
+def test_attention_block_whole_rejects(kw, status):
+    assert _attn_block_whole(**kw) == status
+    assert usp.usp_last_error()
+
+
 def _merge(oa=FAKE, la=FAKE, ob=FAKE + 256, lb=FAKE + 512, o=FAKE + 1024, lse=None, out=0, B=1,
            S=16, h=2, D=64, lo=0, hi=2):
     return L.usp_attention_merge(oa, la, ob, lb, o, lse, out, B, S, h, D, lo, hi, None)

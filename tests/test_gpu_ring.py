@@ -1,6 +1,8 @@
 """GPU parity of the Ulysses+Ring pieces: attention of a query block against a
-key/value block of another length (usp_attention_fwd_block) and the
-log-sum-exp merge (usp_attention_merge), alone and composed into ring passes.
+key/value block of another length (usp_attention_fwd_block, and
+usp_attention_fwd_block_whole for blocks run on separate streams at once) and
+the log-sum-exp merge (usp_attention_merge), alone and composed into ring
+passes.
 
 Tolerances: block attention as plain attention (bf16 inputs graded on the fp32
 output, max-abs <= 1e-2 and relative Frobenius <= 5e-3; fp32 <= 1e-5; lse
@@ -126,6 +128,86 @@ def test_query_rows_split_bitwise(use_ws):
         assert torch.equal(part, o[:, a:b]) and torch.equal(lp, lse[:, :, a:b]), (a, b)
 
 
+def _splits(Sk, D):
+    """Whether the bf16 block call walks each row's keys in two halves: 8 to
+    1024 key tiles of 64 keys (D = 128) or 128 keys (D = 64)."""
+    bn = 64 if D == 128 else 128
+    return 8 <= -(-Sk // bn) <= 1024
+
+
+def _block_whole(dq, dk, dv, out_dtype, lo=0, hi=None, stream=None):
+    """One usp_attention_fwd_block_whole call; returns (o, lse)."""
+    import torch
+    B, Sq, h, D = dq.shape
+    hi = h if hi is None else hi
+    o = poisoned((B, Sq, h, D), out_dtype)
+    lse = torch.full((B, h, Sq), float("nan"), device=DEV)
+    usp.usp_attention_fwd_block_whole(dq, dk, dv, o, head_lo=lo, head_hi=hi, lse=lse,
+                                      stream=stream)
+    return o, lse
+
+
+@pytest.mark.parametrize("B,Sq,Sk,h,hkv,D", BLOCK_CASES + [(1, 300, 1300, 2, 1, 128),
+                                                           (1, 200, 70000, 1, 1, 128)])
+def test_block_whole_full_compare(B, Sq, Sk, h, hkv, D):
+    """Whole key walks against the oracle; where the block call does not split
+    the keys either, the same bits as the block call."""
+    import torch
+    q, k, v = _draw_block(B, Sq, Sk, h, hkv, D, seed=300 + Sq + Sk)
+    ref, ref_lse = A.attention(*(widen(x, BF) for x in (q, k, v)), return_lse=True)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    log(f"block whole bf16->f32 B={B} Sq={Sq} Sk={Sk} h={h} hkv={hkv} D={D}")
+    o, lse = _block_whole(dq, dk, dv, F)
+    log(f"block whole bf16->bf16 B={B} Sq={Sq} Sk={Sk}")
+    o_b, _ = _block_whole(dq, dk, dv, BF)
+    log(f"block (default) bf16->f32 B={B} Sq={Sq} Sk={Sk}")
+    o_d, l_d = _block(dq, dk, dv, F, False)
+    torch.cuda.synchronize()
+    out, lout = to_host(o), lse.cpu().numpy()
+    ma, rf = err(out, ref)
+    assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (ma, rf)
+    assert np.max(np.abs(lout - ref_lse)) <= BF16_LSE_ABS
+    ob = widen(to_host(o_b), BF)
+    assert np.all(np.abs(ob - ref) <= np.maximum(BF16_MAX_ABS, bf16_ulp(ref)))
+    same = torch.equal(o, o_d) and torch.equal(lse, l_d)
+    assert same == (not _splits(Sk, D)), (Sk, D, same)
+
+
+@pytest.mark.parametrize("B,Sq,Sk,h,hkv,D", [(1, 70, 33, 2, 1, 64), (2, 17, 1290, 2, 2, 128)])
+def test_block_whole_f32_is_the_block_call(B, Sq, Sk, h, hkv, D):
+    """fp32 inputs never split their keys: the whole-walk call is the block
+    call bit for bit."""
+    import torch
+    q, k, v = _draw_block(B, Sq, Sk, h, hkv, D, seed=450 + Sq, dtype=F)
+    dq, dk, dv = (to_dev(x, F) for x in (q, k, v))
+    log(f"block whole f32 B={B} Sq={Sq} Sk={Sk} h={h} hkv={hkv} D={D}")
+    o, lse = _block_whole(dq, dk, dv, F)
+    o2, l2 = _block(dq, dk, dv, F, False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    ma, rf = err(to_host(o), A.attention(q, k, v))
+    assert ma <= F32_MAX_ABS and rf <= F32_REL_FROB, (ma, rf)
+
+
+def test_block_whole_query_rows_split_bitwise():
+    """A query row's result does not depend on the query block or the head
+    range it is launched with."""
+    import torch
+    Sq, Sk, h, D = 900, 1300, 3, 128
+    q, k, v = _draw_block(1, Sq, Sk, h, h, D, seed=610)
+    dq, dk, dv = (to_dev(x, BF) for x in (q, k, v))
+    log("block whole: query split bitwise")
+    o, lse = _block_whole(dq, dk, dv, F)
+    for a, b in ((0, 1), (1, 300), (257, 900), (511, 512)):
+        part, lp = _block_whole(dq[:, a:b].contiguous(), dk, dv, F)
+        torch.cuda.synchronize()
+        assert torch.equal(part, o[:, a:b]) and torch.equal(lp, lse[:, :, a:b]), (a, b)
+    oh, lh = _block_whole(dq, dk, dv, F, lo=1, hi=2)
+    torch.cuda.synchronize()
+    assert torch.equal(oh[:, :, 1], o[:, :, 1]) and torch.equal(lh[:, 1], lse[:, 1])
+    assert torch.isnan(oh[:, :, 0]).all() and torch.isnan(oh[:, :, 2]).all()
+
+
 def _merge_inputs(B, S, h, D, seed):
     """fp32 block outputs and normalisers, with lse spread widely, a row where
     one side is empty (-inf) and a row where both are."""
@@ -202,6 +284,64 @@ def _ring_pass(dq, kv_blocks, order, out_dtype, use_ws=True, lo=0, hi=None):
         else:
             usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o_acc, l_acc, head_lo=lo, head_hi=hi)
     return o_acc, l_acc
+
+
+def _ring_pass_streams(dq, kv_blocks, order, out_dtype, two_streams):
+    """A ring pass with usp_attention_fwd_block_whole: the first block on the
+    current stream, the later ones on a second stream (when ``two_streams``)
+    as they would arrive, each folded on the current stream in ring order
+    once its block is done; the last fold writes ``out_dtype``. Returns
+    (o, lse)."""
+    import torch
+    B, Sq, h, D = dq.shape
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if two_streams else main
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    o_acc, l_acc = _block_whole(dq, *kv_blocks[order[0]], F, stream=main)
+    parts = []
+    for i in order[1:]:
+        with torch.cuda.stream(side):
+            o_i, l_i = _block_whole(dq, *kv_blocks[i], F, stream=side)
+        done = torch.cuda.Event()
+        done.record(side)
+        parts.append((o_i, l_i, done))
+    o = o_acc
+    for n, (o_i, l_i, done) in enumerate(parts):
+        main.wait_event(done)
+        if n == len(parts) - 1 and out_dtype == BF:
+            o = poisoned((B, Sq, h, D), BF)
+        usp.usp_attention_merge(o_acc, l_acc, o_i, l_i, o, l_acc, stream=main)
+    torch.cuda.synchronize()
+    return o, l_acc
+
+
+def test_ring_pass_whole_two_streams():
+    """A ring pass of three blocks (one of them ragged) with the whole-walk
+    block call, the later blocks on a second stream: the same bits as on one
+    stream, and the oracle's attention over all the keys."""
+    import torch
+    Sq, h, D = 700, 2, 128
+    lens = (1300, 1299, 577)
+    q = synth.draw_qkv(1, Sq, h, D, 900)[0]
+    kv = [synth.draw_qkv(1, n, h, D, 901 + i)[1:] for i, n in enumerate(lens)]
+    ref, ref_lse = A.attention(widen(q, BF), np.concatenate([widen(x[0], BF) for x in kv], axis=1),
+                               np.concatenate([widen(x[1], BF) for x in kv], axis=1),
+                               return_lse=True)
+    dq = to_dev(q, BF)
+    dkv = [(to_dev(a, BF), to_dev(b, BF)) for a, b in kv]
+    order = RG.ring_order(1, 3)
+    for dt in (F, BF):
+        log(f"ring pass whole, one stream, out {dt}")
+        o1, l1 = _ring_pass_streams(dq, dkv, order, dt, False)
+        log(f"ring pass whole, two streams, out {dt}")
+        o2, l2 = _ring_pass_streams(dq, dkv, order, dt, True)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), dt
+        out = widen(to_host(o1), BF) if dt == BF else to_host(o1)
+        ma, rf = err(out, ref)
+        assert ma <= BF16_MAX_ABS and rf <= BF16_REL_FROB, (dt, ma, rf)
+        assert np.max(np.abs(l1.cpu().numpy() - ref_lse)) <= BF16_LSE_ABS
 
 
 def _ring_world(w, q, k, v, out_dtype):
@@ -317,11 +457,14 @@ def test_one_ring_block_is_the_block_call():
     assert torch.equal(o, o2) and torch.equal(lse, l2)
 
 
-def test_video_dit_ring_share_sampled():
+@pytest.mark.parametrize("form", ["block", "whole_two_streams"])
+def test_video_dit_ring_share_sampled(form):
     """One rank's share of the 4 x 2 video-DiT grid at its real size: ring
     block 1, head group 2 (10 heads, 16380 query rows, two K/V blocks of
-    16380), the launches the benchmark times; 48 sampled rows per head
-    against the oracle over the whole sequence's keys."""
+    16380), in the launches the benchmark times (the block call folded on one
+    stream; the whole-walk call with the second block on a second stream);
+    48 sampled rows per head against the oracle over the whole sequence's
+    keys."""
     import torch
     w = synth.WORKLOADS["video_dit_ring"]
     q, k, v = synth.draw_workload(w)
@@ -341,8 +484,11 @@ def test_video_dit_ring_share_sampled():
     qj = blk(dq, r)
     kv = [(blk(dk, i), blk(dv, i)) for i in range(w.ring)]
     del dq, dk, dv
-    log("video_dit_ring share: ring pass")
-    o, lse = _ring_pass(qj, kv, RG.ring_order(r, w.ring), F)
+    log(f"video_dit_ring share: ring pass ({form})")
+    if form == "block":
+        o, lse = _ring_pass(qj, kv, RG.ring_order(r, w.ring), F)
+    else:
+        o, lse = _ring_pass_streams(qj, kv, RG.ring_order(r, w.ring), F, True)
     torch.cuda.synchronize()
     out, lout = to_host(o), lse.cpu().numpy()
     rng = np.random.default_rng(9)

@@ -21,14 +21,16 @@ One rank's share of the work behind a small C ABI (``include/usp.h``,
     grouped key/value heads;
   * ``usp_attention_fwd_block`` / ``usp_attention_merge`` — a query block
     against one key/value block with its log-sum-exp, and the merge of such
-    results: one ring step of Ulysses+Ring attention.
+    results: one ring step of Ulysses+Ring attention;
+    ``usp_attention_fwd_block_whole`` the block call with whole key walks,
+    for ring blocks run on separate streams at once.
 
 The Python functions of the same names only marshal arguments (PyTorch
 tensors for device memory, PyTorch streams); ``synth`` draws seeded inputs.
 """
 from ._binding import (  # noqa: F401
     USP_BF16, USP_F32, USP_MAX_PARTS, UspError, header_symbols, lib, usp_attention_fwd,
-    usp_attention_fwd_block, usp_attention_fwd_chunked, usp_attention_fwd_chunked_ws,
+    usp_attention_fwd_block, usp_attention_fwd_block_whole, usp_attention_fwd_chunked, usp_attention_fwd_chunked_ws,
     usp_attention_fwd_gqa, usp_attention_fwd_noalloc,
     usp_attention_fwd_ws, usp_attention_merge,
     usp_attention_workspace_bytes,

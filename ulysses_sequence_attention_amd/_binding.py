@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         L.usp_attention_fwd_block.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
                                               _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                               _f32, _vp, _vp, ctypes.c_size_t, _vp]
+        L.usp_attention_fwd_block_whole.argtypes = L.usp_attention_fwd_block.argtypes[:16] + [_vp]
         L.usp_attention_merge.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i64,
                                           _i32, _i32, _i32, _i32, _vp]
         rows = [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _vp]
@@ -103,7 +104,7 @@ def lib() -> ctypes.CDLL:
                      "usp_attention_fwd_chunked", "usp_attention_fwd_chunked_ws",
                      "usp_attention_workspace_bytes",
                      "usp_attention_fwd_ws", "usp_attention_fwd_gqa", "usp_attention_fwd_block",
-                     "usp_attention_merge", "usp_scatter_rows",
+                     "usp_attention_fwd_block_whole", "usp_attention_merge", "usp_scatter_rows",
                      "usp_gather_rows", "usp_reduce_scatter_rows"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
@@ -469,6 +470,21 @@ def usp_attention_fwd_block(q, k, v, o, head_lo: int = 0, head_hi=None, scale: f
                                          B, Sq, k.shape[1], h, k.shape[2], D, head_lo, hi, scale,
                                          _ptr(lse), _ptr(ws), nbytes, _stream(q, stream)),
            "usp_attention_fwd_block")
+
+
+def usp_attention_fwd_block_whole(q, k, v, o, head_lo: int = 0, head_hi=None, scale: float = 0.0,
+                                  lse=None, stream=None) -> None:
+    """usp_attention_fwd_block with every query row's keys walked in one pass
+    (no workspace): for the key blocks of a ring pass run on separate
+    streams at the same time."""
+    kd = _dims(k, "k", 4)
+    _attn_io(q, k, v, o, lse, None, kv_rows=kd[1], kv_heads=kd[2])
+    B, Sq, h, D = q.shape
+    hi = h if head_hi is None else head_hi
+    _check(lib().usp_attention_fwd_block_whole(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype(q),
+                                               _dtype(o), B, Sq, k.shape[1], h, k.shape[2], D,
+                                               head_lo, hi, scale, _ptr(lse), _stream(q, stream)),
+           "usp_attention_fwd_block_whole")
 
 
 def usp_attention_merge(o_a, lse_a, o_b, lse_b, o, lse=None, head_lo: int = 0, head_hi=None,

@@ -57,7 +57,10 @@
 // round of 256 half-walks); an even split, since the longer half sets every
 // CU's finish time. Shorter and longer walks run whole (at D = 64 a short
 // walk runs in 4-wave workgroups of 128 rows with 64-key tiles, three per
-// CU). Two forms of the split:
+// CU). Callers that run several launches at once (the key blocks of a ring
+// step on separate streams) may ask for whole walks at every length: the
+// launches then fill each other's last rounds and no state is merged. Two
+// forms of the split:
 //   * key groups (usp_attention_fwd): a workgroup of 8 waves is two groups
 //     of 4 waves that walk the two halves for the same 128 rows, each with
 //     its own K/V buffers, and merge through LDS;
@@ -719,7 +722,7 @@ bool short_walk(int64_t Sk, int D, int BN) {
 }
 
 template <int D, int BN, bool kOutBf16>
-int launch_tiles(Params& p, int64_t tiles, void* ws, hipStream_t s) {
+int launch_tiles(Params& p, int64_t tiles, void* ws, bool whole, hipStream_t s) {
   if constexpr (D == 64) {
     if (short_walk(p.Sk, D, BN)) {
       // two 128-row workgroups per 256-row tile; no state to merge
@@ -727,7 +730,7 @@ int launch_tiles(Params& p, int64_t tiles, void* ws, hipStream_t s) {
       return check_launch("attn_bf16_kernel (short walks)");
     }
   }
-  if (!split_keys(p.Sk, BN)) {
+  if (whole || !split_keys(p.Sk, BN)) {
     // whole key walks in 256-row workgroups: no state to merge, no workspace
     attn_bf16_kernel<D, 8, 1, 1, BN, kOutBf16><<<unsigned(tiles), 512, 0, s>>>(p);
     return check_launch("attn_bf16_kernel (whole walks)");
@@ -775,8 +778,8 @@ int launch(const AttnArgs& a, hipStream_t s) {
   if (a.ws && a.ws_bytes < halves_ws_bytes(tiles, a.D))
     return fail(USP_EINVAL, "workspace of %zu bytes is below the %zu this call needs", a.ws_bytes,
                 halves_ws_bytes(tiles, a.D));
-  return a.out_dt == USP_BF16 ? launch_tiles<D, BN, true>(p, tiles, a.ws, s)
-                              : launch_tiles<D, BN, false>(p, tiles, a.ws, s);
+  return a.out_dt == USP_BF16 ? launch_tiles<D, BN, true>(p, tiles, a.ws, a.whole, s)
+                              : launch_tiles<D, BN, false>(p, tiles, a.ws, a.whole, s);
 }
 
 }  // namespace

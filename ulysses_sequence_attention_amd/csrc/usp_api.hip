@@ -217,7 +217,7 @@ static hipMemPool_t device_pool(hipStream_t s) {
 
 static int run_attention(const AttnArgs& a, hipStream_t s) {
   if (a.in_dt == USP_F32) return launch_attention_f32(a, s);
-  if (!a.ws && attention_bf16_splits(a.Sk, a.D) && pool_allowed(s)) {
+  if (!a.ws && !a.whole && attention_bf16_splits(a.Sk, a.D) && pool_allowed(s)) {
     const size_t need = attention_bf16_ws_bytes(a.B, a.S, a.head_hi - a.head_lo, a.D);
     hipMemPool_t pool = device_pool(s);
     void* ws = nullptr;
@@ -504,6 +504,19 @@ int usp_attention_fwd_block(const void* q, const void* k, const void* v, void* o
   if (int st = check_attention(a)) return st;
   if (in_dt != USP_BF16) a.ws = nullptr;
   if (a.ws && !aligned16(a.ws)) return fail(USP_EALIGN, "workspace is not 16-byte aligned");
+  if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
+  if (int st = run_attention(a, (hipStream_t)stream)) return st;
+  return ok();
+}
+
+int usp_attention_fwd_block_whole(const void* q, const void* k, const void* v, void* o,
+                                  usp_dtype in_dt, usp_dtype out_dt, int64_t B, int64_t Sq,
+                                  int64_t Sk, int32_t h, int32_t h_kv, int32_t D, int32_t head_lo,
+                                  int32_t head_hi, float scale, float* lse, void* stream) {
+  AttnArgs a{q, k, v, o, lse, B, Sq, Sk, h, D, head_lo, head_hi, scale, in_dt, out_dt, nullptr, 0,
+             h_kv};
+  a.whole = true;
+  if (int st = check_attention(a)) return st;
   if (!(a.scale > 0.0f)) a.scale = 1.0f / sqrtf((float)D);
   if (int st = run_attention(a, (hipStream_t)stream)) return st;
   return ok();

@@ -74,6 +74,7 @@ struct AttnArgs {
   void* ws;         // bf16 path: key-half workspace, or nullptr for the key-group kernel
   size_t ws_bytes;
   int32_t h_kv;     // heads of k and v (h for plain multi-head attention); divides h
+  bool whole = false;  // bf16 path: walk every row's keys in one pass (never split them)
 };
 int launch_attention_f32(const AttnArgs& a, hipStream_t s);
 // Log-sum-exp merge of two attention results (fp32 o and lse) for heads
