@@ -452,10 +452,10 @@ def trace_summary(dirs, out_txt, warmup, steps):
     for (name, wgs), v in sorted(per_grid.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{name:56s} {wgs:10d} {len(v):6d} {np.mean(v):9.1f} {min(v):9.1f} {max(v):9.1f} "
                      f"{100 * sum(v) / total:6.2f}")
-    lines += ["", "durations in dispatch order (us), for the library's kernels with at most 64 dispatches "
+    lines += ["", "durations in dispatch order (us), for the library's kernels with at most 400 dispatches "
                   "of one launch shape:"]
     for (name, wgs), v in sorted(per_grid.items(), key=lambda kv: -sum(kv[1])):
-        if len(v) <= 64 and ("attn" in name or "relayout" in name or "merge" in name):
+        if len(v) <= 400 and ("attn" in name or "relayout" in name or "merge" in name):
             lines.append(f"  {name} [{wgs} workgroups]: " + " ".join(f"{x:.1f}" for x in v))
     att = per.get(short_kernel_name("attn_bf16_kernel<128, 8, 1, 2, 64, true>"), [])
     mrg = per.get(short_kernel_name("attn_merge_halves<128, true>"), [])
@@ -553,6 +553,15 @@ def host_ms_per_call(torch, fn, warm):
     return host, a.elapsed_time(b) / max(warm, 1)
 
 
+def top_up_warmup(torch, fn, gpu, done, target_ms=100.0, cap=400):
+    """More untimed calls of ``fn(i)`` after ``done`` warm-up calls of ``gpu``
+    ms each, until about ``target_ms`` of GPU work (at most ``cap`` calls): a
+    leg that follows another workload is timed once the clock has settled on
+    its own."""
+    for i in range(done, min(cap, int(target_ms / max(gpu, 1e-3)))):
+        fn(i)
+
+
 def spin_if_host_bound(torch, host, gpu, calls):
     """Queue a spin ahead of ``calls`` timed calls when the host's enqueue
     time per call is not well below the GPU's (short calls); long calls keep
@@ -563,10 +572,11 @@ def spin_if_host_bound(torch, host, gpu, calls):
 
 
 def timed(torch, fn, reps, warm=3):
-    """Median / minimum / mean of ``reps`` calls of ``fn(i)`` after ``warm``,
-    each between two HIP events; short calls are issued behind a GPU spin
-    (queue_ahead)."""
+    """Median / minimum / mean of ``reps`` calls of ``fn(i)`` after ``warm``
+    (and more, up to about 0.1 s of GPU work), each between two HIP events;
+    short calls are issued behind a GPU spin (queue_ahead)."""
     host, gpu = host_ms_per_call(torch, fn, warm)
+    top_up_warmup(torch, fn, gpu, warm)
     spin_if_host_bound(torch, host, gpu, reps)
     t = Timer(torch)
     for i in range(reps):
@@ -578,6 +588,7 @@ def back_to_back(torch, fn, reps, warm=3):
     """Mean per call of ``reps`` calls of ``fn(i)`` issued back to back
     between two HIP events (no event between calls) behind a GPU spin, in ms."""
     host, gpu = host_ms_per_call(torch, fn, warm)
+    top_up_warmup(torch, fn, gpu, warm)
     spin_if_host_bound(torch, host, gpu, reps)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -1072,6 +1083,7 @@ def main():
                     tw[2](usp.usp_unpack_heads_to_seq, ob, out)
 
                 host, gpu = host_ms_per_call(torch, run, 3)
+                top_up_warmup(torch, run, gpu, 3)
                 tw = [Timer(torch) for _ in range(4)]
                 n = max(6, reps)
                 spin_if_host_bound(torch, host, gpu, n)
