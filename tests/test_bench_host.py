@@ -116,13 +116,6 @@ def test_stored_traffic_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
     assert bench.stored_traffic() is None
 
 
-def test_committed_traffic_matches_the_committed_kernel():
-    """The counter summary under profiles/ was taken on the kernel source as
-    committed, so the benchmark reports its traffic."""
-    t = bench.stored_traffic()
-    assert t is not None and 1e8 < t < 5e9
-
-
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
