@@ -41,6 +41,19 @@ def test_grouped_block_and_chunked_shapes():
         usp.usp_attention_fwd_chunked(q, t(1, 8, 2, 64), t(1, 8, 4, 64), o, 2)
 
 
+def test_block_whole_shapes_and_device():
+    q, o = t(1, 8, 4, 64), t(1, 8, 4, 64, dtype=F)
+    with pytest.raises(ValueError, match="v has shape"):
+        usp.usp_attention_fwd_block_whole(q, t(1, 5, 2, 64), t(1, 6, 2, 64), o)
+    with pytest.raises(ValueError, match="v has dtype"):
+        usp.usp_attention_fwd_block_whole(q, t(1, 5, 2, 64), t(1, 5, 2, 64, dtype=F), o)
+    with pytest.raises(ValueError, match="lse has shape"):
+        usp.usp_attention_fwd_block_whole(q, t(1, 5, 2, 64), t(1, 5, 2, 64), o,
+                                          lse=t(1, 4, 5, dtype=F))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        usp.usp_attention_fwd_block_whole(q, t(1, 5, 2, 64), t(1, 5, 2, 64), o)
+
+
 def test_merge_shapes():
     oa, la = t(1, 8, 2, 64, dtype=F), t(1, 2, 8, dtype=F)
     with pytest.raises(ValueError, match="o_b has shape"):
